@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the parallel-Newton diagonal GRU/LSTM forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the input projection (prn_input_proj) followed by
+the K-iteration Newton solve (prn_newton_forward).  Prints ONE JSON line.
+
+Default workload: the diagonal LSTM, B=2, T=131072, d_in=d_h=256, fp32,
+K=2 (the long-sequence configuration the bandwidth target is stated for).
+The other workloads (--workload) are parity cases; they can be timed too.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation; HIP events around every library call on the stream the
+kernels run on give per-call durations.  The CPU baseline times the oracle
+(NumPy, float64) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Newton-forward tokens/sec at K=3 (B*T/s) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+
+
+def algorithmic_newton_bytes(w) -> float:
+    """Bytes the K-pass Newton method must move per forward: per channel-token,
+    read xproj once per iteration (K*G), read the previous iterate and write
+    each new one for iterations 2..K and 1..K-1 (2(K-1)S), write h (1)."""
+    elt = 4 if w.dtype == "f32" else 2
+    per = w.K * w.G + 2 * (w.K - 1) * w.S + 1
+    return float(w.tokens) * w.d_h * per * elt
+
+
+def proj_flops(w) -> float:
+    return 2.0 * w.tokens * w.G * w.d_h * w.d_in
+
+
+def cpu_baseline(w, budget_s: float = 20.0) -> dict:
+    """The oracle as it stands (projection + Newton, float64 NumPy), on rows
+    of the first batch row: a prefix of T_s steps, all channels, 1 thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import newton as onewton
+    from oracle import proj as oproj
+    from oracle import rounding as oround
+    from workloads import make_inputs
+
+    T_s = min(w.T, 8192)
+    ws = w.scaled(B=1, T=T_s, n_seqs=0)
+    inp = make_inputs(ws, seed=0)
+    cu = None
+    if w.n_seqs:
+        full = make_inputs(w, seed=0)["cu_seqlens"]
+        cu = np.concatenate([full[full < T_s], [T_s]]).astype(np.int64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            xp = oproj.input_proj(oround.load(inp["x"], w.dtype), oround.load(inp["W"], w.dtype),
+                                  inp["bias"].astype(np.float64), w.G)
+            xp = oround.store(xp, w.dtype)
+            onewton.newton(w.cell, xp, inp["a"].astype(np.float64), w.K, cu_seqlens=cu, dtype=w.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > budget_s / 2 or reps >= 3:
+                break
+    tok = reps * ws.tokens
+    return {"value": tok / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x (B=1, T={T_s}, all {w.d_h} channels, K={w.K}) of {w.name}: "
+                      f"numpy float64 projection + Newton, 1 thread, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lstm_t131k")
+    ap.add_argument("--K", type=int, default=None, help="override the workload's Newton depth")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import nonlinear_rnn_amd as prn
+    from nonlinear_rnn_amd import binding as B
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if args.K:
+        w = w.scaled(K=args.K)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+
+    inp = make_inputs(w, seed=0)
+
+    def up(arr):
+        if w.dtype == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(arr).to(dev)
+
+    x, W = up(inp["x"]), up(inp["W"])
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    a = torch.from_numpy(inp["a"]).to(dev)
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    n_seqs = 0 if cu is None else cu.numel() - 1
+    xproj = torch.empty((w.B, w.T, w.G, w.d_h), dtype=dt, device=dev)
+    H = torch.empty((w.B, w.T, w.d_h), dtype=dt, device=dev)
+    res = torch.zeros(w.K + 1, dtype=torch.float32, device=dev)
+    ws_n = B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, w.K, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.prn_input_proj(x, W, bias, xproj, cell=w.cell, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        B.prn_newton_forward(xproj, a, w.K, H, cell=w.cell, cu_seqlens=cu, residual_out=res, workspace=ws,
+                             stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_proj = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_newt = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_step = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    print(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    residuals = res.cpu().tolist()
+    ms_step = wall * 1e3 / args.steps
+    value = w.tokens / (wall / args.steps)
+
+    newton_ms = float(t_newt.mean())
+    proj_ms = float(t_proj.mean())
+    alg_bytes = algorithmic_newton_bytes(w)
+    roof_newton = {"kernel": "prn_newton_forward (all its launches)", "bound": "hbm",
+                   "achieved": alg_bytes / (newton_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                   "traffic": None}
+    roof_newton["frac"] = roof_newton["achieved"] / roof_newton["peak"]
+    fl = proj_flops(w)
+    roof_proj = {"kernel": "k_proj (prn_input_proj)", "bound": "mfma",
+                 "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                 "traffic": None}
+    roof_proj["frac"] = roof_proj["achieved"] / roof_proj["peak"]
+    dominant = roof_newton if newton_ms >= proj_ms else roof_proj
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "cell": f"diag_{w.cell}", "B": w.B, "T": w.T, "d_in": w.d_in,
+                   "d_h": w.d_h, "K": w.K, "n_seqs": w.n_seqs, "tokens": w.tokens},
+        "roofline": dominant,
+        "roofline_newton": roof_newton,
+        "roofline_proj": roof_proj,
+        "breakdown_ms": {"proj_mean": proj_ms, "newton_mean": newton_ms, "newton_median": float(np.median(t_newt)),
+                         "newton_min": float(t_newt.min()), "step_event_mean": float(t_step.mean())},
+        "newton_tokens_per_s": w.tokens / (newton_ms * 1e-3),
+        "residuals": residuals,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+/*
+ * prn.h -- C ABI of libprn: parallel Newton forward of diagonal GRU / LSTM
+ * recurrences on AMD Instinct MI355X (gfx950).
+ *
+ * The sequential recurrence s_t = f(s_{t-1}, x_t) is replaced by K Newton
+ * iterations over the whole trajectory.  Each iteration evaluates the cell
+ * and its per-channel Jacobian J_t at the previous guess, forms the affine
+ * maps s_t = J_t s_{t-1} + b_t with b_t = f(s^old_{t-1}, x_t) - J_t s^old_{t-1},
+ * solves them with a chunked parallel scan over time, and reduces the
+ * residual max|F(H)|, F_t = h_t - f(h_{t-1}, x_t).
+ *
+ * Sources (pararnn-torch pages):
+ *   FAQs, "Does parallel Newton match sequential unroll?"    agreement tau
+ *   FAQs, "How many Newton iterations should I use?"         K pinned or per T
+ *   FAQs, "Does torch.compile / autocast work?"              fixed K, no host sync
+ *   FAQs, "train() vs eval()"                                Newton vs sequential
+ *   Numerics contract, "Two thresholds", "1. Runtime"       residual max|F(H)|
+ *   shapes/layout page, contiguity and ragged packs           (1, N, d) + cu_seqlens,
+ *                                                             J = 0 at segment heads,
+ *                                                             unsupported pins raise
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent)
+ *     unless a comment says "host".  Every tensor is dense, row-major and
+ *     contiguous in the layout given; callers copy strided views first.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after a call returns, and is re-entrant: concurrent
+ *     calls are fine as long as they use distinct workspaces and outputs.
+ *   - All work is enqueued on params->stream (a hipStream_t; NULL = the null
+ *     stream).  No entry point synchronises the host with the device.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-OK status means nothing was launched (except PRN_ERR_DEVICE, which
+ *     reports a launch failure).  prn_last_error() gives the reason.
+ *   - Storage dtype (params->dtype) applies to x, W, xproj, h0, H_out,
+ *     state_last_out and the iterates kept in the workspace.  Arithmetic is
+ *     fp32 whatever the storage dtype; stores round to nearest even.
+ */
+#ifndef PRN_H_
+#define PRN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRN_OK = 0,
+  PRN_ERR_INVALID_ARG = 1,  /* null pointer, bad size, K < 1, bad cu_seqlens  */
+  PRN_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
+  PRN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required    */
+  PRN_ERR_DEVICE = 4        /* a HIP call or kernel launch failed            */
+} prn_status;
+
+/* Cells.  Gate order inside a token's projected row:
+ *   PRN_CELL_DIAG_GRU   G = 3 gates [z | r | c], state S = 1 (h)
+ *       z = sig(x_z + a_z h), r = sig(x_r + a_r h), c = tanh(x_c + a_c r h),
+ *       h' = (1 - z) h + z c
+ *   PRN_CELL_DIAG_LSTM  G = 4 gates [i | f | o | g], state S = 2 (c, h)
+ *       i,f,o = sig(x_* + a_* h), g = tanh(x_g + a_g h),
+ *       c' = f c + i g, h' = o tanh(c')
+ * (diagonal "mix='diag'" cells of the shapes/layout page's support table) */
+enum { PRN_CELL_DIAG_GRU = 0, PRN_CELL_DIAG_LSTM = 1 };
+
+/* Storage dtypes. */
+enum { PRN_F32 = 0, PRN_BF16 = 1 };
+
+typedef struct {
+  int32_t cell;            /* PRN_CELL_DIAG_GRU | PRN_CELL_DIAG_LSTM                     */
+  int32_t dtype;           /* PRN_F32 | PRN_BF16                                          */
+  int64_t B;               /* batch rows; must be 1 for a ragged pack                     */
+  int64_t T;               /* steps per row; for a ragged pack the total token count N    */
+  int64_t d_in;            /* input width (prn_input_proj only)                           */
+  int64_t d_h;             /* hidden width = channels per gate                            */
+  int64_t n_seqs;          /* 0: rectangular batch; > 0: segments in the ragged pack      */
+  const float* a;          /* (G, d_h) fp32 diagonal recurrent weights, gate order above  */
+  void* state_last_out;    /* optional (rows, S, d_h) storage dtype: final state of every
+                              sequence (rows = B, or n_seqs for a pack); LSTM order (c, h) */
+  void* workspace;         /* device scratch owned by the caller, 256-byte aligned         */
+  size_t workspace_bytes;  /* its size; must be >= prn_workspace_bytes(params, K)         */
+  void* stream;            /* hipStream_t                                                 */
+} prn_params;
+
+/* Input projection, once per forward:
+ *   xproj[b,t,g,i] = sum_j x[b,t,j] * W[g*d_h + i, j] + bias[g*d_h + i]
+ * (the input weight W_x of the FAQs "decode_wx" / shapes page "W_x").
+ *   x      (B, T, d_in)  storage dtype
+ *   W      (G*d_h, d_in) storage dtype, rows gate-major
+ *   bias   (G*d_h) fp32, or NULL for none (LSTM callers fold the +1 forget
+ *          bias in here)
+ *   xproj_out (B, T, G, d_h) storage dtype
+ * fp32 storage multiplies in fp32 on the matrix cores; bf16 multiplies bf16
+ * with fp32 accumulation and rounds the result to bf16.  Uses no workspace. */
+prn_status prn_input_proj(const void* x, const void* W, const float* bias,
+                          const prn_params* params, void* xproj_out);
+
+/* Parallel Newton forward (the train-mode path of the FAQs' "train() vs
+ * eval()"): K iterations from the guess H = 0, then the final trajectory.
+ *   xproj      (B, T, G, d_h) storage dtype, biases included
+ *   h0         initial state (rows, S, d_h) storage dtype, or NULL for zeros;
+ *              rows = B, or n_seqs for a ragged pack (one per segment)
+ *   K          >= 1 Newton iterations (fixed; no early exit, no host sync)
+ *   cu_seqlens NULL for a rectangular batch, else (n_seqs + 1) int32
+ *              offsets with cu[0] = 0, non-decreasing, cu[n_seqs] = T, B = 1
+ *              (shapes/layout page, ragged packs).  Each segment start is a
+ *              head: J = 0 and the previous state is that segment's h0.
+ *              Empty segments are allowed; their final state is their h0.
+ *              Its contents are not read on the host; prn_validate_cu_seqlens
+ *              checks a host copy.  Malformed contents give wrong results
+ *              but never out-of-bounds accesses.
+ *   H_out      (B, T, d_h) storage dtype: h of the K-th iterate
+ *   residual_out  NULL, or (K + 1) fp32: residual_out[k] = max|F(H^(k))| over
+ *              batch, time, state component and channel, of the iterate as
+ *              stored (H^(0) = 0).  A non-finite value reads as +Inf.  The
+ *              caller applies the gate (Numerics contract: fail above 1.0).
+ * Divergence is reported through the residual, never as a status. */
+prn_status prn_newton_forward(const void* xproj, const prn_params* params, const void* h0,
+                              int32_t K, const int32_t* cu_seqlens, void* H_out,
+                              float* residual_out);
+
+/* Sequential unroll s_t = f(s_{t-1}, x_t) (the eval-mode path and the truth
+ * the Newton result must match within tau).  Arguments as for
+ * prn_newton_forward.  Uses no workspace. */
+prn_status prn_sequential_forward(const void* xproj, const prn_params* params, const void* h0,
+                                  const int32_t* cu_seqlens, void* H_out);
+
+/* Bytes of workspace prn_newton_forward needs for these params and K
+ * (0 on invalid params; see prn_last_error). */
+size_t prn_workspace_bytes(const prn_params* params, int32_t K);
+
+/* Host-side check of ragged offsets (the validate_cu_seqlens contract of
+ * the shapes/layout page): cu_host has n_seqs + 1 entries, cu[0] = 0,
+ * non-decreasing, cu[n_seqs] = N.  cu_host is a HOST pointer. */
+prn_status prn_validate_cu_seqlens(const int32_t* cu_host, int64_t n_seqs, int64_t N);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* prn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t prn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRN_H_ */

@@ -1,0 +1,16 @@
+"""Parallel Newton forward of diagonal GRU / LSTM recurrences on AMD MI355X.
+
+The compute lives in libprn.so (HIP, gfx950; C ABI in include/prn.h).
+``binding`` marshals torch tensors into that ABI under the same names;
+``api`` adds allocation, contiguity, K schedules, the residual gate and the
+agreement check.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, PrnError, lib, prn_input_proj, prn_last_error, prn_newton_forward, prn_sequential_forward,
+    prn_validate_cu_seqlens, prn_version, prn_workspace_bytes,
+)
+from .api import (  # noqa: F401
+    AGREEMENT_ATOL, AgreementError, AgreementReport, NewtonDivergenceError, RESIDUAL_FAIL, RESIDUAL_WARN,
+    forward, gate_residual, input_proj, newton_forward, resolve_k, sequential_forward, validate_cu_seqlens,
+    verify_agreement,
+)

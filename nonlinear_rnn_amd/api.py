@@ -1,0 +1,173 @@
+"""Caller-facing helpers over the C ABI: allocation, contiguity, K schedules,
+the residual gate and the agreement check.
+
+Contract points from the pararnn-torch pages that live here:
+  * shapes/layout page: fused paths copy strided views to a contiguous
+    layout first (correct results, more traffic); ragged packs are x of
+    batch 1 and length N plus cu_seqlens of length S+1, int32 or int64,
+    validated before use; an unsupported pinned combination raises rather
+    than silently running something else.
+  * FAQs, "How many Newton iterations should I use?": K pinned, or looked
+    up in a per-T table.
+  * Numerics contract, "Two thresholds" / "1. Runtime": after K steps,
+    max|F(H)| above residual_fail (1.0) raises NewtonDivergenceError; above
+    the warn band a newton_residual_high warning is issued.
+  * Numerics contract, "3. Opt-in oracle": verify_agreement runs Newton and
+    the sequential unroll on one batch and compares them (max-abs, tau).
+"""
+from __future__ import annotations
+
+import dataclasses
+import warnings
+
+import torch
+
+from . import binding as B_
+
+RESIDUAL_FAIL = 1.0
+# warn band: 1e-3 for fp32 storage; bf16 storage rounds every stored state
+# to 8 significant bits, which alone leaves |F| near 2^-9 max|h|.
+RESIDUAL_WARN = {torch.float32: 1e-3, torch.bfloat16: 2e-2}
+# agreement tau: 1e-4 in fp32 (FAQs); a wider band for bf16 storage
+AGREEMENT_ATOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+class NewtonDivergenceError(RuntimeError):
+    """max|F(H)| after K Newton steps exceeded residual_fail."""
+
+
+class AgreementError(AssertionError):
+    """Newton and the sequential unroll disagree by more than tau."""
+
+
+@dataclasses.dataclass
+class AgreementReport:
+    ok: bool
+    max_abs: float
+    atol: float
+    K: int
+    residuals: list
+    device: str
+    dtype: str
+
+    def to_dict(self) -> dict:
+        return dataclasses.asdict(self)
+
+
+def resolve_k(T: int, table: dict) -> int:
+    """K for length T from {T_key: K}: the entry with the smallest key >= T,
+    else the largest key's entry."""
+    keys = sorted(int(k) for k in table)
+    if not keys:
+        raise ValueError("empty K table")
+    for k in keys:
+        if T <= k:
+            return int(table[k])
+    return int(table[keys[-1]])
+
+
+def validate_cu_seqlens(cu_seqlens, N: int, device=None) -> torch.Tensor:
+    """Check ragged offsets on the host; return them as a contiguous int32 device tensor."""
+    cu = torch.as_tensor(cu_seqlens)
+    if cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    if cu.dtype not in (torch.int32, torch.int64):
+        raise TypeError(f"cu_seqlens must be int32 or int64, got {cu.dtype}")
+    host = cu.detach().cpu().to(torch.int64)
+    if int(host.max()) >= 2 ** 31:
+        raise ValueError("cu_seqlens values must fit in int32")
+    B_.prn_validate_cu_seqlens(host.to(torch.int32), N)
+    dev = device if device is not None else (cu.device if cu.device.type == "cuda" else "cuda")
+    return host.to(torch.int32).to(dev).contiguous()
+
+
+def _contig(t):
+    return None if t is None else t.contiguous()
+
+
+def input_proj(x, W, bias=None, *, cell: str) -> torch.Tensor:
+    x, W = x.contiguous(), W.contiguous()
+    bias = None if bias is None else bias.to(torch.float32).contiguous()
+    G = B_.GATES[cell]
+    Bn, T, _ = x.shape
+    out = torch.empty((Bn, T, G, W.shape[0] // G), dtype=x.dtype, device=x.device)
+    B_.prn_input_proj(x, W, bias, out, cell=cell)
+    return out
+
+
+def workspace_for(cell, xproj, K, n_seqs=0) -> torch.Tensor:
+    Bn, T, _, d_h = xproj.shape
+    n = B_.prn_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, K, n_seqs=n_seqs)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
+
+
+def gate_residual(residuals, dtype, residual_fail=RESIDUAL_FAIL, residual_warn=None) -> None:
+    """Apply the runtime echelon of the numerics contract to r_K (host values)."""
+    rK = float(residuals[-1])
+    if not (rK <= residual_fail):   # also catches NaN / Inf
+        raise NewtonDivergenceError(
+            f"max|F(H)| = {rK:.3e} after K = {len(residuals) - 1} Newton steps exceeds residual_fail = "
+            f"{residual_fail}; skip the optimizer step on this batch")
+    warn = RESIDUAL_WARN.get(dtype, 1e-3) if residual_warn is None else residual_warn
+    if rK > warn:
+        warnings.warn(f"newton_residual_high: max|F(H)| = {rK:.3e} > {warn:.1e}", RuntimeWarning, stacklevel=3)
+
+
+def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_table=None,
+                   residual_fail=RESIDUAL_FAIL, residual_warn=None, gate=True, return_state=False):
+    """Parallel Newton forward.  Returns (H (B,T,d_h), residuals [r_0..r_K] on
+    the host[, final states]).  K may be None with a k_table."""
+    xproj = xproj.contiguous()
+    a = a.to(torch.float32).contiguous()
+    Bn, T, _, d_h = xproj.shape
+    if k_table is not None and K is None:
+        K = resolve_k(T, k_table)
+    if K is None or int(K) < 1:
+        raise ValueError("K must be >= 1")
+    K = int(K)
+    cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
+    n_seqs = 0 if cu is None else cu.numel() - 1
+    rows = Bn if cu is None else n_seqs
+    H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
+    res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
+    st = (torch.empty((rows, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
+          if return_state else None)
+    ws = workspace_for(cell, xproj, K, n_seqs)
+    B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=_contig(h0), cu_seqlens=cu, residual_out=res,
+                          state_last_out=st, workspace=ws)
+    residuals = res.cpu().tolist()   # the one host sync of a forward
+    if gate:
+        gate_residual(residuals, xproj.dtype, residual_fail, residual_warn)
+    return (H, residuals, st) if return_state else (H, residuals)
+
+
+def sequential_forward(xproj, a, *, cell: str, h0=None, cu_seqlens=None, return_state=False):
+    xproj = xproj.contiguous()
+    a = a.to(torch.float32).contiguous()
+    Bn, T, _, d_h = xproj.shape
+    cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
+    rows = Bn if cu is None else cu.numel() - 1
+    H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
+    st = (torch.empty((rows, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
+          if return_state else None)
+    B_.prn_sequential_forward(xproj, a, H, cell=cell, h0=_contig(h0), cu_seqlens=cu, state_last_out=st)
+    return (H, st) if return_state else H
+
+
+def forward(x, W, bias, a, K=3, *, cell: str, **kw):
+    """Projection + Newton: the train-mode forward of one diagonal layer."""
+    return newton_forward(input_proj(x, W, bias, cell=cell), a, K, cell=cell, **kw)
+
+
+def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol=None,
+                     raise_on_fail=False) -> AgreementReport:
+    """Run Newton and the sequential unroll on one batch; compare max-abs to tau."""
+    H_n, res = newton_forward(xproj, a, K, cell=cell, h0=h0, cu_seqlens=cu_seqlens, gate=False)
+    H_s = sequential_forward(xproj, a, cell=cell, h0=h0, cu_seqlens=cu_seqlens)
+    atol = AGREEMENT_ATOL.get(xproj.dtype, 1e-4) if atol is None else atol
+    m = float((H_n.float() - H_s.float()).abs().max()) if H_n.numel() else 0.0
+    rep = AgreementReport(ok=bool(m <= atol), max_abs=m, atol=atol, K=K, residuals=res,
+                          device=str(xproj.device), dtype=str(xproj.dtype))
+    if raise_on_fail and not rep.ok:
+        raise AgreementError(f"Newton vs sequential max_abs {m:.3e} > tau {atol:.1e}: {rep.to_dict()}")
+    return rep

@@ -1,0 +1,203 @@
+"""ctypes binding of libprn (include/prn.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors that live on the GPU (torch provides device memory and streams),
+checks that their shapes, dtypes and layouts are what the C ABI expects, and
+raises PrnError with the library's message on a non-OK status.  All
+arithmetic happens in the HIP library; if the library is missing, loading
+fails loudly (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PRN_LIB", os.path.join(HERE, "libprn.so"))
+
+PRN_OK, PRN_ERR_INVALID_ARG, PRN_ERR_UNSUPPORTED, PRN_ERR_WORKSPACE, PRN_ERR_DEVICE = range(5)
+STATUS_NAMES = {0: "PRN_OK", 1: "PRN_ERR_INVALID_ARG", 2: "PRN_ERR_UNSUPPORTED",
+                3: "PRN_ERR_WORKSPACE", 4: "PRN_ERR_DEVICE"}
+CELLS = {"gru": 0, "lstm": 1}
+GATES = {"gru": 3, "lstm": 4}
+STATE = {"gru": 1, "lstm": 2}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+# every symbol include/prn.h declares
+EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_workspace_bytes",
+           "prn_validate_cu_seqlens", "prn_last_error", "prn_version")
+
+
+class PrnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class prn_params(ctypes.Structure):
+    _fields_ = [
+        ("cell", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_h", ctypes.c_int64),
+        ("n_seqs", ctypes.c_int64),
+        ("a", ctypes.c_void_p),
+        ("state_last_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libprn.so (built by nonlinear_rnn_amd.build); raise if it is not there."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libprn not built: {LIB_PATH} is missing "
+                               "(run python -m nonlinear_rnn_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(prn_params)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.prn_input_proj.argtypes = [vp, vp, vp, P, vp]
+        L.prn_newton_forward.argtypes = [vp, P, vp, i32, vp, vp, vp]
+        L.prn_sequential_forward.argtypes = [vp, P, vp, vp, vp]
+        L.prn_workspace_bytes.argtypes = [P, i32]
+        L.prn_workspace_bytes.restype = ctypes.c_size_t
+        L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
+        L.prn_last_error.restype = ctypes.c_char_p
+        L.prn_version.restype = i32
+        for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward",
+                     "prn_validate_cu_seqlens"):
+            getattr(L, name).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def prn_last_error() -> str:
+    return lib().prn_last_error().decode()
+
+
+def prn_version() -> int:
+    return int(lib().prn_version())
+
+
+def _check(status: int) -> None:
+    if status != PRN_OK:
+        raise PrnError(status, prn_last_error())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in: int = 0, n_seqs: int = 0,
+                a=None, state_last_out=None, workspace=None, stream=None) -> prn_params:
+    if cell not in CELLS:
+        raise ValueError(f"unknown cell {cell!r}")
+    if dtype not in DTYPES:
+        raise TypeError(f"unsupported storage dtype {dtype}")
+    p = prn_params()
+    p.cell, p.dtype = CELLS[cell], DTYPES[dtype]
+    p.B, p.T, p.d_in, p.d_h, p.n_seqs = B, T, d_in, d_h, n_seqs
+    p.a = _ptr(a)
+    p.state_last_out = _ptr(state_last_out)
+    if workspace is not None:
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    p.stream = _stream(stream) if torch.cuda.is_available() else 0
+    return p
+
+
+def prn_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, K: int, n_seqs: int = 0) -> int:
+    p = make_params(cell, dtype, B, T, d_h, n_seqs=n_seqs)
+    n = int(lib().prn_workspace_bytes(ctypes.byref(p), K))
+    if n == 0 and prn_last_error():
+        raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
+    return n
+
+
+def prn_validate_cu_seqlens(cu_host, N: int) -> None:
+    """Check ragged offsets on a host int32 array / CPU tensor."""
+    import numpy as np
+    arr = np.ascontiguousarray(torch.as_tensor(cu_host).cpu().numpy(), dtype=np.int32)
+    _check(lib().prn_validate_cu_seqlens(arr.ctypes.data, arr.size - 1, N))
+
+
+def prn_input_proj(x, W, bias, xproj_out, *, cell: str, stream=None) -> None:
+    """xproj_out (B,T,G,d_h) = x (B,T,d_in) @ W (G*d_h, d_in)^T + bias (G*d_h)."""
+    _dev(x, "x")
+    _dev(W, "W", x.dtype)
+    _dev(bias, "bias", torch.float32)
+    _dev(xproj_out, "xproj_out", x.dtype)
+    B, T, d_in = x.shape
+    G = GATES[cell]
+    d_h = W.shape[0] // G
+    if W.shape != (G * d_h, d_in) or xproj_out.shape != (B, T, G, d_h):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} W {tuple(W.shape)} xproj {tuple(xproj_out.shape)}")
+    if bias is not None and bias.shape != (G * d_h,):
+        raise ValueError("bias must have G*d_h entries")
+    p = make_params(cell, x.dtype, B, T, d_h, d_in=d_in, stream=stream)
+    _check(lib().prn_input_proj(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(xproj_out)))
+
+
+def _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell):
+    _dev(xproj, "xproj")
+    _dev(a, "a", torch.float32)
+    _dev(H_out, "H_out", xproj.dtype)
+    _dev(h0, "h0", xproj.dtype)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(state_last_out, "state_last_out", xproj.dtype)
+    B, T, G, d_h = xproj.shape
+    if G != GATES[cell] or a.shape != (G, d_h) or H_out.shape != (B, T, d_h):
+        raise ValueError(f"shape mismatch: xproj {tuple(xproj.shape)} a {tuple(a.shape)} H_out {tuple(H_out.shape)}")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rows = B if cu_seqlens is None else n_seqs
+    S = STATE[cell]
+    for t, name in ((h0, "h0"), (state_last_out, "state_last_out")):
+        if t is not None and t.shape != (rows, S, d_h):
+            raise ValueError(f"{name} must be {(rows, S, d_h)}, got {tuple(t.shape)}")
+    return B, T, d_h, n_seqs
+
+
+def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None, residual_out=None,
+                       state_last_out=None, workspace=None, stream=None) -> None:
+    B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
+    _dev(residual_out, "residual_out", torch.float32)
+    if residual_out is not None and residual_out.numel() < K + 1:
+        raise ValueError("residual_out needs K + 1 entries")
+    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
+                    workspace=workspace, stream=stream)
+    _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
+                                    _ptr(H_out), _ptr(residual_out)))
+
+
+def prn_sequential_forward(xproj, a, H_out, *, cell: str, h0=None, cu_seqlens=None, state_last_out=None,
+                           stream=None) -> None:
+    B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
+    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
+                    stream=stream)
+    _check(lib().prn_sequential_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), _ptr(cu_seqlens), _ptr(H_out)))

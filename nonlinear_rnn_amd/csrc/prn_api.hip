@@ -1,0 +1,283 @@
+// Host side of libprn: argument validation, workspace planning and the
+// launch sequence of every entry point declared in include/prn.h.
+//
+// Nothing here synchronises with the device; everything is enqueued on the
+// caller's stream (FAQs, "Does torch.compile / autocast work?": a fixed-K
+// loop with no residual host sync).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "newton_kernels.h"
+#include "proj.h"
+#include "prn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+prn_status fail(prn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// three-phase geometry: lanes = 64 channels, NW waves of LS serial steps
+constexpr int kLS = 8;
+constexpr int kNW = 4;
+constexpr int kLC = kLS * kNW;
+constexpr int kScanSeg = 16;
+constexpr int64_t kMaxGrid = 65535;
+
+struct Shape {
+  int G, S;
+  size_t elt;       // bytes per stored element
+  int64_t rows;     // sequences: B, or n_seqs for a ragged pack
+  bool ragged;
+};
+
+prn_status check_common(const prn_params* p, Shape* sh) {
+  if (!p) return fail(PRN_ERR_INVALID_ARG, "params is NULL");
+  if (p->cell != PRN_CELL_DIAG_GRU && p->cell != PRN_CELL_DIAG_LSTM)
+    return fail(PRN_ERR_INVALID_ARG, "unknown cell %d", p->cell);
+  if (p->dtype != PRN_F32 && p->dtype != PRN_BF16)
+    return fail(PRN_ERR_INVALID_ARG, "unknown storage dtype %d", p->dtype);
+  if (p->B < 1 || p->T < 0 || p->d_h < 1)
+    return fail(PRN_ERR_INVALID_ARG, "bad sizes B=%lld T=%lld d_h=%lld", (long long)p->B,
+                (long long)p->T, (long long)p->d_h);
+  if (p->n_seqs < 0) return fail(PRN_ERR_INVALID_ARG, "n_seqs < 0");
+  if (p->n_seqs > 0 && p->B != 1)
+    return fail(PRN_ERR_INVALID_ARG, "a ragged pack (n_seqs > 0) needs B == 1, got B=%lld", (long long)p->B);
+  if (p->B > kMaxGrid || p->n_seqs > kMaxGrid || (p->d_h + 63) / 64 > kMaxGrid)
+    return fail(PRN_ERR_UNSUPPORTED, "B, n_seqs and d_h/64 must each be <= %lld", (long long)kMaxGrid);
+  sh->G = p->cell == PRN_CELL_DIAG_GRU ? 3 : 4;
+  sh->S = p->cell == PRN_CELL_DIAG_GRU ? 1 : 2;
+  sh->elt = p->dtype == PRN_F32 ? 4 : 2;
+  sh->ragged = p->n_seqs > 0;
+  sh->rows = sh->ragged ? p->n_seqs : p->B;
+  const double elems = double(p->B) * double(p->T) * sh->G * double(p->d_h);
+  if (elems > 4.0e18) return fail(PRN_ERR_INVALID_ARG, "tensor too large");
+  return PRN_OK;
+}
+
+bool misaligned(const void* ptr, size_t elt) { return ptr && (reinterpret_cast<uintptr_t>(ptr) % elt) != 0; }
+
+prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* xproj, const void* h0,
+                             const int32_t* cu, const void* H_out) {
+  if (!p->a) return fail(PRN_ERR_INVALID_ARG, "recurrent weights a is NULL");
+  if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
+  if (sh.ragged && !cu) return fail(PRN_ERR_INVALID_ARG, "n_seqs > 0 but cu_seqlens is NULL");
+  if (!sh.ragged && cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
+  if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(H_out, sh.elt) ||
+      misaligned(p->state_last_out, sh.elt) || misaligned(p->a, 4) || misaligned(cu, 4))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
+  return PRN_OK;
+}
+
+struct Plan {
+  int64_t n_ch;
+  int nbuf;  // iterate buffers: H^(k) for k = 1..K-1 lives in buffer (k - 1) % 2
+  size_t agg_off, carry_off, it_off[2], it_bytes, total;
+};
+
+Plan plan_tp(const prn_params* p, const Shape& sh, int K) {
+  Plan pl{};
+  pl.n_ch = (p->T + kLC - 1) / kLC;
+  const size_t NC = sh.S * sh.S + sh.S;
+  const size_t agg = align_up(size_t(p->B) * pl.n_ch * NC * p->d_h * 4);
+  const size_t car = align_up(size_t(p->B) * pl.n_ch * sh.S * p->d_h * 4);
+  const size_t it = align_up(size_t(p->B) * p->T * sh.S * p->d_h * sh.elt);
+  pl.nbuf = K >= 3 ? 2 : (K == 2 ? 1 : 0);
+  pl.agg_off = 0;
+  pl.carry_off = agg;
+  pl.it_off[0] = agg + car;
+  pl.it_off[1] = agg + car + it;
+  pl.it_bytes = it;
+  pl.total = agg + car + pl.nbuf * it;
+  return pl;
+}
+
+prn_status launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PRN_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return PRN_OK;
+}
+
+template <int DT>
+void final_states_empty(const prn_params* p, const Shape& sh, const void* h0, const int32_t* cu,
+                        hipStream_t st) {
+  using T = typename prn::Storage<DT>::T;
+  if (!p->state_last_out || !sh.ragged) return;
+  const int64_t n = p->n_seqs * sh.S * p->d_h;
+  const int S = sh.S;
+  const dim3 grid(unsigned((n + 255) / 256));
+  if (S == 1)
+    prn::k_empty_segments<DT, 1><<<grid, 256, 0, st>>>(cu, p->n_seqs, p->d_h, static_cast<const T*>(h0),
+                                                      static_cast<T*>(p->state_last_out));
+  else
+    prn::k_empty_segments<DT, 2><<<grid, 256, 0, st>>>(cu, p->n_seqs, p->d_h, static_cast<const T*>(h0),
+                                                      static_cast<T*>(p->state_last_out));
+}
+
+template <class C, int DT>
+prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, const void* h0_v, int K,
+                     const int32_t* cu, void* Hout_v, float* res) {
+  using T = typename prn::Storage<DT>::T;
+  constexpr int S = C::S;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const Plan pl = plan_tp(p, sh, K);
+  const T* xproj = static_cast<const T*>(xproj_v);
+  const T* h0 = static_cast<const T*>(h0_v);
+  T* Hout = static_cast<T*>(Hout_v);
+  T* slast = static_cast<T*>(p->state_last_out);
+  char* ws = static_cast<char*>(p->workspace);
+  float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
+  float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
+  // H^(k) (k = 1..K-1) is stored in iterate buffer (k - 1) % 2; iteration k
+  // reads buffer (k - 2) % 2 and writes (k - 1) % 2, never the same one.
+  auto iter_buf = [&](int k) -> T* {
+    const int i = (k - 1) & 1;
+    if (k < 1 || k >= K || i >= pl.nbuf || pl.it_off[i] + pl.it_bytes > pl.total) return nullptr;
+    return reinterpret_cast<T*>(ws + pl.it_off[i]);
+  };
+  for (int k = 1; k < K; ++k)
+    if (!iter_buf(k)) return fail(PRN_ERR_WORKSPACE, "internal: iterate %d has no workspace buffer", k);
+  unsigned int* r = reinterpret_cast<unsigned int*>(res);
+  auto slot = [&](int k) { return r ? r + k : nullptr; };
+
+  if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
+  const dim3 grid(unsigned(pl.n_ch), unsigned((p->d_h + 63) / 64), unsigned(p->B));
+  const dim3 block(64 * kNW);
+  const dim3 sgrid(unsigned((p->d_h + 63) / 64), unsigned(p->B));
+  const dim3 sblock(64 * kScanSeg);
+  if (p->T > 0) {
+    prn::k_tp_first<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, h0, cu, p->a, p->T, p->d_h, p->n_seqs,
+                                                             pl.n_ch, agg, slot(0));
+    prn::k_tp_scan<S, kScanSeg><<<sgrid, sblock, 0, st>>>(agg, carry, p->d_h, pl.n_ch);
+    for (int k = 1; k < K; ++k) {
+      const T* hprev = k == 1 ? nullptr : iter_buf(k - 1);
+      prn::k_tp_fix<C, DT, kLS, kNW, true, false><<<grid, block, 0, st>>>(
+          xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, iter_buf(k), nullptr, nullptr,
+          agg, slot(k));
+      prn::k_tp_scan<S, kScanSeg><<<sgrid, sblock, 0, st>>>(agg, carry, p->d_h, pl.n_ch);
+    }
+    const T* hprev = K == 1 ? nullptr : iter_buf(K - 1);
+    prn::k_tp_fix<C, DT, kLS, kNW, false, true><<<grid, block, 0, st>>>(
+        xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, nullptr, Hout, slast, nullptr,
+        slot(K));
+  } else if (slast && !sh.ragged) {
+    // zero-length rows: the final state is the initial state
+    const int64_t n = p->B * S * p->d_h;
+    prn::k_copy_or_zero<T><<<unsigned((n + 255) / 256), 256, 0, st>>>(h0, slast, n);
+  }
+  final_states_empty<DT>(p, sh, h0_v, cu, st);
+  return launched("prn_newton_forward");
+}
+
+template <class C, int DT>
+prn_status sequential(const prn_params* p, const Shape& sh, const void* xproj_v, const void* h0_v,
+                      const int32_t* cu, void* Hout_v) {
+  using T = typename prn::Storage<DT>::T;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const dim3 grid(unsigned((p->d_h + 63) / 64), unsigned(sh.rows));
+  prn::k_sequential<C, DT><<<grid, 64, 0, st>>>(static_cast<const T*>(xproj_v), static_cast<const T*>(h0_v), cu,
+                                                p->a, p->T, p->d_h, p->n_seqs, static_cast<T*>(Hout_v),
+                                                static_cast<T*>(p->state_last_out));
+  return launched("prn_sequential_forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t prn_version(void) { return 100; }
+
+const char* prn_last_error(void) { return g_err.c_str(); }
+
+prn_status prn_validate_cu_seqlens(const int32_t* cu, int64_t n_seqs, int64_t N) {
+  if (!cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (n_seqs < 1) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens needs at least 2 entries (n_seqs >= 1)");
+  if (cu[0] != 0) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int64_t j = 0; j < n_seqs; ++j)
+    if (cu[j + 1] < cu[j])
+      return fail(PRN_ERR_INVALID_ARG, "cu_seqlens decreases at %lld (%d -> %d)", (long long)j, cu[j], cu[j + 1]);
+  if (cu[n_seqs] != N)
+    return fail(PRN_ERR_INVALID_ARG, "cu_seqlens[-1] = %d, expected N = %lld", cu[n_seqs], (long long)N);
+  return PRN_OK;
+}
+
+size_t prn_workspace_bytes(const prn_params* p, int32_t K) {
+  Shape sh;
+  if (check_common(p, &sh) != PRN_OK) return 0;
+  if (K < 1) {
+    fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+    return 0;
+  }
+  return plan_tp(p, sh, K).total;
+}
+
+prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void* h0, int32_t K,
+                              const int32_t* cu, void* H_out, float* residual_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+  if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
+  if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
+  const size_t need = plan_tp(p, sh, K).total;
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
+                p->workspace, need);
+  if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+    return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32) return newton_tp<prn::CellGRU, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+    return newton_tp<prn::CellGRU, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+  }
+  if (p->dtype == PRN_F32) return newton_tp<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+  return newton_tp<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+}
+
+prn_status prn_sequential_forward(const void* xproj, const prn_params* p, const void* h0, const int32_t* cu,
+                                  void* H_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32) return sequential<prn::CellGRU, prn::kF32>(p, sh, xproj, h0, cu, H_out);
+    return sequential<prn::CellGRU, prn::kBF16>(p, sh, xproj, h0, cu, H_out);
+  }
+  if (p->dtype == PRN_F32) return sequential<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, cu, H_out);
+  return sequential<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, cu, H_out);
+}
+
+prn_status prn_input_proj(const void* x, const void* W, const float* bias, const prn_params* p, void* xproj_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (p->d_in < 1) return fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
+  const int64_t M = p->B * p->T, N = sh.G * p->d_h, Kd = p->d_in;
+  if (M == 0) return PRN_OK;
+  if (!x || !W || !xproj_out) return fail(PRN_ERR_INVALID_ARG, "x, W or xproj_out is NULL");
+  if (misaligned(x, 16) || misaligned(W, 16) || misaligned(xproj_out, 16) || misaligned(bias, 4))
+    return fail(PRN_ERR_INVALID_ARG, "x, W and xproj_out must be 16-byte aligned");
+  const int kvec = p->dtype == PRN_F32 ? 4 : 8;
+  if (Kd % kvec != 0)
+    return fail(PRN_ERR_UNSUPPORTED, "input projection needs d_in %% %d == 0 for this storage dtype", kvec);
+  if (M > (int64_t(1) << 31) * 128 || N > (int64_t(1) << 31))
+    return fail(PRN_ERR_UNSUPPORTED, "input projection too large");
+  prn::launch_proj(p->dtype == PRN_BF16, x, W, bias, xproj_out, M, N, Kd, static_cast<hipStream_t>(p->stream));
+  return launched("prn_input_proj");
+}
+
+}  // extern "C"

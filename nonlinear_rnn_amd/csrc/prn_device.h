@@ -1,0 +1,231 @@
+// Device building blocks shared by the Newton, scan and sequential kernels:
+// storage-dtype loads/stores, fast transcendentals, the two diagonal cells
+// with their closed-form per-channel Jacobians, and per-channel affine maps.
+//
+// Everything is fp32 arithmetic whatever the storage dtype (FAQs, "What about
+// Turing GPUs": the algebra inside the kernel stays fp32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prn {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int64_t imin(int64_t x, int64_t y) { return x < y ? x : y; }
+__device__ __forceinline__ int64_t imax(int64_t x, int64_t y) { return x > y ? x : y; }
+
+// ----------------------------------------------------------- dtypes -------
+
+enum StorageType { kF32 = 0, kBF16 = 1 };
+
+template <int DT> struct Storage;
+template <> struct Storage<kF32> {
+  using T = float;
+  static __device__ __forceinline__ float load(const T* p) { return *p; }
+  static __device__ __forceinline__ T pack(float v) { return v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+template <> struct Storage<kBF16> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float load(const T* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+  // round to nearest, ties to even; NaN stays a (quiet) NaN
+  static __device__ __forceinline__ T pack(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<T>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<T>(u >> 16);
+  }
+  static __device__ __forceinline__ float round(float v) {
+    return __uint_as_float(static_cast<uint32_t>(pack(v)) << 16);
+  }
+};
+
+// ------------------------------------------------- transcendentals -------
+// v_exp_f32 computes 2^x and v_rcp_f32 1/x, each to about 1 ulp.  The
+// logistic function and tanh are built from them:
+//   sig(u)  = 1 / (1 + 2^(-u log2 e))
+//   tanh(u) = 2 sig(2u) - 1
+// Saturation is exact at both ends (2^(+big) = inf -> rcp = 0).
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigm(float u) { return rcp(1.0f + ex2(u * -kLog2e)); }
+__device__ __forceinline__ float tanh_(float u) {
+  return fmaf(2.0f, rcp(1.0f + ex2(u * (-2.0f * kLog2e))), -1.0f);
+}
+
+// |x| with NaN mapped to +Inf, so that a max over residuals never drops a NaN
+__device__ __forceinline__ float abs_nan_inf(float x) {
+  const float v = fabsf(x);
+  return __builtin_isnan(v) ? __builtin_inff() : v;
+}
+
+// ---------------------------------------------------- affine maps --------
+// One channel's map s -> A s + b (S = 1 or 2).  compose(m2, m1) is "m2 after
+// m1": (A2 A1, A2 b1 + b2).
+
+template <int S> struct Aff;
+template <> struct Aff<1> {
+  float a, b;
+  static __device__ __forceinline__ Aff identity() { return {1.0f, 0.0f}; }
+};
+template <> struct Aff<2> {
+  float a00, a01, a10, a11, b0, b1;
+  static __device__ __forceinline__ Aff identity() { return {1.0f, 0.0f, 0.0f, 1.0f, 0.0f, 0.0f}; }
+};
+
+__device__ __forceinline__ Aff<1> compose(const Aff<1>& m2, const Aff<1>& m1) {
+  return {m2.a * m1.a, fmaf(m2.a, m1.b, m2.b)};
+}
+__device__ __forceinline__ Aff<2> compose(const Aff<2>& m2, const Aff<2>& m1) {
+  Aff<2> r;
+  r.a00 = fmaf(m2.a00, m1.a00, m2.a01 * m1.a10);
+  r.a01 = fmaf(m2.a00, m1.a01, m2.a01 * m1.a11);
+  r.a10 = fmaf(m2.a10, m1.a00, m2.a11 * m1.a10);
+  r.a11 = fmaf(m2.a10, m1.a01, m2.a11 * m1.a11);
+  r.b0 = fmaf(m2.a00, m1.b0, fmaf(m2.a01, m1.b1, m2.b0));
+  r.b1 = fmaf(m2.a10, m1.b0, fmaf(m2.a11, m1.b1, m2.b1));
+  return r;
+}
+__device__ __forceinline__ void apply(const Aff<1>& m, float* s) { s[0] = fmaf(m.a, s[0], m.b); }
+__device__ __forceinline__ void apply(const Aff<2>& m, float* s) {
+  const float c = s[0], h = s[1];
+  s[0] = fmaf(m.a00, c, fmaf(m.a01, h, m.b0));
+  s[1] = fmaf(m.a10, c, fmaf(m.a11, h, m.b1));
+}
+
+// --------------------------------------------------------- cells ---------
+// fj(): f(s) and the per-channel Jacobian J = df/ds at state s, packed as the
+// Newton map (J, b = f - J s).  At a segment head the caller passes head =
+// true: J := 0 and b := f(h0) (shapes/layout page: J = 0 on the scan).
+// f(): the cell value only (residual of the final iterate).
+
+struct CellGRU {
+  static constexpr int G = 3, S = 1;
+  using Map = Aff<1>;
+  // x: [z, r, c] projected inputs; s: [h]; a: [a_z, a_r, a_c]
+  static __device__ __forceinline__ void f(const float* x, const float* s, const float* a, float* out) {
+    const float h = s[0];
+    const float z = sigm(fmaf(a[0], h, x[0]));
+    const float r = sigm(fmaf(a[1], h, x[1]));
+    const float c = tanh_(fmaf(a[2], r * h, x[2]));
+    out[0] = fmaf(z, c - h, h);
+  }
+  static __device__ __forceinline__ Map fj(const float* x, const float* s, const float* a, bool head,
+                                           float* fout) {
+    const float h = s[0];
+    const float z = sigm(fmaf(a[0], h, x[0]));
+    const float r = sigm(fmaf(a[1], h, x[1]));
+    const float c = tanh_(fmaf(a[2], r * h, x[2]));
+    const float fv = fmaf(z, c - h, h);
+    fout[0] = fv;
+    if (head) return {0.0f, fv};
+    const float omz = 1.0f - z;
+    const float dz = z * omz * a[0];
+    const float dr = r * (1.0f - r) * a[1];
+    const float dc = fmaf(-c, c, 1.0f) * a[2] * fmaf(h, dr, r);
+    const float J = fmaf(z, dc, fmaf(c - h, dz, omz));
+    return {J, fmaf(-J, h, fv)};
+  }
+};
+
+struct CellLSTM {
+  static constexpr int G = 4, S = 2;
+  using Map = Aff<2>;
+  // x: [i, f, o, g]; s: [c, h]; a: [a_i, a_f, a_o, a_g]
+  static __device__ __forceinline__ void f(const float* x, const float* s, const float* a, float* out) {
+    const float c = s[0], h = s[1];
+    const float ig = sigm(fmaf(a[0], h, x[0]));
+    const float fg = sigm(fmaf(a[1], h, x[1]));
+    const float og = sigm(fmaf(a[2], h, x[2]));
+    const float gg = tanh_(fmaf(a[3], h, x[3]));
+    const float c1 = fmaf(fg, c, ig * gg);
+    out[0] = c1;
+    out[1] = og * tanh_(c1);
+  }
+  static __device__ __forceinline__ Map fj(const float* x, const float* s, const float* a, bool head,
+                                           float* fout) {
+    const float c = s[0], h = s[1];
+    const float ig = sigm(fmaf(a[0], h, x[0]));
+    const float fg = sigm(fmaf(a[1], h, x[1]));
+    const float og = sigm(fmaf(a[2], h, x[2]));
+    const float gg = tanh_(fmaf(a[3], h, x[3]));
+    const float c1 = fmaf(fg, c, ig * gg);
+    const float tc = tanh_(c1);
+    const float h1 = og * tc;
+    fout[0] = c1;
+    fout[1] = h1;
+    if (head) return {0.0f, 0.0f, 0.0f, 0.0f, c1, h1};
+    const float di = ig * (1.0f - ig) * a[0];
+    const float df = fg * (1.0f - fg) * a[1];
+    const float dO = og * (1.0f - og) * a[2];
+    const float dg = fmaf(-gg, gg, 1.0f) * a[3];
+    const float j01 = fmaf(c, df, fmaf(gg, di, ig * dg));   // dc'/dh
+    const float odt = og * fmaf(-tc, tc, 1.0f);             // o (1 - tanh^2 c')
+    const float j10 = odt * fg;                             // dh'/dc
+    const float j11 = fmaf(tc, dO, odt * j01);              // dh'/dh
+    Map m;
+    m.a00 = fg;
+    m.a01 = j01;
+    m.a10 = j10;
+    m.a11 = j11;
+    m.b0 = c1 - fmaf(fg, c, j01 * h);
+    m.b1 = h1 - fmaf(j10, c, j11 * h);
+    return m;
+  }
+};
+
+// ------------------------------------------------ segment tracking -------
+// Which steps are segment heads, and which segment a step belongs to.
+// Rectangular batch: row b is one segment (index b) starting at t = 0.
+// Ragged pack: segment j covers [cu[j], cu[j+1]); empty segments are
+// skipped.  Indices stay in [0, n_seqs) whatever cu holds.
+
+struct SegTracker {
+  const int32_t* cu;  // null for a rectangular batch
+  int64_t n_seqs;
+  int64_t seg;        // current segment (row b for a rectangular batch)
+  int64_t start;      // first step of the current segment
+  int64_t next;       // first step of the next segment (INT64_MAX if none)
+
+  __device__ __forceinline__ void init(const int32_t* cu_, int64_t n_seqs_, int64_t row, int64_t t0) {
+    cu = cu_;
+    n_seqs = n_seqs_;
+    if (!cu) {
+      seg = row;
+      start = 0;
+      next = INT64_MAX;
+      return;
+    }
+    // largest j in [0, n_seqs) with cu[j] <= t0
+    int64_t lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (static_cast<int64_t>(cu[mid]) <= t0) lo = mid; else hi = mid - 1;
+    }
+    seg = lo;
+    start = cu[seg];
+    next = (seg + 1 < n_seqs) ? static_cast<int64_t>(cu[seg + 1]) : INT64_MAX;
+  }
+  // advance to step t (t non-decreasing); returns true if t is a head
+  __device__ __forceinline__ bool at(int64_t t) {
+    if (cu) {
+      while (next <= t) {
+        ++seg;
+        start = next;
+        next = (seg + 1 < n_seqs) ? static_cast<int64_t>(cu[seg + 1]) : INT64_MAX;
+      }
+    }
+    return t == start || t == 0;  // the first step of a row is always a head
+  }
+  // is t the last step of its segment (T = steps in the row)?
+  __device__ __forceinline__ bool last(int64_t t, int64_t T) const { return t + 1 == next || t + 1 == T; }
+};
+
+}  // namespace prn

@@ -1,0 +1,133 @@
+"""CPU-only checks of the C ABI: libprn loads, exports every symbol of
+include/prn.h, and rejects bad arguments on the host before launching
+anything (no GPU needed, no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import nonlinear_rnn_amd as prn
+from nonlinear_rnn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libprn.so not built")
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "prn.h")).read()
+    return sorted(set(re.findall(r"\b(prn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree_and_library_exports_all():
+    syms = header_symbols()
+    assert syms == sorted(B.EXPORTS)
+    L = B.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert B.prn_version() >= 100
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Field offsets of the ctypes mirror equal what a C compiler makes of prn.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = [f[0] for f in B.prn_params._fields_]
+    src = tmp_path / "off.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "prn.h"\nint main(void){\n'
+                   + "".join(f'printf("%zu\\n", offsetof(prn_params, {n}));\n' for n in names)
+                   + 'printf("%zu\\n", sizeof(prn_params));return 0;}\n')
+    exe = tmp_path / "off"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [getattr(B.prn_params, n).offset for n in names] + [ctypes.sizeof(B.prn_params)]
+    assert got == want
+
+
+def _params(**kw):
+    p = B.prn_params()
+    p.cell, p.dtype, p.B, p.T, p.d_in, p.d_h, p.n_seqs = 0, 0, 2, 100, 8, 16, 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+FAKE = 1 << 20   # an aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,K,status", [
+    (dict(cell=7), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(dtype=5), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(B=0), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(d_h=0), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(T=-1), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(), 0, B.PRN_ERR_INVALID_ARG),
+    (dict(n_seqs=3), 3, B.PRN_ERR_INVALID_ARG),                       # B=2 with a pack
+    (dict(a=None), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), 3, B.PRN_ERR_WORKSPACE),                          # no workspace given
+    (dict(a=FAKE, workspace=FAKE, workspace_bytes=16), 3, B.PRN_ERR_WORKSPACE),
+    (dict(a=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),                    # misaligned
+])
+def test_newton_forward_rejects_bad_arguments_before_launch(kw, K, status):
+    p = _params(**kw)
+    st = B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, K, None, FAKE, None)
+    assert st == status, B.prn_last_error()
+    assert B.prn_last_error()
+
+
+def test_newton_forward_rejects_pack_inconsistency():
+    p = _params(B=1, a=FAKE)
+    assert B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, FAKE, FAKE, None) == B.PRN_ERR_INVALID_ARG
+    p = _params(B=1, n_seqs=4, a=FAKE)
+    assert B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None) == B.PRN_ERR_INVALID_ARG
+
+
+def test_input_proj_rejects_unsupported_shapes():
+    p = _params(d_in=6)   # fp32 needs d_in % 4 == 0
+    assert B.lib().prn_input_proj(FAKE, FAKE, None, ctypes.byref(p), FAKE) == B.PRN_ERR_UNSUPPORTED
+    p = _params(d_in=8)
+    assert B.lib().prn_input_proj(None, FAKE, None, ctypes.byref(p), FAKE) == B.PRN_ERR_INVALID_ARG
+
+
+def test_workspace_bytes_grows_with_K_and_is_zero_on_bad_params():
+    w1 = B.prn_workspace_bytes("lstm", torch.float32, 2, 1000, 64, 1)
+    w2 = B.prn_workspace_bytes("lstm", torch.float32, 2, 1000, 64, 2)
+    w3 = B.prn_workspace_bytes("lstm", torch.float32, 2, 1000, 64, 3)
+    assert 0 < w1 < w2 < w3
+    assert w3 % 256 == 0
+    p = _params(d_h=0)
+    assert B.lib().prn_workspace_bytes(ctypes.byref(p), 3) == 0
+
+
+@pytest.mark.parametrize("cu,N,ok", [
+    ([0, 5, 5, 9], 9, True),
+    ([0, 9], 9, True),
+    ([1, 5, 9], 9, False),
+    ([0, 6, 5, 9], 9, False),
+    ([0, 5, 8], 9, False),
+    ([0], 0, False),
+])
+def test_validate_cu_seqlens(cu, N, ok):
+    if ok:
+        B.prn_validate_cu_seqlens(np.array(cu), N)
+    else:
+        with pytest.raises(B.PrnError):
+            B.prn_validate_cu_seqlens(np.array(cu), N)
+
+
+def test_k_table_and_residual_gate_on_host():
+    assert prn.resolve_k(100, {64: 2, 1024: 3}) == 3
+    assert prn.resolve_k(10 ** 6, {64: 2, 1024: 3}) == 3
+    prn.gate_residual([0.9, 1e-6], torch.float32)
+    with pytest.warns(RuntimeWarning, match="newton_residual_high"):
+        prn.gate_residual([0.9, 0.5], torch.float32)
+    for bad in (1.5, float("inf"), float("nan")):
+        with pytest.raises(prn.NewtonDivergenceError):
+            prn.gate_residual([0.9, bad], torch.float32)
+    prn.gate_residual([0.9, 1.0], torch.float32, residual_warn=2.0)   # exactly 1.0 passes (">" gate)

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Tolerances (max-abs):
+  * GPU Newton vs oracle Newton at equal K: 1e-5 with fp32 storage; 2e-2
+    with bf16 storage (every stored state carries a rounding of up to 2^-9
+    relative, which the next linearisation feeds on).
+  * GPU Newton at K = 3 (GRU) or K = 4 (LSTM) vs the oracle's sequential
+    unroll: tau = 1e-4 in fp32 (FAQs, "Does parallel Newton match sequential
+    unroll?"), 2e-2 in bf16.
+  * residuals r_k: 2e-5 + 1e-3 r (fp32), 2e-2 + 2e-2 r (bf16); r_K against
+    an fp64 recomputation on the GPU's own output: 1e-6 + 1e-4 r.
+  * projection: fp32 1e-5; bf16 one rounding of the fp32 sum (2^-8 |ref|)
+    plus 1e-4.
+The small cases span several chunks (32 steps), several 64-channel tiles
+with a partial last tile, and a ragged time tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (gpu_run, gpu_sequential, oracle_newton, oracle_sequential, say, small_inputs, to_dev,
+                         to_f64, tol, TORCH_DT)
+import nonlinear_rnn_amd as prn
+from oracle import proj as oproj
+from oracle import newton as onewton
+from oracle import rounding as oround
+from workloads import Workload, WORKLOADS, random_state
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    Workload("gru_small", "gru", 3, 1000, 24, 80, "f32", 3),
+    Workload("lstm_small", "lstm", 2, 777, 16, 72, "f32", 2),
+    Workload("gru_bf16_small", "gru", 2, 600, 32, 64, "bf16", 3),
+    Workload("lstm_bf16_small", "lstm", 2, 300, 16, 130, "bf16", 3),
+    Workload("gru_ragged_small", "gru", 1, 1500, 16, 40, "f32", 3, n_seqs=7),
+    Workload("lstm_ragged_small", "lstm", 1, 900, 16, 64, "f32", 3, n_seqs=5, seg_lo=1, seg_hi=400),
+    WORKLOADS["gru_tiny"],
+]
+IDS = [w.name for w in SMALL]
+
+
+def xp64_of(w, xproj):
+    return to_f64(xproj)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_projection_matches_oracle(w):
+    say(f"[case] projection {w}")
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, 1)
+    got = to_f64(out["xproj"])
+    ref = oproj.input_proj(oround.load(inp["x"], w.dtype), oround.load(inp["W"], w.dtype),
+                           inp["bias"].astype(np.float64), w.G)
+    if w.dtype == "f32":
+        assert np.abs(got - ref).max() <= 1e-5
+    else:
+        assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-4)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_newton_matches_oracle_at_equal_K(w):
+    say(f"[case] newton equal-K {w}")
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, w.K)
+    xp = xp64_of(w, out["xproj"])
+    ref = oracle_newton(w, xp, inp["a"], w.K, cu=inp["cu_seqlens"])
+    H = to_f64(out["H"])
+    err = np.abs(H - ref["H"][..., -1, :]).max()
+    say(f"  max|H_gpu - H_oracle| = {err:.3e}; residuals gpu {out['res']} oracle {ref['residuals']}")
+    assert err <= tol(w, 1e-5)
+    last = to_f64(out["last"])
+    assert np.abs(last - ref["last"]).max() <= tol(w, 1e-5)
+    r_g, r_o = out["res"], np.array(ref["residuals"])
+    bound = (2e-5 + 1e-3 * r_o) if w.dtype == "f32" else (2e-2 + 2e-2 * r_o)
+    assert np.all(np.abs(r_g - r_o) <= bound), (r_g, r_o)
+
+
+@pytest.mark.parametrize("w", [w for w in SMALL if w.cell == "gru"] + [SMALL[1].scaled(K=4)],
+                         ids=lambda w: f"{w.name}-K{w.K}")
+def test_newton_agrees_with_sequential_within_tau(w):
+    say(f"[case] tau {w}")
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, w.K)
+    xp = xp64_of(w, out["xproj"])
+    seq, _ = oracle_sequential(w, xp, inp["a"], cu=inp["cu_seqlens"])
+    err = np.abs(to_f64(out["H"]) - seq[..., -1, :]).max()
+    say(f"  max|H_newton - h_sequential| = {err:.3e}")
+    assert err <= tol(w, 1e-4)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_sequential_kernel_matches_oracle(w):
+    say(f"[case] sequential {w}")
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, 1)
+    H, last = gpu_sequential(w, inp, out["xproj"])
+    xp = xp64_of(w, out["xproj"])
+    seq, slast = oracle_sequential(w, xp, inp["a"], cu=inp["cu_seqlens"])
+    assert np.abs(to_f64(H) - seq[..., -1, :]).max() <= tol(w, 1e-5)
+    assert np.abs(to_f64(last) - slast).max() <= tol(w, 1e-5)
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[4]], ids=["gru_small", "gru_ragged_small"])
+def test_final_residual_equals_recomputation_on_output(w):
+    say(f"[case] residual recomputation {w}")
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, w.K)
+    xp = xp64_of(w, out["xproj"])
+    H = to_f64(out["H"])[..., None, :]
+    heads = onewton.head_segments(w.B, w.T, inp["cu_seqlens"])
+    rows = w.B if inp["cu_seqlens"] is None else w.n_seqs
+    r = onewton.residual("gru", H, xp, inp["a"].astype(np.float64), heads, np.zeros((rows, 1, w.d_h)))
+    assert abs(out["res"][-1] - r) <= 1e-6 + 1e-4 * r
+
+
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[4]], ids=lambda w: w.name)
+def test_runs_are_bitwise_deterministic(w):
+    say(f"[case] determinism {w}")
+    inp = small_inputs(w)
+    o1 = gpu_run(w, inp, w.K)
+    o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
+    assert torch.equal(o1["H"], o2["H"])
+    assert torch.equal(o1["last"], o2["last"])
+    assert np.array_equal(o1["res"], o2["res"])
+
+
+def test_batch_rows_are_independent():
+    w = SMALL[1]
+    say(f"[case] batch independence {w}")
+    inp = small_inputs(w)
+    full = gpu_run(w, inp, w.K)
+    for b in range(w.B):
+        wb = w.scaled(B=1)
+        ob = gpu_run(wb, inp, w.K, xproj=full["xproj"][b:b + 1].contiguous())
+        assert torch.equal(ob["H"][0], full["H"][b])
+        assert torch.equal(ob["last"][0], full["last"][b])
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_nonzero_h0_and_final_state(cell):
+    w = Workload(f"{cell}_h0", cell, 2, 200, 16, 48, "f32", 3)
+    say(f"[case] h0 {w}")
+    inp = small_inputs(w)
+    h0 = random_state(w, w.B, seed=3)
+    out = gpu_run(w, inp, w.K, h0=h0)
+    xp = xp64_of(w, out["xproj"])
+    ref = oracle_newton(w, xp, inp["a"], w.K, h0=h0)
+    assert np.abs(to_f64(out["H"]) - ref["H"][..., -1, :]).max() <= 1e-5
+    assert np.abs(to_f64(out["last"]) - ref["last"]).max() <= 1e-5
+    # continuation: the second half started from the first half's final state
+    # equals the second half of one run (up to Newton's own error at K)
+    K = 6
+    whole = gpu_run(w, inp, K, h0=h0, xproj=out["xproj"])
+    w1 = w.scaled(T=100)
+    first = gpu_run(w1, inp, K, h0=h0, xproj=out["xproj"][:, :100].contiguous())
+    second = gpu_run(w1, inp, K, h0=first["last"].float().cpu().numpy(),
+                     xproj=out["xproj"][:, 100:].contiguous())
+    assert torch.allclose(second["H"], whole["H"][:, 100:], atol=1e-5, rtol=0)
+
+
+def test_packed_segments_match_separate_runs_and_empty_segments():
+    w = Workload("gru_pack", "gru", 1, 700, 16, 40, "f32", 3)
+    say(f"[case] pack vs segments {w}")
+    inp = small_inputs(w)
+    cu = np.array([0, 0, 64, 64, 65, 300, 700, 700], dtype=np.int32)   # empty, length-1 and trailing empty
+    h0 = random_state(w, len(cu) - 1, seed=5)
+    wp = w.scaled(n_seqs=len(cu) - 1)
+    pk = gpu_run(wp, inp, w.K, h0=h0, cu=cu)
+    xp = xp64_of(w, pk["xproj"])
+    ref = oracle_newton(wp, xp, inp["a"], w.K, h0=h0, cu=cu)
+    assert np.abs(to_f64(pk["H"]) - ref["H"][..., -1, :]).max() <= 1e-5
+    assert np.abs(to_f64(pk["last"]) - ref["last"]).max() <= 1e-5
+    for j in range(len(cu) - 1):
+        lo, hi = int(cu[j]), int(cu[j + 1])
+        if hi == lo:
+            assert torch.equal(pk["last"][j].cpu(), torch.from_numpy(h0[j]))
+            continue
+        ws = w.scaled(T=hi - lo)
+        one = gpu_run(ws, inp, w.K, h0=h0[j:j + 1], xproj=pk["xproj"][:, lo:hi].contiguous())
+        assert torch.allclose(one["H"][0], pk["H"][0, lo:hi], atol=1e-5, rtol=0)
+
+
+@pytest.mark.parametrize("T,d_h,K", [(1, 16, 3), (31, 64, 2), (32, 64, 3), (33, 65, 3), (70, 1, 1),
+                                     (45, 63, 50), (0, 16, 3)])
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_edge_shapes(cell, T, d_h, K):
+    w = Workload(f"{cell}_edge", cell, 2, T, 8, d_h, "f32", K)
+    say(f"[case] edge {w}")
+    inp = small_inputs(w)
+    h0 = random_state(w, w.B, seed=9)
+    out = gpu_run(w, inp, K, h0=h0)
+    if T == 0:
+        assert np.array_equal(out["res"], np.zeros(K + 1))
+        assert np.abs(to_f64(out["last"]) - h0).max() == 0
+        return
+    xp = xp64_of(w, out["xproj"])
+    ref = oracle_newton(w, xp, inp["a"], K, h0=h0)
+    assert np.abs(to_f64(out["H"]) - ref["H"][..., -1, :]).max() <= 1e-5
+    assert np.abs(to_f64(out["last"]) - ref["last"]).max() <= 1e-5
+    if K >= T:   # Newton is exact after T iterations
+        seq, _ = oracle_sequential(w, xp, inp["a"], h0=h0)
+        assert np.abs(to_f64(out["H"]) - seq[..., -1, :]).max() <= 1e-5
+
+
+def test_strided_view_example_from_the_shapes_page():
+    """A (2, 32, 8) view with time stride 2 through the contiguity-copying
+    wrapper: ParaGRU(8, 16), K = 3, must match the sequential unroll."""
+    say("[case] strided view")
+    g = torch.Generator().manual_seed(0)
+    base = torch.randn(2, 64, 8, generator=g).cuda()
+    x = base[:, ::2, :]
+    assert not x.is_contiguous()
+    W = (torch.randn(48, 8, generator=g) / 8 ** 0.5).cuda()
+    a = (torch.rand(3, 16, generator=g) - 0.5).cuda()
+    y_n, res = prn.forward(x, W, None, a, 3, cell="gru")
+    y_s = prn.sequential_forward(prn.input_proj(x, W, None, cell="gru"), a, cell="gru")
+    assert (y_n - y_s).abs().max().item() <= 1e-4
+    rep = prn.verify_agreement(prn.input_proj(x, W, None, cell="gru"), a, 3, cell="gru")
+    assert rep.ok and rep.max_abs <= 1e-4 and set(rep.to_dict()) >= {"ok", "max_abs"}
+
+
+def test_divergence_gate_fires_on_non_finite_input():
+    say("[case] divergence gate")
+    w = Workload("gru_nan", "gru", 1, 100, 8, 16, "f32", 3)
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, 3)
+    xp = out["xproj"].clone()
+    xp[0, 50, 0, 3] = float("nan")
+    a = torch.from_numpy(inp["a"]).cuda()
+    with pytest.raises(prn.NewtonDivergenceError):
+        prn.newton_forward(xp, a, 3, cell="gru")
+    H, res = prn.newton_forward(xp, a, 3, cell="gru", gate=False)
+    assert res[-1] == float("inf")
+    assert prn.newton_forward(out["xproj"], a, 3, cell="gru")[1][-1] < 1e-3
+
+
+def test_k_table_and_int64_offsets_through_the_wrapper():
+    say("[case] k table / int64 cu")
+    w = Workload("gru_tab", "gru", 1, 300, 8, 16, "f32", 3)
+    inp = small_inputs(w)
+    out = gpu_run(w, inp, 3)
+    a = torch.from_numpy(inp["a"]).cuda()
+    H1, r1 = prn.newton_forward(out["xproj"], a, None, cell="gru", k_table={64: 2, 1024: 3})
+    assert len(r1) == 4 and torch.equal(H1, out["H"])
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64)
+    H2, _ = prn.newton_forward(out["xproj"], a, 3, cell="gru", cu_seqlens=cu)
+    with pytest.raises(prn.PrnError):
+        prn.newton_forward(out["xproj"], a, 3, cell="gru", cu_seqlens=torch.tensor([0, 100, 299]))
