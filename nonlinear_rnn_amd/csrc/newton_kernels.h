@@ -39,12 +39,37 @@ template <> __device__ __forceinline__ Aff<2> load_map<2>(const float* p, int64_
   return {p[0], p[st], p[2 * st], p[3 * st], p[4 * st], p[5 * st]};
 }
 
-// max over a wave, then one atomic per wave.  r >= 0 (NaN already mapped to
-// +Inf), so the IEEE bit pattern orders like an unsigned integer.
-__device__ __forceinline__ void residual_max(float r, unsigned int* slot) {
+// Residual max of one workgroup: max over each wave, then over the waves
+// through LDS; thread 0 writes the workgroup's partial to part[block id].
+// (One partial per workgroup and a separate reduction, rather than a
+// same-address atomic per wave: those serialise in the memory system.)
+template <int NW>
+__device__ __forceinline__ void residual_partial(float r, float* __restrict__ part) {
+  __shared__ float red[NW];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0 && slot) atomicMax(slot, __float_as_uint(r));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = r;
+  __syncthreads();
+  if (threadIdx.x == 0 && part) {
+#pragma unroll
+    for (int v = 1; v < NW; ++v) r = fmaxf(r, red[v]);
+    const int64_t bid = blockIdx.x + static_cast<int64_t>(gridDim.x) * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+    part[bid] = r;
+  }
+}
+
+// residual_out[k] = max over the n partials of slot k; one workgroup per slot.
+__global__ void __launch_bounds__(256) k_residual_reduce(const float* __restrict__ part, int64_t n,
+                                                         float* __restrict__ out) {
+  __shared__ float red[4];
+  const float* p = part + blockIdx.x * n;
+  float r = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) r = fmaxf(r, p[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 template <int DT, int S>
@@ -62,7 +87,7 @@ template <class C, int DT, int LS, int NW>
 __global__ void __launch_bounds__(kWave * NW)
 k_tp_first(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
            const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
-           int64_t n_seqs, int64_t n_ch, float* __restrict__ agg, unsigned int* __restrict__ res0) {
+           int64_t n_seqs, int64_t n_ch, float* __restrict__ agg, float* __restrict__ rpart) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, NC = S * S + S, LC = LS * NW;
@@ -109,7 +134,7 @@ k_tp_first(const typename Storage<DT>::T* __restrict__ xproj, const typename Sto
     for (int v = 1; v < NW; ++v) tot = compose(part[v][lane], tot);
     store_map<S>(agg + ((b * n_ch + chunk) * NC) * d_h + ch, d_h, tot);
   }
-  residual_max(rmax, res0);
+  residual_partial<NW>(rmax, rpart);
 }
 
 // ----------------------------------------------------------------------------
@@ -134,9 +159,18 @@ k_tp_scan(const float* __restrict__ agg, float* __restrict__ carry, int64_t d_h,
   const bool act = ch < d_h;
   const float* ap = agg + (b * n_ch * NC) * d_h + ch;
 
+  // U maps are loaded before any is used, so their latencies overlap
+  constexpr int U = 8;
   Map acc = Map::identity();
-  if (act)
-    for (int64_t c = c0; c < c1; ++c) acc = compose(load_map<S>(ap + c * NC * d_h, d_h), acc);
+  if (act) {
+    for (int64_t c = c0; c < c1; c += U) {
+      Map m[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) m[u] = (c + u < c1) ? load_map<S>(ap + (c + u) * NC * d_h, d_h) : Map::identity();
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = compose(m[u], acc);
+    }
+  }
   part[sgm][lane] = acc;
   __syncthreads();
   if (!act) return;
@@ -145,10 +179,18 @@ k_tp_scan(const float* __restrict__ agg, float* __restrict__ carry, int64_t d_h,
   for (int q = 0; q < S; ++q) st[q] = 0.0f;
   for (int v = 0; v < sgm; ++v) apply(part[v][lane], st);
   float* cp = carry + (b * n_ch * S) * d_h + ch;
-  for (int64_t c = c0; c < c1; ++c) {
+  for (int64_t c = c0; c < c1; c += U) {
+    Map m[U];
 #pragma unroll
-    for (int q = 0; q < S; ++q) cp[(c * S + q) * d_h] = st[q];
-    apply(load_map<S>(ap + c * NC * d_h, d_h), st);
+    for (int u = 0; u < U; ++u) m[u] = (c + u < c1) ? load_map<S>(ap + (c + u) * NC * d_h, d_h) : Map::identity();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u < c1) {
+#pragma unroll
+        for (int q = 0; q < S; ++q) cp[((c + u) * S + q) * d_h] = st[q];
+        apply(m[u], st);
+      }
+    }
   }
 }
 
@@ -170,7 +212,7 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
          const float* __restrict__ a, int64_t T, int64_t d_h, int64_t n_seqs, int64_t n_ch,
          const float* __restrict__ carry, typename Storage<DT>::T* __restrict__ Hnext,
          typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
-         float* __restrict__ agg_next, unsigned int* __restrict__ res_k) {
+         float* __restrict__ agg_next, float* __restrict__ rpart) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, NC = S * S + S, LC = LS * NW;
@@ -285,7 +327,7 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
       store_map<S>(agg_next + ((b * n_ch + chunk) * NC) * d_h + ch, d_h, tot);
     }
   }
-  residual_max(rmax, res_k);
+  residual_partial<NW>(rmax, rpart);
 }
 
 // ----------------------------------------------------------------------------
@@ -369,6 +411,11 @@ template <class T>
 __global__ void k_copy_or_zero(const T* __restrict__ src, T* __restrict__ dst, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = src ? src[i] : T(0);
+}
+
+__global__ void k_zero_u32(unsigned* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 __global__ void k_zero_f32(float* __restrict__ p, int64_t n) {

@@ -1,0 +1,307 @@
+// Single-pass parallel Newton: all K iterations of one chunk in one
+// workgroup, the chunk's projected inputs held in registers throughout,
+// carries obtained by a decoupled look-back over the preceding chunks.
+//
+// The three phases of the chunked affine scan are still there, per
+// iteration:  (1) the workgroup composes its chunk's maps (lane-serial over
+// LS steps, then across waves through LDS);  (2) the carry across chunks
+// comes from the chunk records of the predecessors: each chunk publishes its
+// aggregate map, then looks back until it meets a predecessor whose
+// inclusive prefix (the state after its last step) is published, composing
+// aggregates on the way, and publishes its own inclusive prefix;  (3) each
+// lane re-runs its steps from its carry-in (the fix-up), and the same pass
+// linearises the new states for the next iteration.
+//
+// What this buys over separate phase kernels: the projected inputs cross
+// HBM once per forward instead of once per phase, no iterate is ever
+// written (only the final h), and the linearisation of iteration k+1 comes
+// from the fix-up pass of iteration k (K + 1 cell evaluations per step in
+// all, the last one for the final residual).
+//
+// Forward progress: a workgroup takes a ticket from a global counter when it
+// starts, and the ticket (not blockIdx) decides its chunk, chunk-major over
+// the independent chains (row, 64-channel tile).  A chunk therefore only
+// ever waits for chunks with smaller tickets, which have started; chunk 0 of
+// every chain never waits.  Every wait is bounded (spin_limit polls); on
+// timeout the carry becomes NaN (so the residual reads +Inf) and an error
+// word in the workspace is set: the kernel always terminates.
+//
+// Memory ordering of the chunk records: every record word is written and
+// read with relaxed agent-scope atomics, which gfx950 performs at the
+// device-wide coherence point (sc1), never from a per-XCD cache.  A
+// publishing wave stores the record's data, waits until all its stores are
+// acknowledged (s_waitcnt vmcnt(0)), and only then stores the status word;
+// a reader issues its data loads only after its status load has returned.
+// A reader that sees a status therefore sees the data it announces.  (This
+// avoids the L2 write-back / invalidate of agent-scope release / acquire
+// fences, which cost about 2 us per publication here.)
+#pragma once
+
+#include "newton_kernels.h"
+
+namespace prn {
+
+constexpr unsigned kRecEmpty = 0, kRecAggregate = 1, kRecPrefix = 2;  // status word of a chunk record
+
+// coherent (device-scope) record accesses
+__device__ __forceinline__ void rec_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float rec_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// publish a status once every record store of this wave has completed
+__device__ __forceinline__ void rec_publish(unsigned* status, unsigned v, int lane) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_store(status, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int S> __device__ __forceinline__ void rec_store_map(float* p, const Aff<S>& m);
+template <> __device__ __forceinline__ void rec_store_map<1>(float* p, const Aff<1>& m) {
+  rec_store(p, m.a);
+  rec_store(p + kWave, m.b);
+}
+template <> __device__ __forceinline__ void rec_store_map<2>(float* p, const Aff<2>& m) {
+  rec_store(p, m.a00); rec_store(p + kWave, m.a01); rec_store(p + 2 * kWave, m.a10);
+  rec_store(p + 3 * kWave, m.a11); rec_store(p + 4 * kWave, m.b0); rec_store(p + 5 * kWave, m.b1);
+}
+template <int S> __device__ __forceinline__ Aff<S> rec_load_map(const float* p);
+template <> __device__ __forceinline__ Aff<1> rec_load_map<1>(const float* p) {
+  return {rec_load(p), rec_load(p + kWave)};
+}
+template <> __device__ __forceinline__ Aff<2> rec_load_map<2>(const float* p) {
+  return {rec_load(p), rec_load(p + kWave), rec_load(p + 2 * kWave),
+          rec_load(p + 3 * kWave), rec_load(p + 4 * kWave), rec_load(p + 5 * kWave)};
+}
+
+struct SpRecords {
+  unsigned* status;    // [K][n_chains][n_ch]
+  float* agg;          // [K][n_chains][n_ch][NC][64]
+  float* pre;          // [K][n_chains][n_ch][S][64]
+  unsigned* ticket;    // 1 counter
+  unsigned* error;     // 1 word: set when a look-back wait timed out
+};
+
+// Carry-in of chunk `chunk` (the state just before its first step) by a
+// decoupled look-back, executed by one whole wave (lane = channel).  Each
+// round reads the status words of the 64 nearest unconsumed predecessors
+// with one load (lane i looks at chunk jh - i), finds the nearest published
+// inclusive prefix behind an unbroken run of published aggregates, and
+// consumes that run: the aggregates are composed (loaded RB at a time, their
+// latencies overlapped) and applied to the prefix.  A run that ends at an
+// unpublished chunk is consumed as far as it goes before polling again.  The
+// chunk's own aggregate is published only if the first round cannot already
+// resolve the carry.  Chunk 0 of a chain has carry 0 (its first step is a
+// segment head, J = 0).
+template <int S>
+__device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t base, int64_t chunk,
+                                               const Aff<S>& tot, int lane, unsigned spin_limit, float* cin) {
+  using Map = Aff<S>;
+  constexpr int NC = S * S + S, RB = 4;
+#pragma unroll
+  for (int q = 0; q < S; ++q) cin[q] = 0.0f;
+  if (chunk == 0) return;
+  Map accm = Map::identity();
+  int64_t jh = chunk - 1;
+  bool published = false;
+  unsigned spins = 0;
+  while (true) {
+    const int64_t jj = jh - lane;
+    const unsigned st = jj >= 0 ? __hip_atomic_load(rec.status + base + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : kRecEmpty;
+    const unsigned long long ready = __ballot(st != kRecEmpty);
+    const unsigned long long pref = __ballot(st == kRecPrefix);
+    const int n_ready = ~ready ? __builtin_ctzll(~ready) : 64;
+    const int i_p = pref ? __builtin_ctzll(pref) : 64;
+    const bool hit = i_p < n_ready;
+    const int n_use = hit ? i_p : n_ready;
+    if (!hit && !published) {   // cannot resolve yet: let successors use our aggregate
+      rec_store_map<S>(rec.agg + (base + chunk) * NC * kWave + lane, tot);
+      rec_publish(rec.status + base + chunk, kRecAggregate, lane);
+      published = true;
+    }
+    if (n_use == 0 && !hit) {
+      if (++spins > spin_limit) {  // timed out: poison the carry, flag the error, stop waiting
+        if (lane == 0) atomicOr(rec.error, 1u);
+#pragma unroll
+        for (int q = 0; q < S; ++q) cin[q] = __builtin_nanf("");
+        return;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      continue;
+    }
+    for (int r0 = 0; r0 < n_use; r0 += RB) {
+      Map mb[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+        mb[u] = (r0 + u < n_use) ? rec_load_map<S>(rec.agg + (base + jh - r0 - u) * NC * kWave + lane)
+                                 : Map::identity();
+#pragma unroll
+      for (int u = 0; u < RB; ++u) accm = compose(accm, mb[u]);
+    }
+    if (hit) {
+      const float* pp = rec.pre + (base + jh - i_p) * S * kWave + lane;
+#pragma unroll
+      for (int q = 0; q < S; ++q) cin[q] = rec_load(pp + q * kWave);
+      apply(accm, cin);
+      return;
+    }
+    jh -= n_use;
+  }
+}
+
+template <class C, int DT, int LS, int NW>
+__global__ void __launch_bounds__(kWave * NW)
+k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
+            const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
+            int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
+            typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
+            float* __restrict__ rpart, SpRecords rec, unsigned spin_limit) {
+  using ST = Storage<DT>;
+  using Map = typename C::Map;
+  constexpr int G = C::G, S = C::S, LC = LS * NW;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  __shared__ Map part[2][NW][kWave];
+  __shared__ float carry_sh[2][S][kWave];
+  __shared__ float red[NW];
+  __shared__ unsigned tk;
+
+  if (threadIdx.x == 0) tk = atomicAdd(rec.ticket, 1u);
+  __syncthreads();
+  const int64_t ticket = tk;
+  const int64_t n_wg = n_ch * n_chains;
+  const int64_t chunk = ticket / n_chains, chain = ticket % n_chains;
+  const int64_t b = chain / n_tiles, tile = chain % n_tiles;
+  const int64_t ch = tile * kWave + lane;
+  const int64_t t0 = chunk * LC + static_cast<int64_t>(w) * LS;
+  const bool act = ticket < n_wg && ch < d_h && t0 < T;
+  const int n = act ? static_cast<int>(imin(LS, T - t0)) : 0;
+
+  float av[G];
+  float xs[LS][G];
+  Map ms[LS];
+  Map acc = Map::identity();
+  float rmax = 0.0f;
+  SegTracker sg;
+
+  // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
+  if (act) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) av[g] = a[g * d_h + ch];
+    const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
+#pragma unroll
+    for (int j = 0; j < LS; ++j)
+      if (j < n)
+#pragma unroll
+        for (int g = 0; g < G; ++g) xs[j][g] = ST::load(xp + (j * G + g) * d_h);
+    sg.init(cu, n_seqs, b, t0);
+#pragma unroll
+    for (int j = 0; j < LS; ++j) {
+      if (j < n) {
+        const bool head = sg.at(t0 + j);
+        float prev[S];
+#pragma unroll
+        for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+        if (head && h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, prev);
+        float fv[S];
+        ms[j] = C::fj(xs[j], prev, av, head, fv);
+        acc = compose(ms[j], acc);
+#pragma unroll
+        for (int q = 0; q < S; ++q) rmax = fmaxf(rmax, abs_nan_inf(fv[q]));
+      }
+    }
+  }
+
+  auto residual_out = [&](int k, float r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
+    if (lane == 0) red[w] = r;
+    __syncthreads();
+    if (threadIdx.x == 0 && rpart && ticket < n_wg) {
+#pragma unroll
+      for (int v = 1; v < NW; ++v) r = fmaxf(r, red[v]);
+      rpart[k * n_wg + ticket] = r;
+    }
+  };
+  residual_out(0, rmax);
+
+  for (int k = 0; k < K; ++k) {
+    const int pb = k & 1;
+    part[pb][w][lane] = acc;
+    __syncthreads();
+
+    // ---- carry across chunks: one wave publishes and looks back ----
+    if (w == NW - 1 && ticket < n_wg) {
+      Map tot = part[pb][0][lane];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) tot = compose(part[pb][v][lane], tot);
+      const int64_t base = (static_cast<int64_t>(k) * n_chains + chain) * n_ch;
+      float cin[S];
+      lookback_carry<S>(rec, base, chunk, tot, lane, spin_limit, cin);
+      float incl[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        incl[q] = cin[q];
+        carry_sh[pb][q][lane] = cin[q];
+      }
+      apply(tot, incl);
+#pragma unroll
+      for (int q = 0; q < S; ++q) rec_store(rec.pre + (base + chunk) * S * kWave + q * kWave + lane, incl[q]);
+      rec_publish(rec.status + base + chunk, kRecPrefix, lane);
+    }
+    __syncthreads();
+
+    // ---- fix-up of iteration k+1, linearisation of iteration k+2 ----
+    const bool last = (k == K - 1);
+    acc = Map::identity();
+    rmax = 0.0f;
+    if (act) {
+      float s[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q) s[q] = carry_sh[pb][q][lane];
+      for (int v = 0; v < w; ++v) apply(part[pb][v][lane], s);
+      float pr[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q) pr[q] = ST::round(s[q]);
+      sg.init(cu, n_seqs, b, t0);
+#pragma unroll
+      for (int j = 0; j < LS; ++j) {
+        if (j < n) {
+          const int64_t t = t0 + j;
+          const bool head = sg.at(t);
+          apply(ms[j], s);
+          float sr[S];
+#pragma unroll
+          for (int q = 0; q < S; ++q) sr[q] = ST::round(s[q]);
+          float p[S];
+#pragma unroll
+          for (int q = 0; q < S; ++q) p[q] = pr[q];
+          if (head) {
+#pragma unroll
+            for (int q = 0; q < S; ++q) p[q] = 0.0f;
+            if (h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, p);
+          }
+          float fv[S];
+          if (!last) {
+            ms[j] = C::fj(xs[j], p, av, head, fv);
+            acc = compose(ms[j], acc);
+          } else {
+            C::f(xs[j], p, av, fv);
+            Hout[(b * T + t) * d_h + ch] = ST::pack(s[S - 1]);
+            if (slast && sg.last(t, T)) {
+#pragma unroll
+              for (int q = 0; q < S; ++q) slast[(sg.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            rmax = fmaxf(rmax, abs_nan_inf(sr[q] - fv[q]));
+            pr[q] = sr[q];
+          }
+        }
+      }
+    }
+    residual_out(k + 1, rmax);
+  }
+}
+
+}  // namespace prn

@@ -8,9 +8,11 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "newton_kernels.h"
+#include "newton_sp.h"
 #include "proj.h"
 #include "prn.h"
 
@@ -33,9 +35,22 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // three-phase geometry: lanes = 64 channels, NW waves of LS serial steps
 constexpr int kLS = 8;
-constexpr int kNW = 4;
+constexpr int kNW = 8;
 constexpr int kLC = kLS * kNW;
 constexpr int kScanSeg = 16;
+// single-pass geometry (same lane/wave roles; the tile stays in registers)
+constexpr int kSpLS = 8;
+constexpr int kSpNW = 4;
+constexpr int kSpLC = kSpLS * kSpNW;
+constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
+
+// PRN_ALGO=tp selects the multi-kernel three-phase schedule; the default is
+// the single-pass kernel.  Read at every call, so workspace sizing and the
+// forward agree within a process.
+bool use_three_phase() {
+  const char* e = getenv("PRN_ALGO");
+  return e && (e[0] == 't' || e[0] == 'T');
+}
 constexpr int64_t kMaxGrid = 65535;
 
 struct Shape {
@@ -85,8 +100,9 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
 
 struct Plan {
   int64_t n_ch;
-  int nbuf;  // iterate buffers: H^(k) for k = 1..K-1 lives in buffer (k - 1) % 2
-  size_t agg_off, carry_off, it_off[2], it_bytes, total;
+  int64_t n_wg;  // workgroups of a Newton-pass launch (residual partials per iteration)
+  int nbuf;      // iterate buffers: H^(k) for k = 1..K-1 lives in buffer (k - 1) % 2
+  size_t agg_off, carry_off, rpart_off, it_off[2], it_bytes, total;
 };
 
 Plan plan_tp(const prn_params* p, const Shape& sh, int K) {
@@ -96,14 +112,44 @@ Plan plan_tp(const prn_params* p, const Shape& sh, int K) {
   const size_t agg = align_up(size_t(p->B) * pl.n_ch * NC * p->d_h * 4);
   const size_t car = align_up(size_t(p->B) * pl.n_ch * sh.S * p->d_h * 4);
   const size_t it = align_up(size_t(p->B) * p->T * sh.S * p->d_h * sh.elt);
+  pl.n_wg = pl.n_ch * ((p->d_h + 63) / 64) * p->B;
+  const size_t rp = align_up(size_t(K + 1) * pl.n_wg * 4);
   pl.nbuf = K >= 3 ? 2 : (K == 2 ? 1 : 0);
   pl.agg_off = 0;
   pl.carry_off = agg;
-  pl.it_off[0] = agg + car;
-  pl.it_off[1] = agg + car + it;
+  pl.rpart_off = agg + car;
+  pl.it_off[0] = agg + car + rp;
+  pl.it_off[1] = agg + car + rp + it;
   pl.it_bytes = it;
-  pl.total = agg + car + pl.nbuf * it;
+  pl.total = agg + car + rp + pl.nbuf * it;
   return pl;
+}
+
+struct PlanSp {
+  int64_t n_ch, n_tiles, n_chains, n_wg;
+  size_t status_off, n_status;  // words zeroed per launch: ticket, error, K*n_chains*n_ch statuses
+  size_t agg_off, pre_off, rpart_off, total;
+};
+
+PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
+  PlanSp pl{};
+  pl.n_ch = (p->T + kSpLC - 1) / kSpLC;
+  pl.n_tiles = (p->d_h + 63) / 64;
+  pl.n_chains = p->B * pl.n_tiles;
+  pl.n_wg = pl.n_ch * pl.n_chains;
+  const size_t nrec = size_t(K) * pl.n_chains * pl.n_ch;
+  const size_t NC = sh.S * sh.S + sh.S;
+  pl.n_status = 2 + nrec;
+  pl.status_off = 0;
+  pl.agg_off = align_up(pl.n_status * 4);
+  pl.pre_off = pl.agg_off + align_up(nrec * NC * 64 * 4);
+  pl.rpart_off = pl.pre_off + align_up(nrec * sh.S * 64 * 4);
+  pl.total = pl.rpart_off + align_up(size_t(K + 1) * pl.n_wg * 4);
+  return pl;
+}
+
+size_t workspace_needed(const prn_params* p, const Shape& sh, int K) {
+  return use_three_phase() ? plan_tp(p, sh, K).total : plan_sp(p, sh, K).total;
 }
 
 prn_status launched(const char* what) {
@@ -151,10 +197,9 @@ prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, 
   };
   for (int k = 1; k < K; ++k)
     if (!iter_buf(k)) return fail(PRN_ERR_WORKSPACE, "internal: iterate %d has no workspace buffer", k);
-  unsigned int* r = reinterpret_cast<unsigned int*>(res);
-  auto slot = [&](int k) { return r ? r + k : nullptr; };
+  float* rpart = reinterpret_cast<float*>(ws + pl.rpart_off);
+  auto slot = [&](int k) { return res ? rpart + k * pl.n_wg : nullptr; };
 
-  if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
   const dim3 grid(unsigned(pl.n_ch), unsigned((p->d_h + 63) / 64), unsigned(p->B));
   const dim3 block(64 * kNW);
   const dim3 sgrid(unsigned((p->d_h + 63) / 64), unsigned(p->B));
@@ -174,13 +219,59 @@ prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     prn::k_tp_fix<C, DT, kLS, kNW, false, true><<<grid, block, 0, st>>>(
         xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, nullptr, Hout, slast, nullptr,
         slot(K));
-  } else if (slast && !sh.ragged) {
+    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 256, 0, st>>>(rpart, pl.n_wg, res);
+  } else {
+    if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
+  }
+  if (p->T == 0 && slast && !sh.ragged) {
     // zero-length rows: the final state is the initial state
     const int64_t n = p->B * S * p->d_h;
     prn::k_copy_or_zero<T><<<unsigned((n + 255) / 256), 256, 0, st>>>(h0, slast, n);
   }
   final_states_empty<DT>(p, sh, h0_v, cu, st);
   return launched("prn_newton_forward");
+}
+
+template <class C, int DT>
+prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, const void* h0_v, int K,
+                     const int32_t* cu, void* Hout_v, float* res) {
+  using T = typename prn::Storage<DT>::T;
+  constexpr int S = C::S;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const PlanSp pl = plan_sp(p, sh, K);
+  const T* h0 = static_cast<const T*>(h0_v);
+  T* slast = static_cast<T*>(p->state_last_out);
+  char* ws = static_cast<char*>(p->workspace);
+  if (p->T > 0) {
+    prn::SpRecords rec;
+    unsigned* words = reinterpret_cast<unsigned*>(ws + pl.status_off);
+    rec.ticket = words;
+    rec.error = words + 1;
+    rec.status = words + 2;
+    rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
+    rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
+    float* rpart = res ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
+    prn::k_zero_u32<<<unsigned((pl.n_status + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_status));
+    prn::k_newton_sp<C, DT, kSpLS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+        static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
+        static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit);
+    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 256, 0, st>>>(rpart, pl.n_wg, res);
+  } else {
+    if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
+    if (slast && !sh.ragged) {
+      const int64_t n = p->B * S * p->d_h;
+      prn::k_copy_or_zero<T><<<unsigned((n + 255) / 256), 256, 0, st>>>(h0, slast, n);
+    }
+  }
+  final_states_empty<DT>(p, sh, h0_v, cu, st);
+  return launched("prn_newton_forward");
+}
+
+template <class C, int DT>
+prn_status newton(const prn_params* p, const Shape& sh, const void* xproj, const void* h0, int K,
+                  const int32_t* cu, void* Hout, float* res) {
+  if (use_three_phase()) return newton_tp<C, DT>(p, sh, xproj, h0, K, cu, Hout, res);
+  return newton_sp<C, DT>(p, sh, xproj, h0, K, cu, Hout, res);
 }
 
 template <class C, int DT>
@@ -222,7 +313,7 @@ size_t prn_workspace_bytes(const prn_params* p, int32_t K) {
     fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
     return 0;
   }
-  return plan_tp(p, sh, K).total;
+  return workspace_needed(p, sh, K);
 }
 
 prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void* h0, int32_t K,
@@ -233,18 +324,18 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
   if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
   if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
-  const size_t need = plan_tp(p, sh, K).total;
+  const size_t need = workspace_needed(p, sh, K);
   if (need > 0 && (!p->workspace || p->workspace_bytes < need))
     return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
                 p->workspace, need);
   if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
     return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   if (p->cell == PRN_CELL_DIAG_GRU) {
-    if (p->dtype == PRN_F32) return newton_tp<prn::CellGRU, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
-    return newton_tp<prn::CellGRU, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+    if (p->dtype == PRN_F32) return newton<prn::CellGRU, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+    return newton<prn::CellGRU, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
   }
-  if (p->dtype == PRN_F32) return newton_tp<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
-  return newton_tp<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+  if (p->dtype == PRN_F32) return newton<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+  return newton<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
 }
 
 prn_status prn_sequential_forward(const void* xproj, const prn_params* p, const void* h0, const int32_t* cu,

@@ -45,6 +45,14 @@ def xp64_of(w, xproj):
     return to_f64(xproj)
 
 
+@pytest.fixture(params=["sp", "tp"])
+def algo(request, monkeypatch):
+    """Newton schedule: 'sp' single-pass look-back kernel (default), 'tp'
+    three-phase kernels.  The library reads PRN_ALGO at every call."""
+    monkeypatch.setenv("PRN_ALGO", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("w", SMALL, ids=IDS)
 def test_projection_matches_oracle(w):
     say(f"[case] projection {w}")
@@ -60,7 +68,7 @@ def test_projection_matches_oracle(w):
 
 
 @pytest.mark.parametrize("w", SMALL, ids=IDS)
-def test_newton_matches_oracle_at_equal_K(w):
+def test_newton_matches_oracle_at_equal_K(w, algo):
     say(f"[case] newton equal-K {w}")
     inp = small_inputs(w)
     out = gpu_run(w, inp, w.K)
@@ -79,7 +87,7 @@ def test_newton_matches_oracle_at_equal_K(w):
 
 @pytest.mark.parametrize("w", [w for w in SMALL if w.cell == "gru"] + [SMALL[1].scaled(K=4)],
                          ids=lambda w: f"{w.name}-K{w.K}")
-def test_newton_agrees_with_sequential_within_tau(w):
+def test_newton_agrees_with_sequential_within_tau(w, algo):
     say(f"[case] tau {w}")
     inp = small_inputs(w)
     out = gpu_run(w, inp, w.K)
@@ -103,7 +111,7 @@ def test_sequential_kernel_matches_oracle(w):
 
 
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[4]], ids=["gru_small", "gru_ragged_small"])
-def test_final_residual_equals_recomputation_on_output(w):
+def test_final_residual_equals_recomputation_on_output(w, algo):
     say(f"[case] residual recomputation {w}")
     inp = small_inputs(w)
     out = gpu_run(w, inp, w.K)
@@ -116,17 +124,28 @@ def test_final_residual_equals_recomputation_on_output(w):
 
 
 @pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[4]], ids=lambda w: w.name)
-def test_runs_are_bitwise_deterministic(w):
-    say(f"[case] determinism {w}")
+def test_run_to_run_reproducibility(w, algo):
+    """Three-phase: bitwise identical runs (fixed combination order).
+    Single-pass: the look-back folds a timing-dependent number of chunk
+    aggregates into a carry, so runs may differ by a few ulps; they must
+    agree to 1e-6 (fp32 storage) or one bf16 rounding step."""
+    say(f"[case] reproducibility {w}")
     inp = small_inputs(w)
     o1 = gpu_run(w, inp, w.K)
-    o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
-    assert torch.equal(o1["H"], o2["H"])
-    assert torch.equal(o1["last"], o2["last"])
-    assert np.array_equal(o1["res"], o2["res"])
+    for _ in range(3):
+        o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
+        if algo == "tp":
+            assert torch.equal(o1["H"], o2["H"])
+            assert torch.equal(o1["last"], o2["last"])
+            assert np.array_equal(o1["res"], o2["res"])
+        else:
+            lim = 1e-6 if w.dtype == "f32" else 1e-2
+            assert (o1["H"].float() - o2["H"].float()).abs().max().item() <= lim
+            assert (o1["last"].float() - o2["last"].float()).abs().max().item() <= lim
+            assert np.all(np.abs(o1["res"] - o2["res"]) <= lim + 1e-5 * o1["res"])
 
 
-def test_batch_rows_are_independent():
+def test_batch_rows_are_independent(algo):
     w = SMALL[1]
     say(f"[case] batch independence {w}")
     inp = small_inputs(w)
@@ -134,12 +153,16 @@ def test_batch_rows_are_independent():
     for b in range(w.B):
         wb = w.scaled(B=1)
         ob = gpu_run(wb, inp, w.K, xproj=full["xproj"][b:b + 1].contiguous())
-        assert torch.equal(ob["H"][0], full["H"][b])
-        assert torch.equal(ob["last"][0], full["last"][b])
+        if algo == "tp":   # same chunk boundaries, same arithmetic
+            assert torch.equal(ob["H"][0], full["H"][b])
+            assert torch.equal(ob["last"][0], full["last"][b])
+        else:
+            assert (ob["H"][0] - full["H"][b]).abs().max().item() <= 1e-6
+            assert (ob["last"][0] - full["last"][b]).abs().max().item() <= 1e-6
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_nonzero_h0_and_final_state(cell):
+def test_nonzero_h0_and_final_state(cell, algo):
     w = Workload(f"{cell}_h0", cell, 2, 200, 16, 48, "f32", 3)
     say(f"[case] h0 {w}")
     inp = small_inputs(w)
@@ -160,7 +183,7 @@ def test_nonzero_h0_and_final_state(cell):
     assert torch.allclose(second["H"], whole["H"][:, 100:], atol=1e-5, rtol=0)
 
 
-def test_packed_segments_match_separate_runs_and_empty_segments():
+def test_packed_segments_match_separate_runs_and_empty_segments(algo):
     w = Workload("gru_pack", "gru", 1, 700, 16, 40, "f32", 3)
     say(f"[case] pack vs segments {w}")
     inp = small_inputs(w)
@@ -185,7 +208,7 @@ def test_packed_segments_match_separate_runs_and_empty_segments():
 @pytest.mark.parametrize("T,d_h,K", [(1, 16, 3), (31, 64, 2), (32, 64, 3), (33, 65, 3), (70, 1, 1),
                                      (45, 63, 50), (0, 16, 3)])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_edge_shapes(cell, T, d_h, K):
+def test_edge_shapes(cell, T, d_h, K, algo):
     w = Workload(f"{cell}_edge", cell, 2, T, 8, d_h, "f32", K)
     say(f"[case] edge {w}")
     inp = small_inputs(w)
@@ -221,7 +244,7 @@ def test_strided_view_example_from_the_shapes_page():
     assert rep.ok and rep.max_abs <= 1e-4 and set(rep.to_dict()) >= {"ok", "max_abs"}
 
 
-def test_divergence_gate_fires_on_non_finite_input():
+def test_divergence_gate_fires_on_non_finite_input(algo):
     say("[case] divergence gate")
     w = Workload("gru_nan", "gru", 1, 100, 8, 16, "f32", 3)
     inp = small_inputs(w)
@@ -248,3 +271,17 @@ def test_k_table_and_int64_offsets_through_the_wrapper():
     H2, _ = prn.newton_forward(out["xproj"], a, 3, cell="gru", cu_seqlens=cu)
     with pytest.raises(prn.PrnError):
         prn.newton_forward(out["xproj"], a, 3, cell="gru", cu_seqlens=torch.tensor([0, 100, 299]))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_single_pass_and_three_phase_agree(w, monkeypatch):
+    """Two independent schedules of the same Newton iteration (different
+    chunking, carries from a look-back vs from a separate scan kernel)."""
+    say(f"[case] sp vs tp {w}")
+    inp = small_inputs(w)
+    monkeypatch.setenv("PRN_ALGO", "sp")
+    o1 = gpu_run(w, inp, w.K)
+    monkeypatch.setenv("PRN_ALGO", "tp")
+    o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
+    assert (o1["H"].float() - o2["H"].float()).abs().max().item() <= tol(w, 1e-5)
+    assert np.all(np.abs(o1["res"] - o2["res"]) <= tol(w, 2e-5) + 1e-3 * o2["res"])
