@@ -41,6 +41,39 @@ def algorithmic_newton_bytes(w) -> float:
     return float(w.tokens) * w.d_h * per * elt
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; a profile taken from other sources is stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "nonlinear_rnn_amd", "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload (FETCH_SIZE + WRITE_SIZE, each scaled by what a
+    512 MiB copy reads), or None if there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"].split()[0])
+    except (KeyError, ValueError):
+        return None
+
+
 def proj_flops(w) -> float:
     return 2.0 * w.tokens * w.G * w.d_h * w.d_in
 
@@ -89,6 +122,8 @@ def main() -> int:
     ap.add_argument("--K", type=int, default=None, help="override the workload's Newton depth")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 512 MiB device-to-device copy first (a known-size reference for byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -141,6 +176,13 @@ def main() -> int:
         if ev:
             ev[2].record(stream)
 
+    if args.calib_copy:
+        src = torch.empty(128 * 2 ** 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 536870912 bytes read, 536870912 bytes written", file=sys.stderr, flush=True)
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -165,14 +207,15 @@ def main() -> int:
     newton_ms = float(t_newt.mean())
     proj_ms = float(t_proj.mean())
     alg_bytes = algorithmic_newton_bytes(w)
-    roof_newton = {"kernel": "prn_newton_forward (all its launches)", "bound": "hbm",
+    roof_newton = {"kernel": "k_newton_sp (prn_newton_forward)", "bound": "hbm",
                    "achieved": alg_bytes / (newton_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                   "traffic": None}
+                   "traffic": profiled_traffic("k_newton_sp", w.name),
+                   "algorithmic_bytes": alg_bytes}
     roof_newton["frac"] = roof_newton["achieved"] / roof_newton["peak"]
     fl = proj_flops(w)
     roof_proj = {"kernel": "k_proj (prn_input_proj)", "bound": "mfma",
                  "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                 "traffic": None}
+                 "traffic": profiled_traffic("k_proj", w.name), "algorithmic_flops": fl}
     roof_proj["frac"] = roof_proj["achieved"] / roof_proj["peak"]
     dominant = roof_newton if newton_ms >= proj_ms else roof_proj
 

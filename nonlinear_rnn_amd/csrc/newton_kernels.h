@@ -58,18 +58,31 @@ __device__ __forceinline__ void residual_partial(float r, float* __restrict__ pa
   }
 }
 
-// residual_out[k] = max over the n partials of slot k; one workgroup per slot.
-__global__ void __launch_bounds__(256) k_residual_reduce(const float* __restrict__ part, int64_t n,
-                                                         float* __restrict__ out) {
-  __shared__ float red[4];
+// residual_out[k] = max over the n partials of slot k; one 1024-thread
+// workgroup per slot, four independent running maxima per thread.
+__global__ void __launch_bounds__(1024) k_residual_reduce(const float* __restrict__ part, int64_t n,
+                                                          float* __restrict__ out) {
+  __shared__ float red[16];
   const float* p = part + blockIdx.x * n;
-  float r = 0.0f;
-  for (int64_t i = threadIdx.x; i < n; i += 256) r = fmaxf(r, p[i]);
+  float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * 1024 < n; i += 4 * 1024) {
+    r0 = fmaxf(r0, p[i]);
+    r1 = fmaxf(r1, p[i + 1024]);
+    r2 = fmaxf(r2, p[i + 2048]);
+    r3 = fmaxf(r3, p[i + 3072]);
+  }
+  for (; i < n; i += 1024) r0 = fmaxf(r0, p[i]);
+  float r = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = r;
   __syncthreads();
-  if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int v = 1; v < 16; ++v) r = fmaxf(r, red[v]);
+    out[blockIdx.x] = r;
+  }
 }
 
 template <int DT, int S>

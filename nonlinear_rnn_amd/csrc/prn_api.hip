@@ -219,7 +219,7 @@ prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     prn::k_tp_fix<C, DT, kLS, kNW, false, true><<<grid, block, 0, st>>>(
         xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, nullptr, Hout, slast, nullptr,
         slot(K));
-    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 256, 0, st>>>(rpart, pl.n_wg, res);
+    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
     if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
   }
@@ -255,7 +255,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     prn::k_newton_sp<C, DT, kSpLS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
         static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
         static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit);
-    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 256, 0, st>>>(rpart, pl.n_wg, res);
+    if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
     if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
     if (slast && !sh.ragged) {
