@@ -113,9 +113,8 @@ k_tp_first(const typename Storage<DT>::T* __restrict__ xproj, const typename Sto
   Map acc = Map::identity();
   float rmax = 0.0f;
   if (ch < d_h && t0 < T) {
-    float av[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) av[g] = a[g * d_h + ch];
+    ChanCoef<C> cf;
+    cf.load(a, d_h, ch);
     SegTracker sg;
     sg.init(cu, n_seqs, b, t0);
     const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
@@ -129,10 +128,9 @@ k_tp_first(const typename Storage<DT>::T* __restrict__ xproj, const typename Sto
         for (int q = 0; q < S; ++q) prev[q] = 0.0f;
         if (head && h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, prev);
         float x[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) x[g] = ST::load(xp + (j * G + g) * d_h);
+        load_xs<C, DT>(xp + j * G * d_h, d_h, x);
         float fv[S];
-        const Map m = C::fj(x, prev, av, head, fv);
+        const Map m = C::fj(x, prev, cf.as, cf.a, head, fv);
         acc = compose(m, acc);
 #pragma unroll
         for (int q = 0; q < S; ++q) rmax = fmaxf(rmax, abs_nan_inf(fv[q]));
@@ -237,14 +235,13 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
   const int n = act ? static_cast<int>(imin(LS, T - t0)) : 0;
   __shared__ Map part[NW][kWave];
 
-  float av[G];
+  ChanCoef<C> cf;
   float xs[LS][G];
   Map ms[LS];
   Map acc = Map::identity();
   SegTracker sg;
   if (act) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) av[g] = a[g * d_h + ch];
+    cf.load(a, d_h, ch);
     sg.init(cu, n_seqs, b, t0);
     const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
     const typename ST::T* hp = Hprev ? Hprev + ((b * T + t0 - 1) * S) * d_h + ch : nullptr;
@@ -260,10 +257,9 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
         } else if (hp) {
           load_state<DT, S>(hp + j * S * d_h, d_h, prev);
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g) xs[j][g] = ST::load(xp + (j * G + g) * d_h);
+        load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
         float fv[S];
-        ms[j] = C::fj(xs[j], prev, av, head, fv);
+        ms[j] = C::fj(xs[j], prev, cf.as, cf.a, head, fv);
         acc = compose(ms[j], acc);
       }
     }
@@ -317,10 +313,10 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
           }
           float fv[S];
           if (NEXT) {
-            const Map m2 = C::fj(xs[j], p, av, head, fv);
+            const Map m2 = C::fj(xs[j], p, cf.as, cf.a, head, fv);
             acc2 = compose(m2, acc2);
           } else {
-            C::f(xs[j], p, av, fv);
+            C::f(xs[j], p, cf.as, cf.a, fv);
           }
 #pragma unroll
           for (int q = 0; q < S; ++q) rmax = fmaxf(rmax, abs_nan_inf(sr[q] - fv[q]));
@@ -366,9 +362,8 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
     base = r * T;
     len = T;
   }
-  float av[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) av[g] = a[g * d_h + ch];
+  ChanCoef<C> cf;
+  cf.load(a, d_h, ch);
   float s[S];
 #pragma unroll
   for (int q = 0; q < S; ++q) s[q] = 0.0f;
@@ -380,13 +375,11 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
   for (; t + U <= len; t += U) {
     float x[U][G];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int g = 0; g < G; ++g) x[u][g] = ST::load(xp + ((t + u) * G + g) * d_h);
+    for (int u = 0; u < U; ++u) load_xs<C, DT>(xp + (t + u) * G * d_h, d_h, x[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float o[S];
-      C::f(x[u], s, av, o);
+      C::f(x[u], s, cf.as, cf.a, o);
 #pragma unroll
       for (int q = 0; q < S; ++q) s[q] = o[q];
       hp[(t + u) * d_h] = ST::pack(s[S - 1]);
@@ -394,10 +387,9 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
   }
   for (; t < len; ++t) {
     float x[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] = ST::load(xp + (t * G + g) * d_h);
+    load_xs<C, DT>(xp + t * G * d_h, d_h, x);
     float o[S];
-    C::f(x, s, av, o);
+    C::f(x, s, cf.as, cf.a, o);
 #pragma unroll
     for (int q = 0; q < S; ++q) s[q] = o[q];
     hp[t * d_h] = ST::pack(s[S - 1]);

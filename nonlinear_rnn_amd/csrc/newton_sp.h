@@ -159,67 +159,83 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, LC = LS * NW;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform, kept in SGPRs
   __shared__ Map part[2][NW][kWave];
   __shared__ float carry_sh[2][S][kWave];
-  __shared__ float red[NW];
+  __shared__ unsigned red[NW];
   __shared__ unsigned tk;
 
   if (threadIdx.x == 0) tk = atomicAdd(rec.ticket, 1u);
   __syncthreads();
-  const int64_t ticket = tk;
+  const int64_t ticket = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(tk));
   const int64_t n_wg = n_ch * n_chains;
-  const int64_t chunk = ticket / n_chains, chain = ticket % n_chains;
-  const int64_t b = chain / n_tiles, tile = chain % n_tiles;
-  const int64_t ch = tile * kWave + lane;
+  const int64_t chunk = ticket / n_chains, chain = ticket - chunk * n_chains;
+  const int64_t b = chain / n_tiles, tile = chain - b * n_tiles;
+  const int64_t ch_l = tile * kWave + lane;
+  const bool ch_ok = ch_l < d_h;
+  const int64_t ch = ch_ok ? ch_l : d_h - 1;  // lanes past d_h shadow the last channel (stores masked)
   const int64_t t0 = chunk * LC + static_cast<int64_t>(w) * LS;
-  const bool act = ticket < n_wg && ch < d_h && t0 < T;
-  const int n = act ? static_cast<int>(imin(LS, T - t0)) : 0;
+  const bool wact = ticket < n_wg && t0 < T;
+  const int n = wact ? static_cast<int>(imin(LS, T - t0)) : 0;
+  SegTracker sg;
+  sg.init(cu, n_seqs, b, t0);
+  // a full sub-chunk without a segment head needs no per-step guards
+  const bool fast = n == LS && t0 != 0 && sg.start != t0 && sg.next >= t0 + LS;
 
-  float av[G];
+  ChanCoef<C> cf;
+  cf.load(a, d_h, ch);
   float xs[LS][G];
   Map ms[LS];
   Map acc = Map::identity();
-  float rmax = 0.0f;
-  SegTracker sg;
+  unsigned rmax = 0;
+  const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
+  typename ST::T* hp = Hout + (b * T + t0) * d_h + ch;
 
   // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
-  if (act) {
+  if (fast) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) av[g] = a[g * d_h + ch];
-    const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
+    for (int j = 0; j < LS; ++j) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+#pragma unroll
+    for (int j = 0; j < LS; ++j) {
+      float prev[S], fv[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+      ms[j] = C::template fj<false>(xs[j], prev, cf.as, cf.a, false, fv);
+      acc = compose(ms[j], acc);
+#pragma unroll
+      for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
+    }
+  } else if (wact) {
 #pragma unroll
     for (int j = 0; j < LS; ++j)
-      if (j < n)
-#pragma unroll
-        for (int g = 0; g < G; ++g) xs[j][g] = ST::load(xp + (j * G + g) * d_h);
-    sg.init(cu, n_seqs, b, t0);
+      if (j < n) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    SegTracker st = sg;
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       if (j < n) {
-        const bool head = sg.at(t0 + j);
-        float prev[S];
+        const bool head = st.at(t0 + j);
+        float prev[S], fv[S];
 #pragma unroll
         for (int q = 0; q < S; ++q) prev[q] = 0.0f;
-        if (head && h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, prev);
-        float fv[S];
-        ms[j] = C::fj(xs[j], prev, av, head, fv);
+        if (head && h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, prev);
+        ms[j] = C::fj(xs[j], prev, cf.as, cf.a, head, fv);
         acc = compose(ms[j], acc);
 #pragma unroll
-        for (int q = 0; q < S; ++q) rmax = fmaxf(rmax, abs_nan_inf(fv[q]));
+        for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
       }
     }
   }
 
-  auto residual_out = [&](int k, float r) {
+  auto residual_out = [&](int k, unsigned r) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
+    for (int o = 32; o > 0; o >>= 1) r = max(r, static_cast<unsigned>(__shfl_xor(static_cast<int>(r), o, kWave)));
     if (lane == 0) red[w] = r;
     __syncthreads();
     if (threadIdx.x == 0 && rpart && ticket < n_wg) {
 #pragma unroll
-      for (int v = 1; v < NW; ++v) r = fmaxf(r, red[v]);
-      rpart[k * n_wg + ticket] = r;
+      for (int v = 1; v < NW; ++v) r = max(r, red[v]);
+      rpart[k * n_wg + ticket] = rmax_finish(r);
     }
   };
   residual_out(0, rmax);
@@ -253,49 +269,83 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
     // ---- fix-up of iteration k+1, linearisation of iteration k+2 ----
     const bool last = (k == K - 1);
     acc = Map::identity();
-    rmax = 0.0f;
-    if (act) {
-      float s[S];
+    rmax = 0;
+    float s[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) s[q] = carry_sh[pb][q][lane];
-      for (int v = 0; v < w; ++v) apply(part[pb][v][lane], s);
-      float pr[S];
+    for (int q = 0; q < S; ++q) s[q] = carry_sh[pb][q][lane];
+    for (int v = 0; v < w; ++v) apply(part[pb][v][lane], s);
+    float pr[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) pr[q] = ST::round(s[q]);
-      sg.init(cu, n_seqs, b, t0);
+    for (int q = 0; q < S; ++q) pr[q] = ST::round(s[q]);
+    if (fast) {
+      if (!last) {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) {
+          apply(ms[j], s);
+          float fv[S];
+          ms[j] = C::template fj<false>(xs[j], pr, cf.as, cf.a, false, fv);
+          acc = compose(ms[j], acc);
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            const float sr = ST::round(s[q]);
+            rmax = rmax_bits(rmax, sr - fv[q]);
+            pr[q] = sr;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) {
+          apply(ms[j], s);
+          float fv[S];
+          C::f(xs[j], pr, cf.as, cf.a, fv);
+          if (ch_ok) hp[j * d_h] = ST::pack(s[S - 1]);
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            const float sr = ST::round(s[q]);
+            rmax = rmax_bits(rmax, sr - fv[q]);
+            pr[q] = sr;
+          }
+        }
+        if (slast && ch_ok && (t0 + LS == T || sg.next == t0 + LS)) {
+#pragma unroll
+          for (int q = 0; q < S; ++q) slast[(sg.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+        }
+      }
+    } else if (wact) {
+      SegTracker st = sg;
 #pragma unroll
       for (int j = 0; j < LS; ++j) {
         if (j < n) {
           const int64_t t = t0 + j;
-          const bool head = sg.at(t);
+          const bool head = st.at(t);
           apply(ms[j], s);
-          float sr[S];
-#pragma unroll
-          for (int q = 0; q < S; ++q) sr[q] = ST::round(s[q]);
           float p[S];
 #pragma unroll
           for (int q = 0; q < S; ++q) p[q] = pr[q];
           if (head) {
 #pragma unroll
             for (int q = 0; q < S; ++q) p[q] = 0.0f;
-            if (h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, p);
+            if (h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, p);
           }
           float fv[S];
           if (!last) {
-            ms[j] = C::fj(xs[j], p, av, head, fv);
+            ms[j] = C::fj(xs[j], p, cf.as, cf.a, head, fv);
             acc = compose(ms[j], acc);
           } else {
-            C::f(xs[j], p, av, fv);
-            Hout[(b * T + t) * d_h + ch] = ST::pack(s[S - 1]);
-            if (slast && sg.last(t, T)) {
+            C::f(xs[j], p, cf.as, cf.a, fv);
+            if (ch_ok) {
+              hp[j * d_h] = ST::pack(s[S - 1]);
+              if (slast && st.last(t, T)) {
 #pragma unroll
-              for (int q = 0; q < S; ++q) slast[(sg.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+                for (int q = 0; q < S; ++q) slast[(st.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+              }
             }
           }
 #pragma unroll
           for (int q = 0; q < S; ++q) {
-            rmax = fmaxf(rmax, abs_nan_inf(sr[q] - fv[q]));
-            pr[q] = sr[q];
+            const float sr = ST::round(s[q]);
+            rmax = rmax_bits(rmax, sr - fv[q]);
+            pr[q] = sr;
           }
         }
       }

@@ -45,25 +45,33 @@ template <> struct Storage<kBF16> {
 };
 
 // ------------------------------------------------- transcendentals -------
-// v_exp_f32 computes 2^x and v_rcp_f32 1/x, each to about 1 ulp.  The
-// logistic function and tanh are built from them:
-//   sig(u)  = 1 / (1 + 2^(-u log2 e))
-//   tanh(u) = 2 sig(2u) - 1
+// v_exp_f32 computes 2^x and v_rcp_f32 1/x, each to about 1 ulp.  Gate
+// pre-activations are carried pre-multiplied by the factor that turns them
+// into the exponent the gate needs ("scaled" values v):
+//   sig(u)  = 1 / (1 + 2^v),        v = -log2(e) u
+//   tanh(u) = 2 / (1 + 2^v) - 1,    v = -2 log2(e) u
+// so a gate costs one fma (v = as * h + xs), one exp, one add, one rcp.
 // Saturation is exact at both ends (2^(+big) = inf -> rcp = 0).
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSigScale = -kLog2e;          // logistic gates
+constexpr float kTanhScale = -2.0f * kLog2e;  // tanh gates
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float sigm(float u) { return rcp(1.0f + ex2(u * -kLog2e)); }
-__device__ __forceinline__ float tanh_(float u) {
-  return fmaf(2.0f, rcp(1.0f + ex2(u * (-2.0f * kLog2e))), -1.0f);
-}
+__device__ __forceinline__ float sig_s(float v) { return rcp(1.0f + ex2(v)); }
+__device__ __forceinline__ float tanh_s(float v) { return fmaf(2.0f, rcp(1.0f + ex2(v)), -1.0f); }
 
 // |x| with NaN mapped to +Inf, so that a max over residuals never drops a NaN
 __device__ __forceinline__ float abs_nan_inf(float x) {
   const float v = fabsf(x);
   return __builtin_isnan(v) ? __builtin_inff() : v;
+}
+// running max of |x| on IEEE bit patterns: every NaN pattern of |x| orders
+// above +Inf, so NaN survives (mapped to +Inf by rmax_finish)
+__device__ __forceinline__ unsigned rmax_bits(unsigned r, float x) { return max(r, __float_as_uint(x) & 0x7fffffffu); }
+__device__ __forceinline__ float rmax_finish(unsigned r) {
+  return r > 0x7f800000u ? __builtin_inff() : __uint_as_float(r);
 }
 
 // ---------------------------------------------------- affine maps --------
@@ -101,6 +109,10 @@ __device__ __forceinline__ void apply(const Aff<2>& m, float* s) {
 }
 
 // --------------------------------------------------------- cells ---------
+// Per-channel constants: a (recurrent weights, for the Jacobian) and as =
+// a * scale(gate) (for the scaled pre-activations).  Projected inputs are
+// passed scaled the same way: xs[g] = x[g] * scale(g) (Cell::scale(g)).
+//
 // fj(): f(s) and the per-channel Jacobian J = df/ds at state s, packed as the
 // Newton map (J, b = f - J s).  At a segment head the caller passes head =
 // true: J := 0 and b := f(h0) (shapes/layout page: J = 0 on the scan).
@@ -109,23 +121,26 @@ __device__ __forceinline__ void apply(const Aff<2>& m, float* s) {
 struct CellGRU {
   static constexpr int G = 3, S = 1;
   using Map = Aff<1>;
-  // x: [z, r, c] projected inputs; s: [h]; a: [a_z, a_r, a_c]
-  static __device__ __forceinline__ void f(const float* x, const float* s, const float* a, float* out) {
+  // gates [z, r, c]; state [h]
+  static constexpr __host__ __device__ float scale(int g) { return g == 2 ? kTanhScale : kSigScale; }
+  static __device__ __forceinline__ void f(const float* xs, const float* s, const float* as, const float* /*a*/,
+                                           float* out) {
     const float h = s[0];
-    const float z = sigm(fmaf(a[0], h, x[0]));
-    const float r = sigm(fmaf(a[1], h, x[1]));
-    const float c = tanh_(fmaf(a[2], r * h, x[2]));
+    const float z = sig_s(fmaf(as[0], h, xs[0]));
+    const float r = sig_s(fmaf(as[1], h, xs[1]));
+    const float c = tanh_s(fmaf(as[2], r * h, xs[2]));
     out[0] = fmaf(z, c - h, h);
   }
-  static __device__ __forceinline__ Map fj(const float* x, const float* s, const float* a, bool head,
-                                           float* fout) {
+  template <bool HEAD_POSSIBLE = true>
+  static __device__ __forceinline__ Map fj(const float* xs, const float* s, const float* as, const float* a,
+                                           bool head, float* fout) {
     const float h = s[0];
-    const float z = sigm(fmaf(a[0], h, x[0]));
-    const float r = sigm(fmaf(a[1], h, x[1]));
-    const float c = tanh_(fmaf(a[2], r * h, x[2]));
+    const float z = sig_s(fmaf(as[0], h, xs[0]));
+    const float r = sig_s(fmaf(as[1], h, xs[1]));
+    const float c = tanh_s(fmaf(as[2], r * h, xs[2]));
     const float fv = fmaf(z, c - h, h);
     fout[0] = fv;
-    if (head) return {0.0f, fv};
+    if (HEAD_POSSIBLE && head) return {0.0f, fv};
     const float omz = 1.0f - z;
     const float dz = z * omz * a[0];
     const float dr = r * (1.0f - r) * a[1];
@@ -138,30 +153,33 @@ struct CellGRU {
 struct CellLSTM {
   static constexpr int G = 4, S = 2;
   using Map = Aff<2>;
-  // x: [i, f, o, g]; s: [c, h]; a: [a_i, a_f, a_o, a_g]
-  static __device__ __forceinline__ void f(const float* x, const float* s, const float* a, float* out) {
+  // gates [i, f, o, g]; state [c, h]
+  static constexpr __host__ __device__ float scale(int g) { return g == 3 ? kTanhScale : kSigScale; }
+  static __device__ __forceinline__ void f(const float* xs, const float* s, const float* as, const float* /*a*/,
+                                           float* out) {
     const float c = s[0], h = s[1];
-    const float ig = sigm(fmaf(a[0], h, x[0]));
-    const float fg = sigm(fmaf(a[1], h, x[1]));
-    const float og = sigm(fmaf(a[2], h, x[2]));
-    const float gg = tanh_(fmaf(a[3], h, x[3]));
+    const float ig = sig_s(fmaf(as[0], h, xs[0]));
+    const float fg = sig_s(fmaf(as[1], h, xs[1]));
+    const float og = sig_s(fmaf(as[2], h, xs[2]));
+    const float gg = tanh_s(fmaf(as[3], h, xs[3]));
     const float c1 = fmaf(fg, c, ig * gg);
     out[0] = c1;
-    out[1] = og * tanh_(c1);
+    out[1] = og * tanh_s(c1 * kTanhScale);
   }
-  static __device__ __forceinline__ Map fj(const float* x, const float* s, const float* a, bool head,
-                                           float* fout) {
+  template <bool HEAD_POSSIBLE = true>
+  static __device__ __forceinline__ Map fj(const float* xs, const float* s, const float* as, const float* a,
+                                           bool head, float* fout) {
     const float c = s[0], h = s[1];
-    const float ig = sigm(fmaf(a[0], h, x[0]));
-    const float fg = sigm(fmaf(a[1], h, x[1]));
-    const float og = sigm(fmaf(a[2], h, x[2]));
-    const float gg = tanh_(fmaf(a[3], h, x[3]));
+    const float ig = sig_s(fmaf(as[0], h, xs[0]));
+    const float fg = sig_s(fmaf(as[1], h, xs[1]));
+    const float og = sig_s(fmaf(as[2], h, xs[2]));
+    const float gg = tanh_s(fmaf(as[3], h, xs[3]));
     const float c1 = fmaf(fg, c, ig * gg);
-    const float tc = tanh_(c1);
+    const float tc = tanh_s(c1 * kTanhScale);
     const float h1 = og * tc;
     fout[0] = c1;
     fout[1] = h1;
-    if (head) return {0.0f, 0.0f, 0.0f, 0.0f, c1, h1};
+    if (HEAD_POSSIBLE && head) return {0.0f, 0.0f, 0.0f, 0.0f, c1, h1};
     const float di = ig * (1.0f - ig) * a[0];
     const float df = fg * (1.0f - fg) * a[1];
     const float dO = og * (1.0f - og) * a[2];
@@ -180,6 +198,26 @@ struct CellLSTM {
     return m;
   }
 };
+
+// per-channel constants of a cell
+template <class C>
+struct ChanCoef {
+  float a[C::G], as[C::G];
+  __device__ __forceinline__ void load(const float* __restrict__ aw, int64_t d_h, int64_t ch) {
+#pragma unroll
+    for (int g = 0; g < C::G; ++g) {
+      a[g] = aw[g * d_h + ch];
+      as[g] = a[g] * C::scale(g);
+    }
+  }
+};
+
+// load one step's projected inputs (G values, stride d_h apart) scaled for the gates
+template <class C, int DT>
+__device__ __forceinline__ void load_xs(const typename Storage<DT>::T* p, int64_t d_h, float* xs) {
+#pragma unroll
+  for (int g = 0; g < C::G; ++g) xs[g] = Storage<DT>::load(p + g * d_h) * C::scale(g);
+}
 
 // ------------------------------------------------ segment tracking -------
 // Which steps are segment heads, and which segment a step belongs to.
