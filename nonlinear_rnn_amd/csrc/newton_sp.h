@@ -165,6 +165,9 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   __shared__ float carry_sh[2][S][kWave];
   __shared__ unsigned red[NW];
   __shared__ unsigned tk;
+  // the chunk's scaled projected inputs, read-only after the first walk:
+  // [step][gate][thread] (consecutive lanes, consecutive banks)
+  __shared__ float xsh[LS][G][kWave * NW];
 
   if (threadIdx.x == 0) tk = atomicAdd(rec.ticket, 1u);
   __syncthreads();
@@ -185,8 +188,15 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 
   ChanCoef<C> cf;
   cf.load(a, d_h, ch);
-  float xs[LS][G];
   Map ms[LS];
+  auto xs_put = [&](int j, const float* v) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) xsh[j][g][threadIdx.x] = v[g];
+  };
+  auto xs_get = [&](int j, float* v) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = xsh[j][g][threadIdx.x];
+  };
   Map acc = Map::identity();
   unsigned rmax = 0;
   const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
@@ -194,10 +204,12 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 
   // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
   if (fast) {
+    float xs[LS][G];
 #pragma unroll
     for (int j = 0; j < LS; ++j) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
+      xs_put(j, xs[j]);
       float prev[S], fv[S];
 #pragma unroll
       for (int q = 0; q < S; ++q) prev[q] = 0.0f;
@@ -207,6 +219,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
     }
   } else if (wact) {
+    float xs[LS][G];
 #pragma unroll
     for (int j = 0; j < LS; ++j)
       if (j < n) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
@@ -214,6 +227,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       if (j < n) {
+        xs_put(j, xs[j]);
         const bool head = st.at(t0 + j);
         float prev[S], fv[S];
 #pragma unroll
@@ -253,18 +267,21 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       const int64_t base = (static_cast<int64_t>(k) * n_chains + chain) * n_ch;
       float cin[S];
       lookback_carry<S>(rec, base, chunk, tot, lane, spin_limit, cin);
+#pragma unroll
+      for (int q = 0; q < S; ++q) carry_sh[pb][q][lane] = cin[q];
+      // the inclusive prefix (state after the chunk's last step) goes out
+      // before the barrier; its status is published right after it, while
+      // the other waves already start their fix-up
       float incl[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) {
-        incl[q] = cin[q];
-        carry_sh[pb][q][lane] = cin[q];
-      }
+      for (int q = 0; q < S; ++q) incl[q] = cin[q];
       apply(tot, incl);
 #pragma unroll
       for (int q = 0; q < S; ++q) rec_store(rec.pre + (base + chunk) * S * kWave + q * kWave + lane, incl[q]);
-      rec_publish(rec.status + base + chunk, kRecPrefix, lane);
     }
     __syncthreads();
+    if (w == NW - 1 && ticket < n_wg)
+      rec_publish(rec.status + (static_cast<int64_t>(k) * n_chains + chain) * n_ch + chunk, kRecPrefix, lane);
 
     // ---- fix-up of iteration k+1, linearisation of iteration k+2 ----
     const bool last = (k == K - 1);
@@ -282,8 +299,9 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
           apply(ms[j], s);
-          float fv[S];
-          ms[j] = C::template fj<false>(xs[j], pr, cf.as, cf.a, false, fv);
+          float fv[S], xj[G];
+          xs_get(j, xj);
+          ms[j] = C::template fj<false>(xj, pr, cf.as, cf.a, false, fv);
           acc = compose(ms[j], acc);
 #pragma unroll
           for (int q = 0; q < S; ++q) {
@@ -296,8 +314,9 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
           apply(ms[j], s);
-          float fv[S];
-          C::f(xs[j], pr, cf.as, cf.a, fv);
+          float fv[S], xj[G];
+          xs_get(j, xj);
+          C::f(xj, pr, cf.as, cf.a, fv);
           if (ch_ok) hp[j * d_h] = ST::pack(s[S - 1]);
 #pragma unroll
           for (int q = 0; q < S; ++q) {
@@ -327,12 +346,13 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             for (int q = 0; q < S; ++q) p[q] = 0.0f;
             if (h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, p);
           }
-          float fv[S];
+          float fv[S], xj[G];
+          xs_get(j, xj);
           if (!last) {
-            ms[j] = C::fj(xs[j], p, cf.as, cf.a, head, fv);
+            ms[j] = C::fj(xj, p, cf.as, cf.a, head, fv);
             acc = compose(ms[j], acc);
           } else {
-            C::f(xs[j], p, cf.as, cf.a, fv);
+            C::f(xj, p, cf.as, cf.a, fv);
             if (ch_ok) {
               hp[j * d_h] = ST::pack(s[S - 1]);
               if (slast && st.last(t, T)) {

@@ -4,9 +4,9 @@
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 output tile; its four
 // waves each own a 64 x 64 quadrant made of 2 x 2 blocks of 32 x 32.  K is
-// walked in stages of BK elements (128 bytes of every row): x and W tiles are
-// staged through LDS, double buffered, with the next stage's global loads in
-// flight while the current one is multiplied.
+// walked in stages of 128 bytes of every row: the stage's x rows and W rows
+// share one LDS buffer, double buffered, with the next stage's global loads
+// in flight while the current one is multiplied.
 //
 // Operand layout of the 32 x 32 matrix instructions (wave64): lane l feeds
 // row (l % 32) of A and column (l % 32) of B; lane half h = l / 32 feeds the
@@ -33,29 +33,32 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int BM = 128, BN = 128;
-constexpr int ROWB = 128;              // bytes of one row per K stage
-constexpr int PADB = 16;               // LDS row padding (bytes)
-constexpr int LDS_ROW = ROWB + PADB;   // LDS row stride (bytes)
-constexpr int VPR = ROWB / 16;         // 16-byte vectors per row per stage
-constexpr int NTHR = 256;
-constexpr int VPT = BM * VPR / NTHR;   // vectors per thread per tile per stage
+constexpr int WM = 2, WN = 2;                       // 32x32 blocks per wave (rows, columns)
+constexpr int WR = 2, WC = 2;                       // waves per workgroup (rows, columns)
+constexpr int BM = WR * WM * 32, BN = WC * WN * 32;  // workgroup tile: 128 x 128
+constexpr int ROWB = 128;                           // bytes of one row per K stage
+constexpr int LDS_ROW = ROWB + 16;                  // LDS row stride (bytes), padded
+constexpr int VPR = ROWB / 16;                      // 16-byte vectors per row per stage
+constexpr int NTHR = 64 * WR * WC;
+constexpr int NROWS = BM + BN;                      // A rows then B rows in one LDS buffer
+constexpr int VPT = NROWS * VPR / NTHR;             // vectors per thread per stage
 constexpr int NXCD = 8;
+static_assert(NROWS * VPR % NTHR == 0, "a stage must split evenly over the workgroup");
 
+// round to nearest even; NaN stays a quiet NaN (branch-free)
 __device__ __forceinline__ uint16_t bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t q = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? q : r);
 }
 
 template <bool BF16>
 __global__ void __launch_bounds__(NTHR)
 k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float* __restrict__ bias,
        uint8_t* __restrict__ C, int64_t M, int64_t N, int64_t K, int n_tiles_n, int remap) {
-  constexpr int ELT = BF16 ? 2 : 4;       // bytes per element
-  constexpr int BK = ROWB / ELT;          // k per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][BM * LDS_ROW];
+  constexpr int ELT = BF16 ? 2 : 4;  // bytes per element
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][NROWS * LDS_ROW];
 
   // block -> tile, keeping the column tiles of a row tile on one XCD
   int64_t bid = blockIdx.x;
@@ -63,14 +66,15 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
     const int64_t per = gridDim.x / NXCD;
     bid = (bid % NXCD) * per + bid / NXCD;
   }
-  const int64_t tm = bid / n_tiles_n, tn = bid % n_tiles_n;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = (bid / n_tiles_n) * BM, n0 = (bid % n_tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC;
   const int64_t rowbytes = K * ELT;
 
-  // global -> register staging of one K stage
-  f32x4 ra[VPT], rb[VPT];
+  // global -> register staging of one K stage: rows [0, BM) of the tile come
+  // from x, rows [BM, BM + BN) from W
+  f32x4 rv[VPT];
   auto gload = [&](int64_t kt) {
 #pragma unroll
     for (int p = 0; p < VPT; ++p) {
@@ -78,9 +82,13 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
       const int r = v / VPR, kv = v % VPR;
       const int64_t kbyte = kt * ROWB + kv * 16;
       const bool kin = kbyte < rowbytes;
-      const int64_t gm = m0 + r, gn = n0 + r;
-      ra[p] = (kin && gm < M) ? *reinterpret_cast<const f32x4*>(A + gm * rowbytes + kbyte) : f32x4{0, 0, 0, 0};
-      rb[p] = (kin && gn < N) ? *reinterpret_cast<const f32x4*>(B + gn * rowbytes + kbyte) : f32x4{0, 0, 0, 0};
+      if (r < BM) {
+        const int64_t g = m0 + r;
+        rv[p] = (kin && g < M) ? *reinterpret_cast<const f32x4*>(A + g * rowbytes + kbyte) : f32x4{0, 0, 0, 0};
+      } else {
+        const int64_t g = n0 + (r - BM);
+        rv[p] = (kin && g < N) ? *reinterpret_cast<const f32x4*>(B + g * rowbytes + kbyte) : f32x4{0, 0, 0, 0};
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -88,53 +96,60 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
     for (int p = 0; p < VPT; ++p) {
       const int v = tid + p * NTHR;
       const int r = v / VPR, kv = v % VPR;
-      *reinterpret_cast<f32x4*>(&lds[buf][0][r * LDS_ROW + kv * 16]) = ra[p];
-      *reinterpret_cast<f32x4*>(&lds[buf][1][r * LDS_ROW + kv * 16]) = rb[p];
+      *reinterpret_cast<f32x4*>(&lds[buf][r * LDS_ROW + kv * 16]) = rv[p];
     }
   };
 
-  f32x16 acc[2][2];
+  // bias of this lane's output columns, loaded up front (the epilogue must
+  // not wait on a load between its stores)
+  float bcol[WN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < WN; ++j) {
+    const int64_t gn = n0 + wc * WN * 32 + j * 32 + (lane & 31);
+    bcol[j] = (bias && gn < N) ? bias[gn] : 0.0f;
+  }
+
+  f32x16 acc[WM][WN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t nk = (K + BK - 1) / BK;
+  const int64_t nk = (rowbytes + ROWB - 1) / ROWB;
   gload(0);
   lstore(0);
   __syncthreads();
   const int half = lane >> 5, l32 = lane & 31;
+  const int arow = wr * WM * 32 + l32;       // this lane's A row (block i adds 32 i)
+  const int brow = BM + wc * WN * 32 + l32;  // this lane's B row (block j adds 32 j)
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* la = lds[cur][0];
-    const uint8_t* lb = lds[cur][1];
+    const uint8_t* L = lds[cur];
 #pragma unroll
     for (int kb = 0; kb < VPR / 2; ++kb) {  // 32 bytes of k per step: two 16-byte halves
       const int off = kb * 32 + half * 16;
-      f32x4 av[2], bv[2];
+      f32x4 av[WM], bv[WN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *reinterpret_cast<const f32x4*>(la + (wr * 64 + i * 32 + l32) * LDS_ROW + off);
+      for (int i = 0; i < WM; ++i) av[i] = *reinterpret_cast<const f32x4*>(L + (arow + 32 * i) * LDS_ROW + off);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const f32x4*>(lb + (wc * 64 + j * 32 + l32) * LDS_ROW + off);
+      for (int j = 0; j < WN; ++j) bv[j] = *reinterpret_cast<const f32x4*>(L + (brow + 32 * j) * LDS_ROW + off);
       if constexpr (BF16) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < WN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                                 __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < WM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < WN; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
       }
     }
@@ -142,24 +157,24 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
     __syncthreads();
   }
 
-  // epilogue: bias, round to the storage dtype, store
+  // epilogue: bias, round to the storage dtype, store (bounds checks only
+  // for tiles that overhang M or N)
+  auto put = [&](int64_t gm, int64_t gn, float v) {
+    if constexpr (BF16)
+      reinterpret_cast<uint16_t*>(C)[gm * N + gn] = bf16_rne(v);
+    else
+      reinterpret_cast<float*>(C)[gm * N + gn] = v;
+  };
+  const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t gn = n0 + wc * 64 + j * 32 + l32;
-    const bool nin = gn < N;
-    const float bv = (bias && nin) ? bias[gn] : 0.0f;
+  for (int j = 0; j < WN; ++j) {
+    const int64_t gn = n0 + wc * WN * 32 + j * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t gm = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (nin && gm < M) {
-          const float v = acc[i][j][r] + bv;
-          if constexpr (BF16)
-            reinterpret_cast<uint16_t*>(C)[gm * N + gn] = bf16_rne(v);
-          else
-            reinterpret_cast<float*>(C)[gm * N + gn] = v;
-        }
+        const int64_t gm = m0 + wr * WM * 32 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (full || (gm < M && gn < N)) put(gm, gn, acc[i][j][r] + bcol[j]);
       }
     }
   }
