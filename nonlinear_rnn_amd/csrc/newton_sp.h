@@ -88,21 +88,30 @@ struct SpRecords {
 // inclusive prefix behind an unbroken run of published aggregates, and
 // consumes that run: the aggregates are composed (loaded RB at a time, their
 // latencies overlapped) and applied to the prefix.  A run that ends at an
-// unpublished chunk is consumed as far as it goes before polling again.  The
-// chunk's own aggregate is published only if the first round cannot already
-// resolve the carry.  Chunk 0 of a chain has carry 0 (its first step is a
-// segment head, J = 0).
+// unpublished chunk is consumed as far as it goes before polling again.
+// Chunk 0 of a chain has carry 0 (its first step is a segment head, J = 0).
 template <int S>
 __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t base, int64_t chunk,
-                                               const Aff<S>& tot, int lane, unsigned spin_limit, float* cin) {
+                                               const Aff<S>& tot, int lane, unsigned spin_limit, bool agg_first, float* cin) {
   using Map = Aff<S>;
-  constexpr int NC = S * S + S, RB = 4;
+  constexpr int NC = S * S + S, RB = 8;
 #pragma unroll
   for (int q = 0; q < S; ++q) cin[q] = 0.0f;
   if (chunk == 0) return;
   Map accm = Map::identity();
   int64_t jh = chunk - 1;
+  // Our aggregate's data are stored before the first poll.  With few chains
+  // (consecutive chunks of a chain start close together, so successors are
+  // already waiting) the status is published at once; with many chains the
+  // predecessor is usually done, and the status is published only if the
+  // first poll cannot resolve the carry (the wait for that poll then also
+  // covers the data stores).
+  rec_store_map<S>(rec.agg + (base + chunk) * NC * kWave + lane, tot);
   bool published = false;
+  if (agg_first) {
+    rec_publish(rec.status + base + chunk, kRecAggregate, lane);
+    published = true;
+  }
   unsigned spins = 0;
   while (true) {
     const int64_t jj = jh - lane;
@@ -114,8 +123,7 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
     const int i_p = pref ? __builtin_ctzll(pref) : 64;
     const bool hit = i_p < n_ready;
     const int n_use = hit ? i_p : n_ready;
-    if (!hit && !published) {   // cannot resolve yet: let successors use our aggregate
-      rec_store_map<S>(rec.agg + (base + chunk) * NC * kWave + lane, tot);
+    if (!hit && !published) {
       rec_publish(rec.status + base + chunk, kRecAggregate, lane);
       published = true;
     }
@@ -155,7 +163,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
             int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
             typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
-            float* __restrict__ rpart, SpRecords rec, unsigned spin_limit) {
+            float* __restrict__ rpart, SpRecords rec, unsigned spin_limit, bool agg_first) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, LC = LS * NW;
@@ -266,7 +274,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       for (int v = 1; v < NW; ++v) tot = compose(part[pb][v][lane], tot);
       const int64_t base = (static_cast<int64_t>(k) * n_chains + chain) * n_ch;
       float cin[S];
-      lookback_carry<S>(rec, base, chunk, tot, lane, spin_limit, cin);
+      lookback_carry<S>(rec, base, chunk, tot, lane, spin_limit, agg_first, cin);
 #pragma unroll
       for (int q = 0; q < S; ++q) carry_sh[pb][q][lane] = cin[q];
       // the inclusive prefix (state after the chunk's last step) goes out

@@ -38,11 +38,19 @@ constexpr int kLS = 8;
 constexpr int kNW = 8;
 constexpr int kLC = kLS * kNW;
 constexpr int kScanSeg = 16;
-// single-pass geometry (same lane/wave roles; the tile stays in registers)
-constexpr int kSpLS = 8;
-constexpr int kSpNW = 4;
-constexpr int kSpLC = kSpLS * kSpNW;
+// single-pass geometry (lane = channel, NW waves of LS serial steps): the
+// LSTM keeps 6 steps per lane so that three 4-wave workgroups fit a CU
+template <class C> struct SpGeo;
+template <> struct SpGeo<prn::CellGRU> { static constexpr int LS = 8, NW = 4; };
+template <> struct SpGeo<prn::CellLSTM> { static constexpr int LS = 6, NW = 4; };
+int sp_chunk(int cell) {
+  return cell == PRN_CELL_DIAG_GRU ? SpGeo<prn::CellGRU>::LS * SpGeo<prn::CellGRU>::NW
+                                   : SpGeo<prn::CellLSTM>::LS * SpGeo<prn::CellLSTM>::NW;
+}
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
+// below this many independent chains, chunks publish their aggregate before
+// polling (measured: helps 4-32 chains, hurts 128)
+constexpr int64_t kAggFirstBelowChains = 64;
 
 // PRN_ALGO=tp selects the multi-kernel three-phase schedule; the default is
 // the single-pass kernel.  Read at every call, so workspace sizing and the
@@ -133,7 +141,8 @@ struct PlanSp {
 
 PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
   PlanSp pl{};
-  pl.n_ch = (p->T + kSpLC - 1) / kSpLC;
+  const int lc = sp_chunk(p->cell);
+  pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
   pl.n_wg = pl.n_ch * pl.n_chains;
@@ -252,9 +261,10 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
     float* rpart = res ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
     prn::k_zero_u32<<<unsigned((pl.n_status + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_status));
-    prn::k_newton_sp<C, DT, kSpLS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+    constexpr int LS = SpGeo<C>::LS, NW = SpGeo<C>::NW;
+    prn::k_newton_sp<C, DT, LS, NW><<<unsigned(pl.n_wg), 64 * NW, 0, st>>>(
         static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
-        static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit);
+        static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
     if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
