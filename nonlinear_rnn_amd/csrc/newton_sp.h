@@ -100,18 +100,15 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
   if (chunk == 0) return;
   Map accm = Map::identity();
   int64_t jh = chunk - 1;
-  // Our aggregate's data are stored before the first poll.  With few chains
-  // (consecutive chunks of a chain start close together, so successors are
-  // already waiting) the status is published at once; with many chains the
-  // predecessor is usually done, and the status is published only if the
-  // first poll cannot resolve the carry (the wait for that poll then also
-  // covers the data stores).
+  // Our aggregate's data are stored, and the first poll is issued without
+  // waiting for them: the wait for the poll also covers the stores, so the
+  // status can go out right after it.  With few chains (consecutive chunks
+  // of a chain start close together, so successors are already waiting) the
+  // aggregate status is published after the first poll in any case; with
+  // many chains the predecessor is usually done, and it is published only if
+  // the first poll cannot resolve the carry.
   rec_store_map<S>(rec.agg + (base + chunk) * NC * kWave + lane, tot);
   bool published = false;
-  if (agg_first) {
-    rec_publish(rec.status + base + chunk, kRecAggregate, lane);
-    published = true;
-  }
   unsigned spins = 0;
   while (true) {
     const int64_t jj = jh - lane;
@@ -123,7 +120,7 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
     const int i_p = pref ? __builtin_ctzll(pref) : 64;
     const bool hit = i_p < n_ready;
     const int n_use = hit ? i_p : n_ready;
-    if (!hit && !published) {
+    if ((agg_first || !hit) && !published) {
       rec_publish(rec.status + base + chunk, kRecAggregate, lane);
       published = true;
     }
@@ -137,6 +134,13 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
       __builtin_amdgcn_s_sleep(2);
       continue;
     }
+    // the prefix (if found) is loaded in the same batch as the aggregates
+    float pv[S];
+    if (hit) {
+      const float* pp = rec.pre + (base + jh - i_p) * S * kWave + lane;
+#pragma unroll
+      for (int q = 0; q < S; ++q) pv[q] = rec_load(pp + q * kWave);
+    }
     for (int r0 = 0; r0 < n_use; r0 += RB) {
       Map mb[RB];
 #pragma unroll
@@ -147,9 +151,8 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
       for (int u = 0; u < RB; ++u) accm = compose(accm, mb[u]);
     }
     if (hit) {
-      const float* pp = rec.pre + (base + jh - i_p) * S * kWave + lane;
 #pragma unroll
-      for (int q = 0; q < S; ++q) cin[q] = rec_load(pp + q * kWave);
+      for (int q = 0; q < S; ++q) cin[q] = pv[q];
       apply(accm, cin);
       return;
     }

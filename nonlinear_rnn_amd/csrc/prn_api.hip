@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 #include "newton_kernels.h"
 #include "newton_sp.h"
@@ -38,14 +39,26 @@ constexpr int kLS = 8;
 constexpr int kNW = 8;
 constexpr int kLC = kLS * kNW;
 constexpr int kScanSeg = 16;
-// single-pass geometry (lane = channel, NW waves of LS serial steps): the
-// LSTM keeps 6 steps per lane so that three 4-wave workgroups fit a CU
-template <class C> struct SpGeo;
-template <> struct SpGeo<prn::CellGRU> { static constexpr int LS = 8, NW = 4; };
-template <> struct SpGeo<prn::CellLSTM> { static constexpr int LS = 6, NW = 4; };
-int sp_chunk(int cell) {
-  return cell == PRN_CELL_DIAG_GRU ? SpGeo<prn::CellGRU>::LS * SpGeo<prn::CellGRU>::NW
-                                   : SpGeo<prn::CellLSTM>::LS * SpGeo<prn::CellLSTM>::NW;
+// single-pass geometry (lane = channel, NW = 4 waves of LS serial steps).
+// Longer chunks mean fewer carry look-backs per step, which is what bounds
+// the kernel when few chains (rows x 64-channel tiles) run side by side:
+// every chunk of a chain waits on the look-back of the chunks before it.
+// Measured at the long LSTM shape (8 chains): LS = 6, 8, 10, 12 took 1.00,
+// 0.97, 0.86, 0.78 ms; LS = 14 no longer fits 256 registers and took
+// 1.1 ms.  The GRU takes LS = 16 below 64 chains (4 chains: 0.25 -> 0.18
+// ms against LS = 8) and LS = 12 above (128 chains: 0.96 -> 0.91 ms;
+// LS = 16 took 1.05 ms there).
+// bf16 storage needs more registers per step (unpacking): the bf16 LSTM
+// keeps LS = 8 to stay within 256, and the bf16 GRU with many chains keeps
+// LS = 8 so that three workgroups still fit a CU (measured at 16 x 16384 x
+// 512: LS = 12 took 1.31 ms against 1.20 ms).
+constexpr int kSpNW = 4;
+constexpr int kSpLsLstm = 12, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12, kSpLsGruManyBf16 = 8;
+constexpr int64_t kSpManyChains = 64;
+int sp_ls(int cell, int dtype, int64_t n_chains) {
+  if (cell != PRN_CELL_DIAG_GRU) return dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm;
+  if (n_chains < kSpManyChains) return kSpLsGruFew;
+  return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
 }
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
 // below this many independent chains, chunks publish their aggregate before
@@ -134,6 +147,7 @@ Plan plan_tp(const prn_params* p, const Shape& sh, int K) {
 }
 
 struct PlanSp {
+  int ls;  // steps per lane
   int64_t n_ch, n_tiles, n_chains, n_wg;
   size_t status_off, n_status;  // words zeroed per launch: ticket, error, K*n_chains*n_ch statuses
   size_t agg_off, pre_off, rpart_off, total;
@@ -141,10 +155,11 @@ struct PlanSp {
 
 PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
   PlanSp pl{};
-  const int lc = sp_chunk(p->cell);
-  pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
+  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains);
+  const int lc = pl.ls * kSpNW;
+  pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_wg = pl.n_ch * pl.n_chains;
   const size_t nrec = size_t(K) * pl.n_chains * pl.n_ch;
   const size_t NC = sh.S * sh.S + sh.S;
@@ -261,10 +276,25 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
     float* rpart = res ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
     prn::k_zero_u32<<<unsigned((pl.n_status + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_status));
-    constexpr int LS = SpGeo<C>::LS, NW = SpGeo<C>::NW;
-    prn::k_newton_sp<C, DT, LS, NW><<<unsigned(pl.n_wg), 64 * NW, 0, st>>>(
-        static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
-        static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+    auto launch = [&](auto ls) {
+      constexpr int LS = decltype(ls)::value;
+      prn::k_newton_sp<C, DT, LS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+          static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
+          static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+    };
+    if constexpr (S == 2) {
+      if constexpr (DT == prn::kBF16)
+        launch(std::integral_constant<int, kSpLsLstmBf16>{});
+      else
+        launch(std::integral_constant<int, kSpLsLstm>{});
+    } else {
+      if (pl.ls == kSpLsGruFew)
+        launch(std::integral_constant<int, kSpLsGruFew>{});
+      else if constexpr (DT == prn::kBF16)
+        launch(std::integral_constant<int, kSpLsGruManyBf16>{});
+      else
+        launch(std::integral_constant<int, kSpLsGruMany>{});
+    }
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
     if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
