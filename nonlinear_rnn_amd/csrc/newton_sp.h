@@ -252,23 +252,29 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
     }
   }
 
-  auto residual_out = [&](int k, unsigned r) {
+  // residual r_k: each wave leaves its maximum in red[], and after the next
+  // workgroup barrier (the one that exchanges the waves' maps) thread 0
+  // combines them; red[] is not written again before the look-back barrier
+  auto residual_put = [&](unsigned r) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) r = max(r, static_cast<unsigned>(__shfl_xor(static_cast<int>(r), o, kWave)));
     if (lane == 0) red[w] = r;
-    __syncthreads();
+  };
+  auto residual_finish = [&](int k) {
     if (threadIdx.x == 0 && rpart && ticket < n_wg) {
+      unsigned r = red[0];
 #pragma unroll
       for (int v = 1; v < NW; ++v) r = max(r, red[v]);
       rpart[k * n_wg + ticket] = rmax_finish(r);
     }
   };
-  residual_out(0, rmax);
+  residual_put(rmax);
 
   for (int k = 0; k < K; ++k) {
     const int pb = k & 1;
     part[pb][w][lane] = acc;
     __syncthreads();
+    residual_finish(k);
 
     // ---- carry across chunks: one wave publishes and looks back ----
     if (w == NW - 1 && ticket < n_wg) {
@@ -381,8 +387,10 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         }
       }
     }
-    residual_out(k + 1, rmax);
+    residual_put(rmax);
   }
+  __syncthreads();
+  residual_finish(K);
 }
 
 }  // namespace prn
