@@ -11,6 +11,8 @@ Plain NumPy in float64, written to be checked by eye:
   newton   the sequential unroll (the truth) and the K-iteration Newton
            method with an explicit serial affine recurrence, plus the
            residual max|F(H)|
+  backward gradients through the recurrence: the reverse-time adjoint
+           recurrence at a given trajectory
   scan     exact (rational) affine-map composition, every bracketing, and
            the chunked three-phase scan
   rounding storage-dtype rounding (fp32, bf16 round-to-nearest-even)
@@ -20,4 +22,4 @@ the "Numerics contract" page, and the shapes/layout page on contiguity and
 ragged packs) it follows, or which definition it writes out where the pages
 leave the step open.
 """
-from . import cells, newton, proj, rounding, scan  # noqa: F401
+from . import backward, cells, newton, proj, rounding, scan  # noqa: F401

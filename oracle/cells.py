@@ -95,12 +95,60 @@ def lstm_jac(s, xp, a):
     return J
 
 
+# ---------------------------------------- input and weight partials ---
+# For the backward pass: d s'/d x_g and d s'/d a_g, per channel, as arrays
+# (..., S, G, d) with [..., p, g, :] = d s'_p / d x_g (resp. d a_g).  Every
+# gate is a function of its pre-activation u_g = x_g + a_g * m_g, where the
+# multiplier m_g is h for every gate except the GRU candidate (m_c = r h);
+# so d/d x_g = d/d u_g and d/d a_g = m_g d/d u_g.
+
+def gru_dx(s, xp, a):
+    """d h'/d x_g for g = z, r, c (chain rule through the pre-activations)."""
+    h, z, r, c = gru_gates(s, xp, a)
+    du_z = (c - h) * z * (1.0 - z)
+    du_c = z * (1.0 - c * c)
+    du_r = du_c * a[2] * h * r * (1.0 - r)
+    return np.stack([du_z, du_r, du_c], axis=-2)[..., None, :, :]
+
+
+def gru_da(s, xp, a):
+    h, z, r, c = gru_gates(s, xp, a)
+    d = gru_dx(s, xp, a)
+    m = np.stack([h, h, r * h], axis=-2)[..., None, :, :]
+    return d * m
+
+
+def lstm_dx(s, xp, a):
+    """d (c', h')/d x_g for g = i, f, o, g."""
+    c, h, i, f, o, g = lstm_gates(s, xp, a)
+    c1 = f * c + i * g
+    tc = np.tanh(c1)
+    dc = np.stack([g * i * (1.0 - i), c * f * (1.0 - f), np.zeros_like(c), i * (1.0 - g * g)], axis=-2)
+    dh = o[..., None, :] * (1.0 - tc * tc)[..., None, :] * dc
+    dh[..., 2, :] = tc * o * (1.0 - o)
+    return np.stack([dc, dh], axis=-3)
+
+
+def lstm_da(s, xp, a):
+    c, h = s[..., 0, :], s[..., 1, :]
+    return lstm_dx(s, xp, a) * h[..., None, None, :]
+
+
 CELLS = {
     "gru": (3, 1, gru_f, gru_jac),
     "lstm": (4, 2, lstm_f, lstm_jac),
+}
+PARTIALS = {
+    "gru": (gru_dx, gru_da),
+    "lstm": (lstm_dx, lstm_da),
 }
 
 
 def cell_fns(cell: str):
     """(G, S, f, jac) for a cell name."""
     return CELLS[cell]
+
+
+def cell_partials(cell: str):
+    """(dx, da) for a cell name: d s'/d x and d s'/d a, shaped (..., S, G, d)."""
+    return PARTIALS[cell]
