@@ -78,8 +78,13 @@ typedef struct {
   void* state_last_out;    /* optional (rows, S, d_h) storage dtype: final state of every
                               sequence (rows = B, or n_seqs for a pack); LSTM order (c, h) */
   void* workspace;         /* device scratch owned by the caller, 256-byte aligned         */
-  size_t workspace_bytes;  /* its size; must be >= prn_workspace_bytes(params, K)         */
+  size_t workspace_bytes;  /* its size; must be >= prn_workspace_bytes(params, K) (forward)
+                              or prn_backward_workspace_bytes(params) (backward)          */
   void* stream;            /* hipStream_t                                                 */
+  void* states_out;        /* optional (B, T, S, d_h) storage dtype, forward entry points:
+                              every state s_t of the returned trajectory (LSTM (c, h);
+                              for the GRU it equals H_out).  The backward pass takes it as
+                              its trajectory                                                */
 } prn_params;
 
 /* Input projection, once per forward:
@@ -109,7 +114,8 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias,
  *              Its contents are not read on the host; prn_validate_cu_seqlens
  *              checks a host copy.  Malformed contents give wrong results
  *              but never out-of-bounds accesses.
- *   H_out      (B, T, d_h) storage dtype: h of the K-th iterate
+ *   H_out      (B, T, d_h) storage dtype: h of the K-th iterate (and, when
+ *              params->states_out is set, every state component there)
  *   residual_out  NULL, or (K + 1) fp32: residual_out[k] = max|F(H^(k))| over
  *              batch, time, state component and channel, of the iterate as
  *              stored (H^(0) = 0).  A non-finite value reads as +Inf.  The
@@ -128,6 +134,47 @@ prn_status prn_sequential_forward(const void* xproj, const prn_params* params, c
 /* Bytes of workspace prn_newton_forward needs for these params and K
  * (0 on invalid params; see prn_last_error). */
 size_t prn_workspace_bytes(const prn_params* params, int32_t K);
+
+/* Backward pass: gradients of a loss L through the recurrence, the step a
+ * training iteration needs after the Newton forward (FAQs "train() vs
+ * eval()"; shapes/layout page, the train forward+backward surface of the
+ * diagonal cells and ragged packs).  The pages do not print the backward
+ * equations; this takes the gradient of the sequential recurrence
+ * s_t = f(s_{t-1}, x_t) at the given trajectory, which is the solution of
+ * the adjoint (transposed, reverse-time) linear recurrence
+ *     lam_t = dL/ds_t + J_{t+1}^T lam_{t+1}
+ * with J_{t+1} = df/ds at step t+1, cut to 0 where step t+1 is a segment
+ * head (its previous state is the segment's h0) and past the end of a row;
+ * dL/ds_t is dH_t in the h component plus, at the last step of a sequence,
+ * dstate_last.  It runs as a chunked parallel scan backwards in time (the
+ * forward's scan machinery with the chunk order reversed), then per step
+ *     dxproj_t = (ds_t/dxproj_t)^T lam_t
+ *     da      += (ds_t/da)^T lam_t          (summed over rows and steps)
+ *     dh0_j    = J_t^T lam_t                at the head t of sequence j
+ * and an empty segment passes its dstate_last to its dh0 unchanged.
+ *   xproj       (B, T, G, d_h) storage dtype, as given to the forward
+ *   h0          (rows, S, d_h) storage dtype or NULL (zeros), as given to the forward
+ *   cu_seqlens  NULL or the forward's ragged offsets (same contract)
+ *   states      (B, T, S, d_h) storage dtype: the trajectory s_1..s_T at which
+ *               the gradient is taken (states_out of the forward)
+ *   dH          (B, T, d_h) storage dtype: dL/dH_out
+ *   dstate_last (rows, S, d_h) storage dtype, or NULL for zero: dL/d state_last_out
+ *   dxproj_out  (B, T, G, d_h) storage dtype: dL/dxproj.  The projection's own
+ *               gradients are plain products of it: dW = dxproj^T x,
+ *               dx = dxproj W, dbias = sum of dxproj over tokens
+ *   da_out      (G, d_h) fp32: dL/da (overwritten, not accumulated)
+ *   dh0_out     (rows, S, d_h) storage dtype, or NULL
+ * params->a is the forward's a; params->workspace must hold at least
+ * prn_backward_workspace_bytes(params); state_last_out and states_out are
+ * not used.  The result is deterministic (fixed reduction orders). */
+prn_status prn_newton_backward(const void* xproj, const prn_params* params, const void* h0,
+                               const int32_t* cu_seqlens, const void* states, const void* dH,
+                               const void* dstate_last, void* dxproj_out, float* da_out,
+                               void* dh0_out);
+
+/* Bytes of workspace prn_newton_backward needs for these params (0 on
+ * invalid params; see prn_last_error). */
+size_t prn_backward_workspace_bytes(const prn_params* params);
 
 /* Host-side check of ragged offsets (the validate_cu_seqlens contract of
  * the shapes/layout page): cu_host has n_seqs + 1 entries, cu[0] = 0,

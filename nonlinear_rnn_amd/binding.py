@@ -27,7 +27,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # every symbol include/prn.h declares
 EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_workspace_bytes",
-           "prn_validate_cu_seqlens", "prn_last_error", "prn_version")
+           "prn_newton_backward", "prn_backward_workspace_bytes", "prn_validate_cu_seqlens", "prn_last_error",
+           "prn_version")
 
 
 class PrnError(RuntimeError):
@@ -50,6 +51,7 @@ class prn_params(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("states_out", ctypes.c_void_p),
     ]
 
 
@@ -71,10 +73,13 @@ def lib() -> ctypes.CDLL:
         L.prn_sequential_forward.argtypes = [vp, P, vp, vp, vp]
         L.prn_workspace_bytes.argtypes = [P, i32]
         L.prn_workspace_bytes.restype = ctypes.c_size_t
+        L.prn_newton_backward.argtypes = [vp, P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.prn_backward_workspace_bytes.argtypes = [P]
+        L.prn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
-        for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward",
+        for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_newton_backward",
                      "prn_validate_cu_seqlens"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
@@ -116,7 +121,7 @@ def _stream(stream) -> int:
 
 
 def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in: int = 0, n_seqs: int = 0,
-                a=None, state_last_out=None, workspace=None, stream=None) -> prn_params:
+                a=None, state_last_out=None, states_out=None, workspace=None, stream=None) -> prn_params:
     if cell not in CELLS:
         raise ValueError(f"unknown cell {cell!r}")
     if dtype not in DTYPES:
@@ -126,6 +131,7 @@ def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in
     p.B, p.T, p.d_in, p.d_h, p.n_seqs = B, T, d_in, d_h, n_seqs
     p.a = _ptr(a)
     p.state_last_out = _ptr(state_last_out)
+    p.states_out = _ptr(states_out)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.stream = _stream(stream) if torch.cuda.is_available() else 0
@@ -183,21 +189,69 @@ def _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell):
     return B, T, d_h, n_seqs
 
 
+def _states_out(states_out, xproj, cell):
+    _dev(states_out, "states_out", xproj.dtype)
+    B, T, _, d_h = xproj.shape
+    if states_out is not None and states_out.shape != (B, T, STATE[cell], d_h):
+        raise ValueError(f"states_out must be {(B, T, STATE[cell], d_h)}, got {tuple(states_out.shape)}")
+
+
 def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None, residual_out=None,
-                       state_last_out=None, workspace=None, stream=None) -> None:
+                       state_last_out=None, states_out=None, workspace=None, stream=None) -> None:
     B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
+    _states_out(states_out, xproj, cell)
     _dev(residual_out, "residual_out", torch.float32)
     if residual_out is not None and residual_out.numel() < K + 1:
         raise ValueError("residual_out needs K + 1 entries")
     p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
-                    workspace=workspace, stream=stream)
+                    states_out=states_out, workspace=workspace, stream=stream)
     _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
                                     _ptr(H_out), _ptr(residual_out)))
 
 
 def prn_sequential_forward(xproj, a, H_out, *, cell: str, h0=None, cu_seqlens=None, state_last_out=None,
-                           stream=None) -> None:
+                           states_out=None, stream=None) -> None:
     B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
+    _states_out(states_out, xproj, cell)
     p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
-                    stream=stream)
+                    states_out=states_out, stream=stream)
     _check(lib().prn_sequential_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), _ptr(cu_seqlens), _ptr(H_out)))
+
+
+def prn_backward_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, n_seqs: int = 0) -> int:
+    p = make_params(cell, dtype, B, T, d_h, n_seqs=n_seqs)
+    n = int(lib().prn_backward_workspace_bytes(ctypes.byref(p)))
+    if n == 0 and prn_last_error():
+        raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
+    return n
+
+
+def prn_newton_backward(xproj, a, states, dH, dxproj_out, da_out, *, cell: str, h0=None, cu_seqlens=None,
+                        dstate_last=None, dh0_out=None, workspace=None, stream=None) -> None:
+    """Gradients through the recurrence at the trajectory `states` (B,T,S,d_h):
+    dxproj_out (B,T,G,d_h), da_out (G,d_h) fp32 and optionally dh0_out (rows,S,d_h)."""
+    _dev(xproj, "xproj")
+    _dev(a, "a", torch.float32)
+    _dev(states, "states", xproj.dtype)
+    _dev(dH, "dH", xproj.dtype)
+    _dev(dxproj_out, "dxproj_out", xproj.dtype)
+    _dev(da_out, "da_out", torch.float32)
+    _dev(h0, "h0", xproj.dtype)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(dstate_last, "dstate_last", xproj.dtype)
+    _dev(dh0_out, "dh0_out", xproj.dtype)
+    B, T, G, d_h = xproj.shape
+    S = STATE[cell]
+    if G != GATES[cell] or a.shape != (G, d_h) or da_out.shape != (G, d_h):
+        raise ValueError(f"shape mismatch: xproj {tuple(xproj.shape)} a {tuple(a.shape)} da {tuple(da_out.shape)}")
+    if states.shape != (B, T, S, d_h) or dH.shape != (B, T, d_h) or dxproj_out.shape != xproj.shape:
+        raise ValueError(f"shape mismatch: states {tuple(states.shape)} dH {tuple(dH.shape)} "
+                         f"dxproj {tuple(dxproj_out.shape)}")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rows = B if cu_seqlens is None else n_seqs
+    for t, name in ((h0, "h0"), (dstate_last, "dstate_last"), (dh0_out, "dh0_out")):
+        if t is not None and t.shape != (rows, S, d_h):
+            raise ValueError(f"{name} must be {(rows, S, d_h)}, got {tuple(t.shape)}")
+    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, workspace=workspace, stream=stream)
+    _check(lib().prn_newton_backward(_ptr(xproj), ctypes.byref(p), _ptr(h0), _ptr(cu_seqlens), _ptr(states),
+                                     _ptr(dH), _ptr(dstate_last), _ptr(dxproj_out), _ptr(da_out), _ptr(dh0_out)))

@@ -223,7 +223,7 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
          const float* __restrict__ a, int64_t T, int64_t d_h, int64_t n_seqs, int64_t n_ch,
          const float* __restrict__ carry, typename Storage<DT>::T* __restrict__ Hnext,
          typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
-         float* __restrict__ agg_next, float* __restrict__ rpart) {
+         typename Storage<DT>::T* __restrict__ sout, float* __restrict__ agg_next, float* __restrict__ rpart) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, NC = S * S + S, LC = LS * NW;
@@ -297,6 +297,10 @@ k_tp_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
           for (int q = 0; q < S; ++q) hn[q * d_h] = ST::pack(s[q]);
         } else {
           Hout[(b * T + t) * d_h + ch] = ST::pack(s[S - 1]);
+          if (sout) {
+#pragma unroll
+            for (int q = 0; q < S; ++q) sout[((b * T + t) * S + q) * d_h + ch] = ST::pack(s[q]);
+          }
           if (slast && sg.last(t, T)) {
 #pragma unroll
             for (int q = 0; q < S; ++q) slast[(sg.seg * S + q) * d_h + ch] = ST::pack(s[q]);
@@ -347,7 +351,7 @@ __global__ void __launch_bounds__(kWave)
 k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
              const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
              int64_t n_seqs, typename Storage<DT>::T* __restrict__ Hout,
-             typename Storage<DT>::T* __restrict__ slast) {
+             typename Storage<DT>::T* __restrict__ slast, typename Storage<DT>::T* __restrict__ sout) {
   using ST = Storage<DT>;
   constexpr int G = C::G, S = C::S;
   const int64_t ch = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
@@ -370,6 +374,7 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
   if (h0) load_state<DT, S>(h0 + r * S * d_h + ch, d_h, s);
   const typename ST::T* xp = xproj + base * G * d_h + ch;
   typename ST::T* hp = Hout + base * d_h + ch;
+  typename ST::T* sp = sout ? sout + base * S * d_h + ch : nullptr;
   constexpr int U = 4;
   int64_t t = 0;
   for (; t + U <= len; t += U) {
@@ -383,6 +388,10 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
 #pragma unroll
       for (int q = 0; q < S; ++q) s[q] = o[q];
       hp[(t + u) * d_h] = ST::pack(s[S - 1]);
+      if (sp) {
+#pragma unroll
+        for (int q = 0; q < S; ++q) sp[((t + u) * S + q) * d_h] = ST::pack(s[q]);
+      }
     }
   }
   for (; t < len; ++t) {
@@ -393,6 +402,10 @@ k_sequential(const typename Storage<DT>::T* __restrict__ xproj, const typename S
 #pragma unroll
     for (int q = 0; q < S; ++q) s[q] = o[q];
     hp[t * d_h] = ST::pack(s[S - 1]);
+    if (sp) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) sp[(t * S + q) * d_h] = ST::pack(s[q]);
+    }
   }
   if (slast) {
 #pragma unroll

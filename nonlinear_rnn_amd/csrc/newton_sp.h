@@ -166,7 +166,8 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
             int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
             typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
-            float* __restrict__ rpart, SpRecords rec, unsigned spin_limit, bool agg_first) {
+            typename Storage<DT>::T* __restrict__ sout, float* __restrict__ rpart, SpRecords rec,
+            unsigned spin_limit, bool agg_first) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, LC = LS * NW;
@@ -212,6 +213,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   unsigned rmax = 0;
   const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
   typename ST::T* hp = Hout + (b * T + t0) * d_h + ch;
+  typename ST::T* sp = sout ? sout + (b * T + t0) * S * d_h + ch : nullptr;
 
   // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
   if (fast) {
@@ -334,7 +336,13 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           float fv[S], xj[G];
           xs_get(j, xj);
           C::f(xj, pr, cf.as, cf.a, fv);
-          if (ch_ok) hp[j * d_h] = ST::pack(s[S - 1]);
+          if (ch_ok) {
+            hp[j * d_h] = ST::pack(s[S - 1]);
+            if (sp) {
+#pragma unroll
+              for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
+            }
+          }
 #pragma unroll
           for (int q = 0; q < S; ++q) {
             const float sr = ST::round(s[q]);
@@ -372,6 +380,10 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             C::f(xj, p, cf.as, cf.a, fv);
             if (ch_ok) {
               hp[j * d_h] = ST::pack(s[S - 1]);
+              if (sp) {
+#pragma unroll
+                for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
+              }
               if (slast && st.last(t, T)) {
 #pragma unroll
                 for (int q = 0; q < S; ++q) slast[(st.seg * S + q) * d_h + ch] = ST::pack(s[q]);

@@ -12,6 +12,7 @@
 #include <string>
 #include <type_traits>
 
+#include "backward.h"
 #include "newton_kernels.h"
 #include "newton_sp.h"
 #include "proj.h"
@@ -114,9 +115,27 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
   if (sh.ragged && !cu) return fail(PRN_ERR_INVALID_ARG, "n_seqs > 0 but cu_seqlens is NULL");
   if (!sh.ragged && cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
   if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(H_out, sh.elt) ||
-      misaligned(p->state_last_out, sh.elt) || misaligned(p->a, 4) || misaligned(cu, 4))
+      misaligned(p->state_last_out, sh.elt) || misaligned(p->states_out, sh.elt) || misaligned(p->a, 4) ||
+      misaligned(cu, 4))
     return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   return PRN_OK;
+}
+
+// backward geometry: the forward's three-phase chunks, walked in reverse
+struct PlanBw {
+  int64_t n_ch;
+  size_t agg_off, carry_off, da_off, total;
+};
+
+PlanBw plan_bw(const prn_params* p, const Shape& sh) {
+  PlanBw pl{};
+  pl.n_ch = (p->T + kLC - 1) / kLC;
+  const size_t units = size_t(p->B) * pl.n_ch * p->d_h;
+  pl.agg_off = 0;
+  pl.carry_off = align_up(units * (sh.S * sh.S + sh.S) * 4);
+  pl.da_off = pl.carry_off + align_up(units * sh.S * 4);
+  pl.total = pl.da_off + align_up(units * sh.G * 4);
+  return pl;
 }
 
 struct Plan {
@@ -236,13 +255,13 @@ prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, 
       const T* hprev = k == 1 ? nullptr : iter_buf(k - 1);
       prn::k_tp_fix<C, DT, kLS, kNW, true, false><<<grid, block, 0, st>>>(
           xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, iter_buf(k), nullptr, nullptr,
-          agg, slot(k));
+          nullptr, agg, slot(k));
       prn::k_tp_scan<S, kScanSeg><<<sgrid, sblock, 0, st>>>(agg, carry, p->d_h, pl.n_ch);
     }
     const T* hprev = K == 1 ? nullptr : iter_buf(K - 1);
     prn::k_tp_fix<C, DT, kLS, kNW, false, true><<<grid, block, 0, st>>>(
-        xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, nullptr, Hout, slast, nullptr,
-        slot(K));
+        xproj, hprev, h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, carry, nullptr, Hout, slast,
+        static_cast<T*>(p->states_out), nullptr, slot(K));
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
     if (res) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(res, K + 1);
@@ -280,7 +299,8 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
       constexpr int LS = decltype(ls)::value;
       prn::k_newton_sp<C, DT, LS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
           static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
-          static_cast<T*>(Hout_v), slast, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+          static_cast<T*>(Hout_v), slast, static_cast<T*>(p->states_out), rpart, rec, kSpinLimit,
+          pl.n_chains < kAggFirstBelowChains);
     };
     if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
@@ -322,13 +342,102 @@ prn_status sequential(const prn_params* p, const Shape& sh, const void* xproj_v,
   const dim3 grid(unsigned((p->d_h + 63) / 64), unsigned(sh.rows));
   prn::k_sequential<C, DT><<<grid, 64, 0, st>>>(static_cast<const T*>(xproj_v), static_cast<const T*>(h0_v), cu,
                                                 p->a, p->T, p->d_h, p->n_seqs, static_cast<T*>(Hout_v),
-                                                static_cast<T*>(p->state_last_out));
+                                                static_cast<T*>(p->state_last_out), static_cast<T*>(p->states_out));
   return launched("prn_sequential_forward");
+}
+
+template <class C, int DT>
+prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, const void* h0_v, const int32_t* cu,
+                    const void* states_v, const void* dH_v, const void* dsl_v, void* dxproj_v, float* da,
+                    void* dh0_v) {
+  using T = typename prn::Storage<DT>::T;
+  constexpr int G = C::G, S = C::S;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const PlanBw pl = plan_bw(p, sh);
+  const T* xproj = static_cast<const T*>(xproj_v);
+  const T* h0 = static_cast<const T*>(h0_v);
+  const T* states = static_cast<const T*>(states_v);
+  const T* dH = static_cast<const T*>(dH_v);
+  const T* dsl = static_cast<const T*>(dsl_v);
+  T* dxproj = static_cast<T*>(dxproj_v);
+  T* dh0 = static_cast<T*>(dh0_v);
+  if (p->T > 0) {
+    char* ws = static_cast<char*>(p->workspace);
+    float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
+    float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
+    float* dap = reinterpret_cast<float*>(ws + pl.da_off);
+    const dim3 grid(unsigned(pl.n_ch), unsigned((p->d_h + 63) / 64), unsigned(p->B));
+    const dim3 block(64 * kNW);
+    prn::k_bw_reduce<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
+                                                              p->n_seqs, pl.n_ch, agg);
+    prn::k_tp_scan<S, kScanSeg><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(p->B)), 64 * kScanSeg, 0, st>>>(
+        agg, carry, p->d_h, pl.n_ch);
+    prn::k_bw_fix<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
+                                                           p->n_seqs, pl.n_ch, carry, dxproj, dh0, dap);
+    prn::k_bw_da_reduce<G><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(G)), 256, 0, st>>>(
+        dap, p->B * pl.n_ch, p->d_h, da);
+  } else {
+    prn::k_zero_f32<<<unsigned((G * p->d_h + 255) / 256), 256, 0, st>>>(da, G * p->d_h);
+    if (dh0 && !sh.ragged) {
+      const int64_t n = p->B * S * p->d_h;
+      prn::k_copy_or_zero<T><<<unsigned((n + 255) / 256), 256, 0, st>>>(dsl, dh0, n);
+    }
+  }
+  if (dh0 && sh.ragged) {
+    const int64_t n = p->n_seqs * S * p->d_h;
+    prn::k_bw_empty_dh0<DT, S><<<unsigned((n + 255) / 256), 256, 0, st>>>(cu, p->n_seqs, p->d_h, dsl, dh0);
+  }
+  return launched("prn_newton_backward");
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t prn_backward_workspace_bytes(const prn_params* p) {
+  Shape sh;
+  if (check_common(p, &sh) != PRN_OK) return 0;
+  return plan_bw(p, sh).total;
+}
+
+prn_status prn_newton_backward(const void* xproj, const prn_params* p, const void* h0, const int32_t* cu,
+                               const void* states, const void* dH, const void* dstate_last, void* dxproj_out,
+                               float* da_out, void* dh0_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (!p->a) return fail(PRN_ERR_INVALID_ARG, "recurrent weights a is NULL");
+  if (!da_out) return fail(PRN_ERR_INVALID_ARG, "da_out is NULL");
+  if (p->T > 0 && (!xproj || !states || !dH || !dxproj_out))
+    return fail(PRN_ERR_INVALID_ARG, "xproj, states, dH or dxproj_out is NULL");
+  if (sh.ragged && !cu) return fail(PRN_ERR_INVALID_ARG, "n_seqs > 0 but cu_seqlens is NULL");
+  if (!sh.ragged && cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
+  if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(states, sh.elt) || misaligned(dH, sh.elt) ||
+      misaligned(dstate_last, sh.elt) || misaligned(dxproj_out, sh.elt) || misaligned(dh0_out, sh.elt) ||
+      misaligned(da_out, 4) || misaligned(p->a, 4) || misaligned(cu, 4))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
+  const PlanBw pl = plan_bw(p, sh);
+  if (p->T > 0) {
+    if (!p->workspace || p->workspace_bytes < pl.total)
+      return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
+                  p->workspace, pl.total);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+      return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    if (pl.n_ch > 0x7fffffff) return fail(PRN_ERR_UNSUPPORTED, "sequence too long");
+  }
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32)
+      return backward<prn::CellGRU, prn::kF32>(p, sh, xproj, h0, cu, states, dH, dstate_last, dxproj_out, da_out,
+                                                dh0_out);
+    return backward<prn::CellGRU, prn::kBF16>(p, sh, xproj, h0, cu, states, dH, dstate_last, dxproj_out, da_out,
+                                               dh0_out);
+  }
+  if (p->dtype == PRN_F32)
+    return backward<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, cu, states, dH, dstate_last, dxproj_out, da_out,
+                                               dh0_out);
+  return backward<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, cu, states, dH, dstate_last, dxproj_out, da_out,
+                                              dh0_out);
+}
 
 int32_t prn_version(void) { return 100; }
 

@@ -148,6 +148,29 @@ struct CellGRU {
     const float J = fmaf(z, dc, fmaf(c - h, dz, omz));
     return {J, fmaf(-J, h, fv)};
   }
+  // Backward of one step at (s, x) with cotangent lam = dL/dh': the
+  // pre-activation gradients du_g (= dL/dx_g), dL/da_g = du_g * m_g (m = h,
+  // h, r h) and dL/dh = J^T lam.
+  static __device__ __forceinline__ void vjp(const float* xs, const float* s, const float* as, const float* a,
+                                             const float* lam, float* dx, float* da, float* dprev) {
+    const float h = s[0];
+    const float z = sig_s(fmaf(as[0], h, xs[0]));
+    const float r = sig_s(fmaf(as[1], h, xs[1]));
+    const float rh = r * h;
+    const float c = tanh_s(fmaf(as[2], rh, xs[2]));
+    const float L = lam[0];
+    const float zl = z * L;
+    const float du_z = L * (c - h) * z * (1.0f - z);
+    const float du_c = zl * fmaf(-c, c, 1.0f);
+    const float du_r = du_c * a[2] * h * r * (1.0f - r);
+    dx[0] = du_z;
+    dx[1] = du_r;
+    dx[2] = du_c;
+    da[0] = du_z * h;
+    da[1] = du_r * h;
+    da[2] = du_c * rh;
+    dprev[0] = fmaf(du_c * a[2], r, fmaf(du_r, a[1], fmaf(du_z, a[0], L - zl)));
+  }
 };
 
 struct CellLSTM {
@@ -196,6 +219,32 @@ struct CellLSTM {
     m.b0 = c1 - fmaf(fg, c, j01 * h);
     m.b1 = h1 - fmaf(j10, c, j11 * h);
     return m;
+  }
+  // Backward of one step at (s, x) with cotangent lam = (dL/dc', dL/dh'):
+  // pre-activation gradients du_g (= dL/dx_g), dL/da_g = du_g * h and
+  // (dL/dc, dL/dh) = J^T lam.
+  static __device__ __forceinline__ void vjp(const float* xs, const float* s, const float* as, const float* a,
+                                             const float* lam, float* dx, float* da, float* dprev) {
+    const float c = s[0], h = s[1];
+    const float ig = sig_s(fmaf(as[0], h, xs[0]));
+    const float fg = sig_s(fmaf(as[1], h, xs[1]));
+    const float og = sig_s(fmaf(as[2], h, xs[2]));
+    const float gg = tanh_s(fmaf(as[3], h, xs[3]));
+    const float c1 = fmaf(fg, c, ig * gg);
+    const float tc = tanh_s(c1 * kTanhScale);
+    const float dc1 = fmaf(lam[1] * og, fmaf(-tc, tc, 1.0f), lam[0]);  // total dL/dc'
+    const float du_i = dc1 * gg * ig * (1.0f - ig);
+    const float du_f = dc1 * c * fg * (1.0f - fg);
+    const float du_o = lam[1] * tc * og * (1.0f - og);
+    const float du_g = dc1 * ig * fmaf(-gg, gg, 1.0f);
+    dx[0] = du_i;
+    dx[1] = du_f;
+    dx[2] = du_o;
+    dx[3] = du_g;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) da[g] = dx[g] * h;
+    dprev[0] = dc1 * fg;
+    dprev[1] = fmaf(du_g, a[3], fmaf(du_o, a[2], fmaf(du_f, a[1], du_i * a[0])));
   }
 };
 

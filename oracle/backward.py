@@ -22,8 +22,8 @@ Then, per step,
     dL/dx_t  = (d s_t/d x_t)^T lam_t           (the projected inputs)
     dL/da   += (d s_t/d a)^T lam_t             (summed over rows and steps)
     dL/dh0_j = J_t^T lam_t at the head t of segment j
-and an empty segment (final state = its h0) passes its final-state gradient
-to its h0 unchanged.
+and an empty segment or a zero-length row (final state = its h0, as in the
+forward) passes its final-state gradient to its h0 unchanged.
 """
 from __future__ import annotations
 
@@ -61,7 +61,10 @@ def adjoint(cell, xp, a, states, dH, h0=None, cu_seqlens=None, dstate_last=None)
     if dstate_last is not None:
         dsl = np.asarray(dstate_last, dtype=np.float64)
         if cu_seqlens is None:
-            g[:, T - 1] += dsl
+            if T > 0:
+                g[:, T - 1] += dsl
+            else:                    # a zero-length row ends in its h0
+                dh0 += dsl
         else:
             cu = np.asarray(cu_seqlens, dtype=np.int64)
             for j in range(rows):

@@ -52,7 +52,8 @@ def head_segments(B: int, T: int, cu_seqlens=None) -> np.ndarray:
     """
     hs = np.full((B, T), -1, dtype=np.int64)
     if cu_seqlens is None:
-        hs[:, 0] = np.arange(B)
+        if T > 0:                      # a zero-length row has no step, so no head
+            hs[:, 0] = np.arange(B)
         return hs
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     assert B == 1 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)

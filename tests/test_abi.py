@@ -131,3 +131,34 @@ def test_k_table_and_residual_gate_on_host():
         with pytest.raises(prn.NewtonDivergenceError):
             prn.gate_residual([0.9, bad], torch.float32)
     prn.gate_residual([0.9, 1.0], torch.float32, residual_warn=2.0)   # exactly 1.0 passes (">" gate)
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(cell=7), {}, B.PRN_ERR_INVALID_ARG),
+    (dict(a=None), {}, B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(da=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(states=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(dH=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(dx=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(cu=FAKE), B.PRN_ERR_INVALID_ARG),                  # rectangular with offsets
+    (dict(a=FAKE), dict(dsl=FAKE + 2), B.PRN_ERR_INVALID_ARG),             # misaligned
+    (dict(a=FAKE), {}, B.PRN_ERR_WORKSPACE),                              # no workspace
+    (dict(a=FAKE, workspace=FAKE, workspace_bytes=64), {}, B.PRN_ERR_WORKSPACE),
+    (dict(a=FAKE, workspace=FAKE + 64, workspace_bytes=1 << 40), {}, B.PRN_ERR_WORKSPACE),   # misaligned
+])
+def test_newton_backward_rejects_bad_arguments_before_launch(kw, args, status):
+    p = _params(**kw)
+    a = dict(xproj=FAKE, h0=None, cu=None, states=FAKE, dH=FAKE, dsl=None, dx=FAKE, da=FAKE, dh0=None)
+    a.update(args)
+    st = B.lib().prn_newton_backward(a["xproj"], ctypes.byref(p), a["h0"], a["cu"], a["states"], a["dH"],
+                                     a["dsl"], a["dx"], a["da"], a["dh0"])
+    assert st == status, B.prn_last_error()
+    assert B.prn_last_error()
+
+
+def test_backward_workspace_bytes():
+    w = B.prn_backward_workspace_bytes("lstm", torch.float32, 2, 1000, 64)
+    assert w > 0 and w % 256 == 0
+    assert B.prn_backward_workspace_bytes("gru", torch.float32, 2, 1000, 64) < w
+    p = _params(d_h=0)
+    assert B.lib().prn_backward_workspace_bytes(ctypes.byref(p)) == 0

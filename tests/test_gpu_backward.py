@@ -1,0 +1,224 @@
+"""GPU parity of the backward pass (prn_newton_backward) against the oracle's
+adjoint recurrence, on the same stored numbers: the GPU forward's trajectory
+(states_out), the projected inputs, h0, dL/dH and dL/d(final state), all
+upcast to float64 for the oracle.
+
+Tolerances (max-abs, relative to 1 + max|reference| of the output):
+  * fp32 storage: dxproj and dh0 1e-5, da 1e-4 (da sums B*T products in
+    fp32: about sqrt(B*T) roundings of 2^-24 of terms up to the size of the
+    result);
+  * bf16 storage: dxproj and dh0 are stored in bf16 (one rounding, 2^-9
+    relative) plus the fp32 arithmetic: 1e-2; da stays fp32: 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TORCH_DT, gpu_run, say, small_inputs, to_dev, to_f64
+from nonlinear_rnn_amd import binding as B
+from oracle import backward as obackward
+from oracle import rounding as oround
+from workloads import Workload, WORKLOADS, random_state
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    Workload("gru_small", "gru", 3, 1000, 24, 80, "f32", 3),
+    Workload("lstm_small", "lstm", 2, 777, 16, 72, "f32", 2),
+    Workload("gru_bf16_small", "gru", 2, 600, 32, 64, "bf16", 3),
+    Workload("lstm_bf16_small", "lstm", 2, 300, 16, 130, "bf16", 3),
+    Workload("gru_ragged_small", "gru", 1, 1500, 16, 40, "f32", 3, n_seqs=7),
+    Workload("lstm_ragged_small", "lstm", 1, 900, 16, 64, "f32", 3, n_seqs=5, seg_lo=1, seg_hi=400),
+    WORKLOADS["gru_tiny"],
+]
+IDS = [w.name for w in SMALL]
+
+
+def rel_err(got, ref):
+    return float(np.abs(got - ref).max() / (1.0 + np.abs(ref).max())) if ref.size else 0.0
+
+
+def tols(w):
+    return (1e-5, 1e-4) if w.dtype == "f32" else (1e-2, 1e-4)
+
+
+def gpu_forward_states(w, inp, K, h0=None, cu=None, xproj=None):
+    """Newton forward with states_out; returns (xproj, H, states, last)."""
+    dt = TORCH_DT[w.dtype]
+    out = gpu_run(w, inp, K, h0=h0, cu=cu, xproj=xproj)
+    xproj = out["xproj"]
+    a = torch.from_numpy(inp["a"]).cuda()
+    cu = inp["cu_seqlens"] if cu is None else cu
+    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    n_seqs = 0 if cu is None else len(cu) - 1
+    rows = w.B if cu is None else n_seqs
+    H = torch.empty((w.B, w.T, w.d_h), dtype=dt, device="cuda")
+    states = torch.full((w.B, w.T, w.S, w.d_h), float("nan"), dtype=dt, device="cuda")
+    last = torch.empty((rows, w.S, w.d_h), dtype=dt, device="cuda")
+    ws_n = B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, K, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    h0_d = None if h0 is None else to_dev(h0, w.dtype)
+    B.prn_newton_forward(xproj, a, K, H, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, state_last_out=last,
+                         states_out=states, workspace=ws)
+    torch.cuda.synchronize()
+    return xproj, H, states, last
+
+
+def gpu_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None, want_dh0=True):
+    dt = TORCH_DT[w.dtype]
+    a = torch.from_numpy(inp["a"]).cuda()
+    cu = inp["cu_seqlens"] if cu is None else cu
+    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    n_seqs = 0 if cu is None else len(cu) - 1
+    rows = w.B if cu is None else n_seqs
+    dx = torch.full_like(xproj, float("nan"))
+    da = torch.full((w.G, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
+    dh0 = torch.full((rows, w.S, w.d_h), float("nan"), dtype=dt, device="cuda") if want_dh0 else None
+    ws_n = B.prn_backward_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    h0_d = None if h0 is None else to_dev(h0, w.dtype)
+    B.prn_newton_backward(xproj, a, states, dH, dx, da, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, dstate_last=dsl,
+                          dh0_out=dh0, workspace=ws)
+    torch.cuda.synchronize()
+    return dx, da, dh0
+
+
+def oracle_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None):
+    cu = inp["cu_seqlens"] if cu is None else cu
+    return obackward.adjoint(w.cell, to_f64(xproj), inp["a"].astype(np.float64), to_f64(states), to_f64(dH),
+                             h0=None if h0 is None else oround.store(h0, w.dtype), cu_seqlens=cu,
+                             dstate_last=None if dsl is None else to_f64(dsl))
+
+
+def random_grads(w, rows, seed):
+    rng = np.random.default_rng(seed)
+    dH = to_dev(rng.standard_normal((w.B, w.T, w.d_h)), w.dtype)
+    dsl = to_dev(rng.standard_normal((rows, w.S, w.d_h)), w.dtype)
+    return dH, dsl
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_states_out_is_the_trajectory(w):
+    """states_out holds every state: its h component is H_out, and at a
+    sequence end it is the final state."""
+    say(f"[case] states_out {w}")
+    inp = small_inputs(w)
+    rows = w.B if inp["cu_seqlens"] is None else w.n_seqs
+    h0 = random_state(w, seed=3, rows=rows)
+    xproj, H, states, last = gpu_forward_states(w, inp, w.K, h0=h0)
+    assert torch.equal(states[..., w.S - 1, :], H)
+    cu = inp["cu_seqlens"]
+    if cu is None:
+        assert torch.equal(states[:, -1], last)
+    else:
+        for j in range(len(cu) - 1):
+            if cu[j + 1] > cu[j]:
+                assert torch.equal(states[0, cu[j + 1] - 1], last[j])
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_backward_matches_oracle_adjoint(w):
+    say(f"[case] backward {w}")
+    inp = small_inputs(w)
+    cu = inp["cu_seqlens"]
+    rows = w.B if cu is None else w.n_seqs
+    h0 = random_state(w, seed=4, rows=rows)
+    xproj, H, states, last = gpu_forward_states(w, inp, w.K, h0=h0)
+    dH, dsl = random_grads(w, rows, seed=7)
+    dx, da, dh0 = gpu_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+    rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+    e_dx, e_da, e_dh0 = rel_err(to_f64(dx), rdx), rel_err(to_f64(da), rda), rel_err(to_f64(dh0), rdh0)
+    say(f"  {w.name}: dxproj {e_dx:.2e}  da {e_da:.2e}  dh0 {e_dh0:.2e}  (max|dxproj| {np.abs(rdx).max():.3g}, "
+        f"max|da| {np.abs(rda).max():.3g})")
+    t_x, t_a = tols(w)
+    assert e_dx <= t_x and e_dh0 <= t_x and e_da <= t_a
+
+
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[4]], ids=[SMALL[1].name, SMALL[4].name])
+def test_backward_optional_arguments(w):
+    """No h0, no dstate_last, no dh0_out: the same as zeros / not written."""
+    inp = small_inputs(w)
+    cu = inp["cu_seqlens"]
+    rows = w.B if cu is None else w.n_seqs
+    xproj, H, states, last = gpu_forward_states(w, inp, w.K)
+    dH, _ = random_grads(w, rows, seed=8)
+    dx, da, _ = gpu_backward(w, inp, xproj, states, dH, want_dh0=False)
+    dx2, da2, dh0 = gpu_backward(w, inp, xproj, states, dH, dsl=torch.zeros((rows, w.S, w.d_h),
+                                 dtype=TORCH_DT[w.dtype], device="cuda"))
+    assert torch.equal(dx, dx2) and torch.equal(da, da2)
+    rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH)
+    assert rel_err(to_f64(dx), rdx) <= tols(w)[0] and rel_err(to_f64(dh0), rdh0) <= tols(w)[0]
+
+
+def test_backward_is_deterministic():
+    w = SMALL[1]
+    inp = small_inputs(w)
+    xproj, H, states, last = gpu_forward_states(w, inp, w.K)
+    dH, dsl = random_grads(w, w.B, seed=9)
+    r1 = gpu_backward(w, inp, xproj, states, dH, dsl=dsl)
+    r2 = gpu_backward(w, inp, xproj, states, dH, dsl=dsl)
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_backward_edge_shapes(cell):
+    """T = 0 (da = 0, dh0 = dstate_last), T = 1, empty and one-step segments."""
+    G, S = (3, 1) if cell == "gru" else (4, 2)
+    d = 70
+    for name, B_, T, cu in [("T0", 2, 0, None), ("T1", 3, 1, None), ("one-chunk", 1, 5, None),
+                            ("ragged-empty", 1, 70, [0, 0, 33, 33, 69, 70]), ("ragged-T0", 1, 0, [0, 0, 0])]:
+        n_seqs = 0 if cu is None else len(cu) - 1
+        w = Workload(f"{cell}_{name}", cell, B_, T, 8, d, "f32", 2, n_seqs=n_seqs)
+        say(f"[case] backward edge {w}")
+        rng = np.random.default_rng(12)
+        inp = {"a": rng.uniform(-0.5, 0.5, (G, d)).astype(np.float32),
+               "cu_seqlens": None if cu is None else np.asarray(cu, dtype=np.int32)}
+        rows = B_ if cu is None else n_seqs
+        h0 = random_state(w, seed=5, rows=rows)
+        xproj = to_dev(rng.standard_normal((B_, T, G, d)), "f32")
+        if T == 0:
+            states = torch.empty((B_, 0, S, d), dtype=torch.float32, device="cuda")
+        else:
+            xproj, H, states, last = gpu_forward_states(w, inp, 2, h0=h0, xproj=xproj)
+        dH, dsl = random_grads(w, rows, seed=6)
+        dx, da, dh0 = gpu_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+        rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+        assert rel_err(to_f64(dx), rdx) <= 1e-5 and rel_err(to_f64(da), rda) <= 1e-4, name
+        assert rel_err(to_f64(dh0), rdh0) <= 1e-5, name
+
+
+SAMPLE = {"lstm_t131k": ([0, 1], [0, 130, 255]), "gru_ragged": ([0], [0, 77, 255]), "gru_bf16": ([15], [3, 511])}
+
+
+@pytest.mark.parametrize("name", list(SAMPLE))
+def test_backward_full_size_sampled(name):
+    """At the full workload sizes: sampled channels (channels never interact,
+    so a channel subset of the adjoint is an exact sub-problem)."""
+    w = WORKLOADS[name]
+    say(f"[case] backward full size {w}")
+    inp = small_inputs(w)
+    cu = inp["cu_seqlens"]
+    rows = w.B if cu is None else w.n_seqs
+    xproj, H, states, last = gpu_forward_states(w, inp, w.K)
+    dH, dsl = random_grads(w, rows, seed=10)
+    dx, da, dh0 = gpu_backward(w, inp, xproj, states, dH, dsl=dsl)
+    rws, chs = SAMPLE[name]
+    if cu is not None:
+        rws = [0]
+    sel = lambda t, ax: t[rws][..., chs] if ax else t[..., chs]
+    sub_inp = dict(inp, a=inp["a"][:, chs])
+    sw = Workload(w.name, w.cell, len(rws), w.T, w.d_in, len(chs), w.dtype, w.K, n_seqs=w.n_seqs)
+    sub_dsl = dsl[:, :, chs] if cu is not None else dsl[rws][:, :, chs]
+    rdx, rda, rdh0 = obackward.adjoint(w.cell, to_f64(sel(xproj, 1)), sub_inp["a"].astype(np.float64),
+                                       to_f64(sel(states, 1)), to_f64(sel(dH, 1)), cu_seqlens=cu,
+                                       dstate_last=to_f64(sub_dsl))
+    got_dh0 = dh0[:, :, chs] if cu is not None else dh0[rws][:, :, chs]
+    e_dx, e_dh0 = rel_err(to_f64(sel(dx, 1)), rdx), rel_err(to_f64(got_dh0), rdh0)
+    say(f"  {name}: dxproj {e_dx:.2e} dh0 {e_dh0:.2e}")
+    t_x, t_a = tols(sw)
+    assert e_dx <= t_x and e_dh0 <= t_x
+    if cu is not None or len(rws) == w.B:   # da sums over all rows: comparable only when all rows are sampled
+        e_da = rel_err(to_f64(da[:, chs]), rda)
+        say(f"  {name}: da {e_da:.2e}")
+        assert e_da <= t_a

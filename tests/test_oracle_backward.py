@@ -111,3 +111,14 @@ def test_gradient_of_a_cut_sequence_does_not_cross_a_head():
     dxp, _, dh0 = backward.adjoint("gru", xp, a, states, dH, h0=h0, cu_seqlens=cu)
     assert np.all(dxp[0, :4] == 0.0) and np.all(dh0[0] == 0.0)
     assert np.all(dxp[0, 4:] != 0.0) and np.all(dh0[1] != 0.0)
+
+
+@pytest.mark.parametrize("cell,G,S", CELLS)
+def test_zero_length_rows_pass_final_state_gradient_to_h0(cell, G, S):
+    """A zero-length row (or an all-empty pack) ends in its h0."""
+    d = 3
+    dsl = np.arange(2 * S * d, dtype=np.float64).reshape(2, S, d)
+    for B_, cu in ((2, None), (1, [0, 0, 0])):
+        dxp, da, dh0 = backward.adjoint(cell, np.zeros((B_, 0, G, d)), np.zeros((G, d)), np.zeros((B_, 0, S, d)),
+                                        np.zeros((B_, 0, d)), cu_seqlens=cu, dstate_last=dsl)
+        assert dxp.shape == (B_, 0, G, d) and np.all(da == 0.0) and np.array_equal(dh0, dsl)
