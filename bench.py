@@ -41,6 +41,14 @@ def algorithmic_newton_bytes(w) -> float:
     return float(w.tokens) * w.d_h * per * elt
 
 
+def algorithmic_backward_bytes(w) -> float:
+    """Bytes the backward must move per forward: per channel-token, read the
+    projected inputs (G), the previous state (S) and dL/dh (1) once, and
+    write dL/dxproj (G)."""
+    elt = 4 if w.dtype == "f32" else 2
+    return float(w.tokens) * w.d_h * (2 * w.G + w.S + 1) * elt
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources; a profile taken from other sources is stale."""
     import glob
@@ -122,6 +130,7 @@ def main() -> int:
     ap.add_argument("--workload", default="lstm_t131k")
     ap.add_argument("--K", type=int, default=None, help="override the workload's Newton depth")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size reference for byte counters)")
@@ -201,6 +210,42 @@ def main() -> int:
     t_step = np.array([e[0].elapsed_time(e[2]) for e in evs])
     print(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
+    backward = None
+    if not args.no_backward:
+        # the backward pass at the trajectory of one forward (states_out), timed on its own
+        states = torch.empty((w.B, w.T, w.S, w.d_h), dtype=dt, device=dev)
+        B.prn_newton_forward(xproj, a, w.K, H, cell=w.cell, cu_seqlens=cu, residual_out=res, workspace=ws,
+                             states_out=states, stream=stream)
+        gen = torch.Generator(device=dev).manual_seed(1)
+        dH = torch.randn((w.B, w.T, w.d_h), generator=gen, device=dev).to(dt)
+        dxp = torch.empty_like(xproj)
+        da = torch.empty((w.G, w.d_h), dtype=torch.float32, device=dev)
+        bws = torch.empty(max(B.prn_backward_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, n_seqs=n_seqs), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            B.prn_newton_backward(xproj, a, states, dH, dxp, da, cell=w.cell, cu_seqlens=cu, workspace=bws,
+                                  stream=stream)
+        for _ in range(args.warmup):
+            bstep()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            bev[i][0].record(stream)
+            bstep()
+            bev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_bw = np.array([e[0].elapsed_time(e[1]) for e in bev])
+        bw_ms = float(t_bw.mean())
+        bw_bytes = algorithmic_backward_bytes(w)
+        backward = {"kernels": "k_bw_reduce + k_tp_scan + k_bw_fix + k_bw_da_reduce (prn_newton_backward)",
+                    "ms_mean": bw_ms, "ms_min": float(t_bw.min()), "tokens_per_s": w.tokens / (bw_ms * 1e-3),
+                    "roofline": {"bound": "hbm", "achieved": bw_bytes / (bw_ms * 1e-3) / 1e9,
+                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": bw_bytes / (bw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                 "traffic": None, "algorithmic_bytes": bw_bytes}}
+        print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
+
     residuals = res.cpu().tolist()
     ms_step = wall * 1e3 / args.steps
     value = w.tokens / (wall / args.steps)
@@ -242,6 +287,7 @@ def main() -> int:
                          "newton_min": float(t_newt.min()), "step_event_mean": float(t_step.mean())},
         "newton_tokens_per_s": w.tokens / (newton_ms * 1e-3),
         "residuals": residuals,
+        "backward": backward,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

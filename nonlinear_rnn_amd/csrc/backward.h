@@ -24,14 +24,22 @@
 //                          product (C::vjp) gives dL/dx_t (stored), dL/da
 //                          (accumulated per lane) and mu_{t-1}; at a head,
 //                          mu_{t-1} is dL/dh0 of that segment.
-// dL/da is reduced over rows and chunks in a fixed order (k_bw_da_reduce), so
-// the whole backward is deterministic.
+// dL/da is reduced over rows and chunks in a fixed order (k_bw_da_reduce).
+//
+// The default schedule is the single-pass kernel k_bw_sp, the backward twin
+// of the forward's single-pass kernel: chunks are taken by ticket in reverse
+// time order, each workgroup composes its chunk's maps, obtains the gradient
+// entering it from the later chunks by the same decoupled look-back (chunk
+// records indexed in processing order), publishes what leaves it, and walks
+// its steps backwards; inputs cross HBM once and no scan pass is needed.
+// The three-phase kernels above remain as the PRN_ALGO=tp schedule.
 //
 // Work decomposition as in the forward kernels: lane = channel, wave w = the
 // w-th sub-chunk of LS steps of a chunk of LC = NW LS steps, walked serially.
 #pragma once
 
 #include "newton_kernels.h"
+#include "newton_sp.h"
 
 namespace prn {
 
@@ -254,6 +262,138 @@ k_bw_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
   for (int g = 0; g < G; ++g) dash[w][g][lane] = da[g];
   __syncthreads();
   if (w == 0 && ch < d_h) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s = dash[0][g][lane];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) s += dash[v][g][lane];
+      dap[((b * n_ch + chunk) * G + g) * d_h + ch] = s;
+    }
+  }
+}
+
+// Single-pass backward.  Ticket i takes chain i mod n_chains and processing
+// index r = i / n_chains, i.e. time chunk n_ch - 1 - r: a chunk only waits on
+// chunks later in time, which hold smaller tickets and have started.  Chunk
+// records (status, aggregate map, outgoing gradient) are indexed by r; the
+// look-back is the forward's (lookback_carry), so are its bounded waits.
+template <class C, int DT, int LS, int NW>
+__global__ void __launch_bounds__(kWave * NW)
+k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ states,
+        const typename Storage<DT>::T* __restrict__ h0, const int32_t* __restrict__ cu,
+        const float* __restrict__ a, const typename Storage<DT>::T* __restrict__ dH,
+        const typename Storage<DT>::T* __restrict__ dsl, int64_t T, int64_t d_h, int64_t n_seqs, int64_t n_ch,
+        int64_t n_tiles, int64_t n_chains, typename Storage<DT>::T* __restrict__ dxproj,
+        typename Storage<DT>::T* __restrict__ dh0, float* __restrict__ dap, SpRecords rec, unsigned spin_limit,
+        bool agg_first) {
+  using ST = Storage<DT>;
+  using Map = typename C::Map;
+  constexpr int G = C::G, S = C::S, LC = LS * NW;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  __shared__ Map part[NW][kWave];
+  __shared__ float carry_sh[S][kWave];
+  __shared__ float dash[NW][G][kWave];
+  __shared__ unsigned tk;
+
+  if (threadIdx.x == 0) tk = atomicAdd(rec.ticket, 1u);
+  __syncthreads();
+  const int64_t ticket = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(tk));
+  const int64_t n_wg = n_ch * n_chains;
+  const int64_t rchunk = ticket / n_chains, chain = ticket - rchunk * n_chains;
+  const int64_t chunk = n_ch - 1 - rchunk;
+  const int64_t b = chain / n_tiles, tile = chain - b * n_tiles;
+  const int64_t ch_l = tile * kWave + lane;
+  const bool ch_ok = ch_l < d_h;
+  const int64_t ch = ch_ok ? ch_l : d_h - 1;  // lanes past d_h shadow the last channel (stores masked)
+  const int64_t t0 = chunk * LC + static_cast<int64_t>(w) * LS;
+  const bool wact = ticket < n_wg && t0 < T;
+  const int n = wact ? static_cast<int>(imin(LS, T - t0)) : 0;
+
+  // walk A: this wave's map, kept with the steps' inputs for walk B
+  ChanCoef<C> cf;
+  cf.load(a, d_h, ch);
+  BwStep<C, DT> st[LS];
+  Map acc = Map::identity();
+  RevSegTracker rs;
+  if (wact) {
+    rs.init(cu, n_seqs, b, t0 + n - 1, T);
+#pragma unroll
+    for (int j = LS - 1; j >= 0; --j) {
+      if (j < n) {
+        const int64_t t = t0 + j;
+        rs.at(t);
+        st[j].load(xproj, states, h0, dH, dsl, b, t, T, d_h, ch, rs);
+        float fv[S];
+        const Map m = C::template fj<false>(st[j].xs, st[j].prev, cf.as, cf.a, false, fv);
+        acc = compose(bw_step_map(m, st[j].g, rs.last(t, T)), acc);
+      }
+    }
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+
+  // the gradient entering the chunk from later chunks: one wave looks back
+  const int64_t base = chain * n_ch;
+  if (w == NW - 1 && ticket < n_wg) {
+    Map tot = part[NW - 1][lane];
+#pragma unroll
+    for (int v = NW - 2; v >= 0; --v) tot = compose(part[v][lane], tot);
+    float cin[S];
+    lookback_carry<S>(rec, base, rchunk, tot, lane, spin_limit, agg_first, cin);
+#pragma unroll
+    for (int q = 0; q < S; ++q) carry_sh[q][lane] = cin[q];
+    // what leaves the chunk towards earlier ones goes out before the barrier,
+    // its status right after it
+    float outg[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) outg[q] = cin[q];
+    apply(tot, outg);
+#pragma unroll
+    for (int q = 0; q < S; ++q) rec_store(rec.pre + (base + rchunk) * S * kWave + q * kWave + lane, outg[q]);
+  }
+  __syncthreads();
+  if (w == NW - 1 && ticket < n_wg) rec_publish(rec.status + base + rchunk, kRecPrefix, lane);
+
+  // walk B from this wave's carry-in
+  float da[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) da[g] = 0.0f;
+  if (wact) {
+    float mu[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) mu[q] = carry_sh[q][lane];
+    for (int v = NW - 1; v > w; --v) apply(part[v][lane], mu);
+    rs.init(cu, n_seqs, b, t0 + n - 1, T);
+#pragma unroll
+    for (int j = LS - 1; j >= 0; --j) {
+      if (j < n) {
+        const int64_t t = t0 + j;
+        rs.at(t);
+        const bool cut = rs.last(t, T);
+        float lam[S];
+#pragma unroll
+        for (int q = 0; q < S; ++q) lam[q] = cut ? st[j].g[q] : st[j].g[q] + mu[q];
+        float dx[G], dac[G];
+        C::vjp(st[j].xs, st[j].prev, cf.as, cf.a, lam, dx, dac, mu);
+        if (ch_ok) {
+          typename ST::T* dp = dxproj + ((b * T + t) * G) * d_h + ch;
+#pragma unroll
+          for (int g = 0; g < G; ++g) dp[g * d_h] = ST::pack(dx[g]);
+          if (dh0 && rs.head(t)) {
+#pragma unroll
+            for (int q = 0; q < S; ++q) dh0[(rs.seg * S + q) * d_h + ch] = ST::pack(mu[q]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) da[g] += dac[g];
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) dash[w][g][lane] = da[g];
+  __syncthreads();
+  if (w == 0 && ch_ok && ticket < n_wg) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s = dash[0][g][lane];

@@ -160,7 +160,10 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
   }
 }
 
-template <class C, int DT, int LS, int NW>
+// WS: also write every state of the final trajectory to sout (the training
+// forward); a separate instance, so that the plain forward's registers are
+// not spent on it.
+template <class C, int DT, int LS, int NW, bool WS>
 __global__ void __launch_bounds__(kWave * NW)
 k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
@@ -213,7 +216,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   unsigned rmax = 0;
   const typename ST::T* xp = xproj + ((b * T + t0) * G) * d_h + ch;
   typename ST::T* hp = Hout + (b * T + t0) * d_h + ch;
-  typename ST::T* sp = sout ? sout + (b * T + t0) * S * d_h + ch : nullptr;
+  typename ST::T* sp = WS ? sout + (b * T + t0) * S * d_h + ch : nullptr;
 
   // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
   if (fast) {
@@ -338,7 +341,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           C::f(xj, pr, cf.as, cf.a, fv);
           if (ch_ok) {
             hp[j * d_h] = ST::pack(s[S - 1]);
-            if (sp) {
+            if constexpr (WS) {
 #pragma unroll
               for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
             }
@@ -380,7 +383,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             C::f(xj, p, cf.as, cf.a, fv);
             if (ch_ok) {
               hp[j * d_h] = ST::pack(s[S - 1]);
-              if (sp) {
+              if constexpr (WS) {
 #pragma unroll
                 for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
               }

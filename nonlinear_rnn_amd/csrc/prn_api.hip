@@ -121,19 +121,37 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
   return PRN_OK;
 }
 
-// backward geometry: the forward's three-phase chunks, walked in reverse
+// backward geometry: chunks of kLC steps (NW = 8 waves of 8 steps), walked
+// in reverse.  Single pass (default): status words, chunk records and the
+// da partials; three-phase (PRN_ALGO=tp): aggregates, carries, da partials.
 struct PlanBw {
-  int64_t n_ch;
-  size_t agg_off, carry_off, da_off, total;
+  bool sp;
+  int64_t n_ch, n_tiles, n_chains;
+  size_t words_off, n_words, agg_off, pre_off, carry_off, da_off, total;
 };
 
 PlanBw plan_bw(const prn_params* p, const Shape& sh) {
   PlanBw pl{};
+  pl.sp = !use_three_phase();
   pl.n_ch = (p->T + kLC - 1) / kLC;
+  pl.n_tiles = (p->d_h + 63) / 64;
+  pl.n_chains = p->B * pl.n_tiles;
+  const size_t NC = sh.S * sh.S + sh.S;
   const size_t units = size_t(p->B) * pl.n_ch * p->d_h;
-  pl.agg_off = 0;
-  pl.carry_off = align_up(units * (sh.S * sh.S + sh.S) * 4);
-  pl.da_off = pl.carry_off + align_up(units * sh.S * 4);
+  size_t off = 0;
+  if (pl.sp) {
+    const size_t nrec = size_t(pl.n_chains) * pl.n_ch;
+    pl.n_words = 2 + nrec;
+    pl.words_off = 0;
+    pl.agg_off = align_up(pl.n_words * 4);
+    pl.pre_off = pl.agg_off + align_up(nrec * NC * 64 * 4);
+    off = pl.pre_off + align_up(nrec * sh.S * 64 * 4);
+  } else {
+    pl.agg_off = 0;
+    pl.carry_off = align_up(units * NC * 4);
+    off = pl.carry_off + align_up(units * sh.S * 4);
+  }
+  pl.da_off = off;
   pl.total = pl.da_off + align_up(units * sh.G * 4);
   return pl;
 }
@@ -297,10 +315,15 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     prn::k_zero_u32<<<unsigned((pl.n_status + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_status));
     auto launch = [&](auto ls) {
       constexpr int LS = decltype(ls)::value;
-      prn::k_newton_sp<C, DT, LS, kSpNW><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
-          static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, K,
-          static_cast<T*>(Hout_v), slast, static_cast<T*>(p->states_out), rpart, rec, kSpinLimit,
-          pl.n_chains < kAggFirstBelowChains);
+      T* sout = static_cast<T*>(p->states_out);
+      if (sout)
+        prn::k_newton_sp<C, DT, LS, kSpNW, true><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+            static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains,
+            K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+      else
+        prn::k_newton_sp<C, DT, LS, kSpNW, false><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+            static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains,
+            K, static_cast<T*>(Hout_v), slast, nullptr, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
     };
     if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
@@ -363,17 +386,31 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
   T* dh0 = static_cast<T*>(dh0_v);
   if (p->T > 0) {
     char* ws = static_cast<char*>(p->workspace);
-    float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
-    float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
     float* dap = reinterpret_cast<float*>(ws + pl.da_off);
-    const dim3 grid(unsigned(pl.n_ch), unsigned((p->d_h + 63) / 64), unsigned(p->B));
-    const dim3 block(64 * kNW);
-    prn::k_bw_reduce<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
-                                                              p->n_seqs, pl.n_ch, agg);
-    prn::k_tp_scan<S, kScanSeg><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(p->B)), 64 * kScanSeg, 0, st>>>(
-        agg, carry, p->d_h, pl.n_ch);
-    prn::k_bw_fix<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
-                                                           p->n_seqs, pl.n_ch, carry, dxproj, dh0, dap);
+    if (pl.sp) {
+      prn::SpRecords rec;
+      unsigned* words = reinterpret_cast<unsigned*>(ws + pl.words_off);
+      rec.ticket = words;
+      rec.error = words + 1;
+      rec.status = words + 2;
+      rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
+      rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
+      prn::k_zero_u32<<<unsigned((pl.n_words + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_words));
+      prn::k_bw_sp<C, DT, kLS, kNW><<<unsigned(pl.n_ch * pl.n_chains), 64 * kNW, 0, st>>>(
+          xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, dxproj,
+          dh0, dap, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+    } else {
+      float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
+      float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
+      const dim3 grid(unsigned(pl.n_ch), unsigned((p->d_h + 63) / 64), unsigned(p->B));
+      const dim3 block(64 * kNW);
+      prn::k_bw_reduce<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
+                                                                p->n_seqs, pl.n_ch, agg);
+      prn::k_tp_scan<S, kScanSeg><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(p->B)), 64 * kScanSeg, 0, st>>>(
+          agg, carry, p->d_h, pl.n_ch);
+      prn::k_bw_fix<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
+                                                             p->n_seqs, pl.n_ch, carry, dxproj, dh0, dap);
+    }
     prn::k_bw_da_reduce<G><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(G)), 256, 0, st>>>(
         dap, p->B * pl.n_ch, p->d_h, da);
   } else {

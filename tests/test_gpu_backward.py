@@ -34,6 +34,14 @@ SMALL = [
 IDS = [w.name for w in SMALL]
 
 
+@pytest.fixture(params=["sp", "tp"])
+def algo(request, monkeypatch):
+    """Backward schedule: 'sp' single-pass look-back kernel (default), 'tp'
+    three-phase kernels.  The library reads PRN_ALGO at every call."""
+    monkeypatch.setenv("PRN_ALGO", request.param)
+    return request.param
+
+
 def rel_err(got, ref):
     return float(np.abs(got - ref).max() / (1.0 + np.abs(ref).max())) if ref.size else 0.0
 
@@ -117,8 +125,8 @@ def test_states_out_is_the_trajectory(w):
 
 
 @pytest.mark.parametrize("w", SMALL, ids=IDS)
-def test_backward_matches_oracle_adjoint(w):
-    say(f"[case] backward {w}")
+def test_backward_matches_oracle_adjoint(w, algo):
+    say(f"[case] backward {algo} {w}")
     inp = small_inputs(w)
     cu = inp["cu_seqlens"]
     rows = w.B if cu is None else w.n_seqs
@@ -128,7 +136,7 @@ def test_backward_matches_oracle_adjoint(w):
     dx, da, dh0 = gpu_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
     rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
     e_dx, e_da, e_dh0 = rel_err(to_f64(dx), rdx), rel_err(to_f64(da), rda), rel_err(to_f64(dh0), rdh0)
-    say(f"  {w.name}: dxproj {e_dx:.2e}  da {e_da:.2e}  dh0 {e_dh0:.2e}  (max|dxproj| {np.abs(rdx).max():.3g}, "
+    say(f"  {w.name} {algo}: dxproj {e_dx:.2e}  da {e_da:.2e}  dh0 {e_dh0:.2e}  (max|dxproj| {np.abs(rdx).max():.3g}, "
         f"max|da| {np.abs(rda).max():.3g})")
     t_x, t_a = tols(w)
     assert e_dx <= t_x and e_dh0 <= t_x and e_da <= t_a
@@ -150,7 +158,10 @@ def test_backward_optional_arguments(w):
     assert rel_err(to_f64(dx), rdx) <= tols(w)[0] and rel_err(to_f64(dh0), rdh0) <= tols(w)[0]
 
 
-def test_backward_is_deterministic():
+def test_backward_is_deterministic(algo):
+    """Both schedules fold the carries in a fixed order for the same look-back
+    outcome; the single-pass one can take a different (timing-dependent)
+    number of aggregates, so it is held to the fp32 tolerance instead."""
     w = SMALL[1]
     inp = small_inputs(w)
     xproj, H, states, last = gpu_forward_states(w, inp, w.K)
@@ -158,11 +169,14 @@ def test_backward_is_deterministic():
     r1 = gpu_backward(w, inp, xproj, states, dH, dsl=dsl)
     r2 = gpu_backward(w, inp, xproj, states, dH, dsl=dsl)
     for u, v in zip(r1, r2):
-        assert torch.equal(u, v)
+        if algo == "tp":
+            assert torch.equal(u, v)
+        else:
+            assert rel_err(to_f64(u), to_f64(v)) <= 1e-6
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_backward_edge_shapes(cell):
+def test_backward_edge_shapes(cell, algo):
     """T = 0 (da = 0, dh0 = dstate_last), T = 1, empty and one-step segments."""
     G, S = (3, 1) if cell == "gru" else (4, 2)
     d = 70
