@@ -121,11 +121,24 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
   return PRN_OK;
 }
 
-// backward geometry: chunks of kLC steps (NW = 8 waves of 8 steps), walked
-// in reverse.  Single pass (default): status words, chunk records and the
-// da partials; three-phase (PRN_ALGO=tp): aggregates, carries, da partials.
+// backward geometry.  Single pass (default): per-cell chunks, measured at
+// the long LSTM shape (LS x NW = 8 x 8: 0.95-0.98 ms, 8 x 4: 0.92, 12 x 4:
+// 0.98, 16 x 4: 0.92) and one 65536-step GRU row (8 x 8: 0.165 ms, 8 x 4:
+// 0.20, 16 x 4: 0.17, 16 x 8: 0.15); workspace: status words, chunk records
+// and the da partials.  Three-phase (PRN_ALGO=tp): chunks of kLC steps;
+// aggregates, carries, da partials.
+// As in the forward, long chunks pay off only with few chains: the bf16 GRU
+// at 16 x 16384 x 512 (128 chains) took 1.16 ms at 16 x 8 against 1.0 ms at
+// 8 x 8, so the GRU takes 16 x 8 below 64 chains and 8 x 8 above; the LSTM
+// takes 8 x 8 (1.035 ms on the long LSTM workload; 8 x 4: 1.048 ms).
+constexpr int kBwNW = 8, kBwLsFew = 16, kBwLs = 8;
+int bw_chunk(int cell, int64_t n_chains, bool sp) {
+  if (!sp) return kLC;
+  return (cell == PRN_CELL_DIAG_GRU && n_chains < kSpManyChains ? kBwLsFew : kBwLs) * kBwNW;
+}
 struct PlanBw {
   bool sp;
+  int lc;  // steps per chunk
   int64_t n_ch, n_tiles, n_chains;
   size_t words_off, n_words, agg_off, pre_off, carry_off, da_off, total;
 };
@@ -133,9 +146,10 @@ struct PlanBw {
 PlanBw plan_bw(const prn_params* p, const Shape& sh) {
   PlanBw pl{};
   pl.sp = !use_three_phase();
-  pl.n_ch = (p->T + kLC - 1) / kLC;
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
+  pl.lc = bw_chunk(p->cell, pl.n_chains, pl.sp);
+  pl.n_ch = (p->T + pl.lc - 1) / pl.lc;
   const size_t NC = sh.S * sh.S + sh.S;
   const size_t units = size_t(p->B) * pl.n_ch * p->d_h;
   size_t off = 0;
@@ -396,9 +410,20 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
       rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
       rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
       prn::k_zero_u32<<<unsigned((pl.n_words + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_words));
-      prn::k_bw_sp<C, DT, kLS, kNW><<<unsigned(pl.n_ch * pl.n_chains), 64 * kNW, 0, st>>>(
-          xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, dxproj,
-          dh0, dap, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+      auto launch = [&](auto ls) {
+        constexpr int LS = decltype(ls)::value;
+        prn::k_bw_sp<C, DT, LS, kBwNW><<<unsigned(pl.n_ch * pl.n_chains), 64 * kBwNW, 0, st>>>(
+            xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, dxproj,
+            dh0, dap, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+      };
+      if constexpr (S == 1) {
+        if (pl.lc == kBwLsFew * kBwNW)
+          launch(std::integral_constant<int, kBwLsFew>{});
+        else
+          launch(std::integral_constant<int, kBwLs>{});
+      } else {
+        launch(std::integral_constant<int, kBwLs>{});
+      }
     } else {
       float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
       float* carry = reinterpret_cast<float*>(ws + pl.carry_off);

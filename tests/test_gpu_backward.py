@@ -153,7 +153,9 @@ def test_backward_optional_arguments(w):
     dx, da, _ = gpu_backward(w, inp, xproj, states, dH, want_dh0=False)
     dx2, da2, dh0 = gpu_backward(w, inp, xproj, states, dH, dsl=torch.zeros((rows, w.S, w.d_h),
                                  dtype=TORCH_DT[w.dtype], device="cuda"))
-    assert torch.equal(dx, dx2) and torch.equal(da, da2)
+    # the single-pass schedule folds a timing-dependent number of aggregates
+    # into each carry: runs agree to rounding, not bitwise
+    assert rel_err(to_f64(dx), to_f64(dx2)) <= 1e-6 and rel_err(to_f64(da), to_f64(da2)) <= 1e-6
     rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH)
     assert rel_err(to_f64(dx), rdx) <= tols(w)[0] and rel_err(to_f64(dh0), rdh0) <= tols(w)[0]
 
