@@ -243,7 +243,7 @@ def main() -> int:
                     "roofline": {"bound": "hbm", "achieved": bw_bytes / (bw_ms * 1e-3) / 1e9,
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": bw_bytes / (bw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                 "traffic": None, "algorithmic_bytes": bw_bytes}}
+                                 "traffic": profiled_traffic("k_bw_sp", w.name), "algorithmic_bytes": bw_bytes}}
         print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
     residuals = res.cpu().tolist()
