@@ -116,10 +116,16 @@ def gate_residual(residuals, dtype, residual_fail=RESIDUAL_FAIL, residual_warn=N
 def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_table=None,
                    residual_fail=RESIDUAL_FAIL, residual_warn=None, gate=True, return_state=False):
     """Parallel Newton forward.  Returns (H (B,T,d_h), residuals [r_0..r_K] on
-    the host[, final states]).  K may be None with a k_table."""
+    the host[, final states]).  K may be None: then it comes from k_table, or
+    from the cell's measured K*(T) table (nonlinear_rnn_amd/kstar_table.json)."""
     xproj = xproj.contiguous()
     a = a.to(torch.float32).contiguous()
     Bn, T, _, d_h = xproj.shape
+    if K is None and k_table is None:
+        # max_iters=None: the measured K*(T) envelope of this cell (FAQs,
+        # "How many Newton iterations should I use?")
+        from .kstar import load_table
+        k_table = load_table(cell)
     if k_table is not None and K is None:
         K = resolve_k(T, k_table)
     if K is None or int(K) < 1:

@@ -162,3 +162,14 @@ def test_backward_workspace_bytes():
     assert B.prn_backward_workspace_bytes("gru", torch.float32, 2, 1000, 64) < w
     p = _params(d_h=0)
     assert B.lib().prn_backward_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_committed_kstar_table_is_well_formed():
+    """The measured K*(T) tables: both cells, positive K, monotone in T, and
+    resolvable for any T (no GPU needed to read them)."""
+    from nonlinear_rnn_amd import kstar as gk
+    for cell in ("gru", "lstm"):
+        tab = gk.load_table(cell)
+        ks = [tab[T] for T in sorted(tab)]
+        assert ks and all(k >= 1 for k in ks) and ks == sorted(ks)
+        assert prn.resolve_k(1, tab) == ks[0] and prn.resolve_k(10 ** 7, tab) == ks[-1]
