@@ -154,8 +154,15 @@ def residual(cell, H, xp, a, heads, H0) -> float:
 
 
 def newton(cell, xp, a, K, h0=None, cu_seqlens=None, dtype="f64", jacobian=True,
-           keep_iterates=False):
-    """K Newton iterations from H^(0) = 0.
+           keep_iterates=False, picard=0):
+    """K Newton iterations from H^(0) = 0, or from P = picard Picard sweeps.
+
+    Picard warm-start (FAQs, "How many Newton iterations should I use?":
+    try picard_iters before raising the iteration budget).  Reading: a sweep
+    is the Jacobi step H <- f(shift(H), x) over all steps at once (the
+    previous step's value of the current guess, h0 at a head), stored in the
+    storage dtype; P sweeps from 0 give the guess the Newton iterations
+    start from, and r_0 is the residual of that guess.
 
     xp (B,T,G,d) float64 (already the stored projection, upcast), a (G,d).
     dtype: storage dtype of the iterates ('f64', 'f32', 'bf16').
@@ -172,6 +179,8 @@ def newton(cell, xp, a, K, h0=None, cu_seqlens=None, dtype="f64", jacobian=True,
     H0 = initial_states(B, S, d, cu_seqlens, h0)
     head_mask = heads >= 0
     H = np.zeros((B, T, S, d))
+    for _p in range(picard):
+        H = store(f(previous_states(H, heads, H0), xp, a), dtype)
     res = []
     iterates = []
     for _k in range(K):

@@ -202,3 +202,30 @@ def test_workload_generator_shapes_and_determinism():
     assert L.sum() == 65536 and L.min() > 0
     st = random_state(WORKLOADS["lstm_t131k"], 3, seed=1)
     assert st.shape == (3, 2, 256)
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_picard_warm_start(cell):
+    """P Jacobi sweeps from 0 are exact on the first P steps; k Newton
+    iterations from that guess are exact on the first P + k steps; P = T
+    sweeps alone are the unroll; and r_0 is the residual of the guess."""
+    from oracle import newton as on
+    rng = np.random.default_rng(17)
+    G = 3 if cell == "gru" else 4
+    S = 1 if cell == "gru" else 2
+    B, T, d = 2, 12, 3
+    xp = rng.standard_normal((B, T, G, d))
+    a = rng.uniform(-0.5, 0.5, (G, d))
+    h0 = rng.standard_normal((B, S, d)) * 0.3
+    seq, _ = on.sequential(cell, xp, a, h0=h0)
+    for P in (1, 2, 3):
+        out = on.newton(cell, xp, a, 2, h0=h0, picard=P, keep_iterates=True)
+        for k, Hk in enumerate(out["iterates"], start=1):
+            assert np.abs(Hk[:, :P + k] - seq[:, :P + k]).max() <= 1e-13
+    full = on.newton(cell, xp, a, 1, h0=h0, picard=T)
+    assert np.abs(full["H"] - seq).max() <= 1e-13 and full["residuals"][0] <= 1e-13
+    g1 = on.newton(cell, xp, a, 1, h0=h0, picard=1)
+    _, _, f, _ = cells.cell_fns(cell)
+    guess = f(np.concatenate([h0[:, None], np.zeros((B, T - 1, S, d))], axis=1), xp, a)  # one sweep from 0
+    heads = on.head_segments(B, T)
+    assert g1["residuals"][0] == on.residual(cell, guess, xp, a, heads, h0)
