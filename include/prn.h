@@ -85,6 +85,11 @@ typedef struct {
                               every state s_t of the returned trajectory (LSTM (c, h);
                               for the GRU it equals H_out).  The backward pass takes it as
                               its trajectory                                                */
+  int32_t picard_iters;    /* prn_newton_forward: Picard (Jacobi) sweeps H <- f(shift(H), x)
+                              from 0 before the K Newton iterations (FAQs "How many Newton
+                              iterations should I use?": picard_iters); 0 or 1 (more:
+                              PRN_ERR_UNSUPPORTED, as with PRN_ALGO=tp); r_0 is then the
+                              residual of the Picard guess                                  */
 } prn_params;
 
 /* Input projection, once per forward:

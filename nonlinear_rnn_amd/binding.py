@@ -52,6 +52,7 @@ class prn_params(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("states_out", ctypes.c_void_p),
+        ("picard_iters", ctypes.c_int32),
     ]
 
 
@@ -121,7 +122,8 @@ def _stream(stream) -> int:
 
 
 def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in: int = 0, n_seqs: int = 0,
-                a=None, state_last_out=None, states_out=None, workspace=None, stream=None) -> prn_params:
+                a=None, state_last_out=None, states_out=None, workspace=None, stream=None,
+                picard_iters: int = 0) -> prn_params:
     if cell not in CELLS:
         raise ValueError(f"unknown cell {cell!r}")
     if dtype not in DTYPES:
@@ -132,14 +134,16 @@ def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in
     p.a = _ptr(a)
     p.state_last_out = _ptr(state_last_out)
     p.states_out = _ptr(states_out)
+    p.picard_iters = int(picard_iters)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.stream = _stream(stream) if torch.cuda.is_available() else 0
     return p
 
 
-def prn_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, K: int, n_seqs: int = 0) -> int:
-    p = make_params(cell, dtype, B, T, d_h, n_seqs=n_seqs)
+def prn_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, K: int, n_seqs: int = 0,
+                        picard_iters: int = 0) -> int:
+    p = make_params(cell, dtype, B, T, d_h, n_seqs=n_seqs, picard_iters=picard_iters)
     n = int(lib().prn_workspace_bytes(ctypes.byref(p), K))
     if n == 0 and prn_last_error():
         raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
@@ -197,14 +201,15 @@ def _states_out(states_out, xproj, cell):
 
 
 def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None, residual_out=None,
-                       state_last_out=None, states_out=None, workspace=None, stream=None) -> None:
+                       state_last_out=None, states_out=None, workspace=None, stream=None,
+                       picard_iters: int = 0) -> None:
     B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
     _states_out(states_out, xproj, cell)
     _dev(residual_out, "residual_out", torch.float32)
     if residual_out is not None and residual_out.numel() < K + 1:
         raise ValueError("residual_out needs K + 1 entries")
     p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
-                    states_out=states_out, workspace=workspace, stream=stream)
+                    states_out=states_out, workspace=workspace, stream=stream, picard_iters=picard_iters)
     _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
                                     _ptr(H_out), _ptr(residual_out)))
 

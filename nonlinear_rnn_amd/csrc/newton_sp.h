@@ -162,8 +162,11 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 
 // WS: also write every state of the final trajectory to sout (the training
 // forward); a separate instance, so that the plain forward's registers are
-// not spent on it.
-template <class C, int DT, int LS, int NW, bool WS>
+// not spent on it.  PIC: one Picard sweep before the Newton iterations, so
+// iteration 1 linearises at H^(1)_{t-1} = f(0 (h0 at a head), x_{t-1})
+// rather than at 0; it needs the projected inputs of one step before each
+// wave's sub-chunk, and r_0 is the residual of H^(1).
+template <class C, int DT, int LS, int NW, bool WS, bool PIC>
 __global__ void __launch_bounds__(kWave * NW)
 k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
@@ -218,27 +221,61 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   typename ST::T* hp = Hout + (b * T + t0) * d_h + ch;
   typename ST::T* sp = WS ? sout + (b * T + t0) * S * d_h + ch : nullptr;
 
-  // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads) ----
+  // the Picard guess H^(1) of the step before t0 (PIC; t0 not a head): a
+  // sweep from 0, or from h0 where that step is its segment's head
+  auto picard_before = [&](float* pm) {
+    float xm[G], p0[S];
+    load_xs<C, DT>(xp - G * d_h, d_h, xm);
+#pragma unroll
+    for (int q = 0; q < S; ++q) p0[q] = 0.0f;
+    if (h0 && sg.start == t0 - 1) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, p0);
+    C::f(xm, p0, cf.as, cf.a, pm);
+#pragma unroll
+    for (int q = 0; q < S; ++q) pm[q] = ST::round(pm[q]);
+  };
+
+  // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads), or
+  // at the Picard guess H^(1) ----
   if (fast) {
     float xs[LS][G];
 #pragma unroll
     for (int j = 0; j < LS; ++j) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    float pm[S];
+    if constexpr (PIC) picard_before(pm);
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       xs_put(j, xs[j]);
       float prev[S], fv[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+      for (int q = 0; q < S; ++q) prev[q] = PIC ? pm[q] : 0.0f;
       ms[j] = C::template fj<false>(xs[j], prev, cf.as, cf.a, false, fv);
       acc = compose(ms[j], acc);
+      if constexpr (PIC) {
+        float z[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
+        for (int q = 0; q < S; ++q) z[q] = 0.0f;
+        C::f(xs[j], z, cf.as, cf.a, pm);
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          pm[q] = ST::round(pm[q]);
+          rmax = rmax_bits(rmax, pm[q] - fv[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
+      }
     }
   } else if (wact) {
     float xs[LS][G];
 #pragma unroll
     for (int j = 0; j < LS; ++j)
       if (j < n) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    float pm[S];
+    if constexpr (PIC) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) pm[q] = 0.0f;
+      if (t0 != 0 && sg.start != t0) picard_before(pm);
+    }
     SegTracker st = sg;
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
@@ -247,12 +284,34 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         const bool head = st.at(t0 + j);
         float prev[S], fv[S];
 #pragma unroll
-        for (int q = 0; q < S; ++q) prev[q] = 0.0f;
-        if (head && h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, prev);
+        for (int q = 0; q < S; ++q) prev[q] = PIC ? pm[q] : 0.0f;
+        if (head) {
+#pragma unroll
+          for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+          if (h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, prev);
+        }
         ms[j] = C::fj(xs[j], prev, cf.as, cf.a, head, fv);
         acc = compose(ms[j], acc);
+        if constexpr (PIC) {
+          // H^(1)_t: f(h0, x_t) = fv at a head, f(0, x_t) elsewhere
+          if (head) {
 #pragma unroll
-        for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
+            for (int q = 0; q < S; ++q) pm[q] = fv[q];
+          } else {
+            float z[S];
+#pragma unroll
+            for (int q = 0; q < S; ++q) z[q] = 0.0f;
+            C::f(xs[j], z, cf.as, cf.a, pm);
+          }
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            pm[q] = ST::round(pm[q]);
+            rmax = rmax_bits(rmax, pm[q] - fv[q]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
+        }
       }
     }
   }

@@ -53,11 +53,15 @@ constexpr int kScanSeg = 16;
 // keeps LS = 8 to stay within 256, and the bf16 GRU with many chains keeps
 // LS = 8 so that three workgroups still fit a CU (measured at 16 x 16384 x
 // 512: LS = 12 took 1.31 ms against 1.20 ms).
+// With a Picard sweep the fp32 LSTM at LS = 12 needs 258 registers (one wave
+// per SIMD); it takes LS = 10.
 constexpr int kSpNW = 4;
-constexpr int kSpLsLstm = 12, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12, kSpLsGruManyBf16 = 8;
+constexpr int kSpLsLstm = 12, kSpLsLstmPicard = 10, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12,
+              kSpLsGruManyBf16 = 8;
 constexpr int64_t kSpManyChains = 64;
-int sp_ls(int cell, int dtype, int64_t n_chains) {
-  if (cell != PRN_CELL_DIAG_GRU) return dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm;
+int sp_ls(int cell, int dtype, int64_t n_chains, int picard) {
+  if (cell != PRN_CELL_DIAG_GRU)
+    return dtype == PRN_BF16 ? kSpLsLstmBf16 : (picard > 0 ? kSpLsLstmPicard : kSpLsLstm);
   if (n_chains < kSpManyChains) return kSpLsGruFew;
   return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
 }
@@ -208,7 +212,7 @@ PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
   PlanSp pl{};
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
-  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains);
+  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains, p->picard_iters);
   const int lc = pl.ls * kSpNW;
   pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_wg = pl.n_ch * pl.n_chains;
@@ -330,18 +334,26 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     auto launch = [&](auto ls) {
       constexpr int LS = decltype(ls)::value;
       T* sout = static_cast<T*>(p->states_out);
-      if (sout)
-        prn::k_newton_sp<C, DT, LS, kSpNW, true><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
-            static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains,
-            K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
-      else
-        prn::k_newton_sp<C, DT, LS, kSpNW, false><<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
-            static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains,
-            K, static_cast<T*>(Hout_v), slast, nullptr, rpart, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+      auto go = [&](auto ws, auto pic) {
+        prn::k_newton_sp<C, DT, LS, kSpNW, decltype(ws)::value, decltype(pic)::value>
+            <<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+                static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles,
+                pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, kSpinLimit,
+                pl.n_chains < kAggFirstBelowChains);
+      };
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      if (p->picard_iters > 0) {
+        if (sout) go(T_{}, T_{}); else go(F_{}, T_{});
+      } else {
+        if (sout) go(T_{}, F_{}); else go(F_{}, F_{});
+      }
     };
     if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
         launch(std::integral_constant<int, kSpLsLstmBf16>{});
+      else if (pl.ls == kSpLsLstmPicard)
+        launch(std::integral_constant<int, kSpLsLstmPicard>{});
       else
         launch(std::integral_constant<int, kSpLsLstm>{});
     } else {
@@ -533,6 +545,11 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void
   prn_status s = check_common(p, &sh);
   if (s != PRN_OK) return s;
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+  if (p->picard_iters < 0) return fail(PRN_ERR_INVALID_ARG, "picard_iters must be >= 0");
+  if (p->picard_iters > 1)
+    return fail(PRN_ERR_UNSUPPORTED, "picard_iters = %d: one Picard sweep is supported", p->picard_iters);
+  if (p->picard_iters > 0 && use_three_phase())
+    return fail(PRN_ERR_UNSUPPORTED, "Picard warm-start runs in the single-pass schedule only (PRN_ALGO=tp)");
   if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
   if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
   const size_t need = workspace_needed(p, sh, K);

@@ -73,6 +73,8 @@ FAKE = 1 << 20   # an aligned non-null address; never dereferenced (validation f
     (dict(a=FAKE), 3, B.PRN_ERR_WORKSPACE),                          # no workspace given
     (dict(a=FAKE, workspace=FAKE, workspace_bytes=16), 3, B.PRN_ERR_WORKSPACE),
     (dict(a=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),                    # misaligned
+    (dict(a=FAKE, picard_iters=-1), 3, B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE, picard_iters=2), 3, B.PRN_ERR_UNSUPPORTED),
 ])
 def test_newton_forward_rejects_bad_arguments_before_launch(kw, K, status):
     p = _params(**kw)
