@@ -177,3 +177,89 @@ def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol
     if raise_on_fail and not rep.ok:
         raise AgreementError(f"Newton vs sequential max_abs {m:.3e} > tau {atol:.1e}: {rep.to_dict()}")
     return rep
+
+
+# ------------------------------------------------------------------ training surface ---
+# The train-mode forward + backward of one diagonal layer (FAQs, "train() vs
+# eval()"; shapes/layout page, the train forward+backward surface): the
+# Newton forward keeps its trajectory (states_out) and the backward is
+# prn_newton_backward at that trajectory.  The projection's own gradients
+# are plain matrix products of dL/dxproj, left to torch's BLAS.
+
+class _NewtonFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, xproj, a, h0, cell, K, cu, picard_iters, residual_fail, gate):
+        Bn, T, G, d_h = xproj.shape
+        S = B_.STATE[cell]
+        n_seqs = 0 if cu is None else cu.numel() - 1
+        H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
+        states = torch.empty((Bn, T, S, d_h), dtype=xproj.dtype, device=xproj.device)
+        res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
+        n = B_.prn_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, K, n_seqs=n_seqs, picard_iters=picard_iters)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
+        B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=h0, cu_seqlens=cu, residual_out=res,
+                              states_out=states, workspace=ws, picard_iters=picard_iters)
+        ctx.residuals = res.cpu().tolist()
+        if gate:
+            gate_residual(ctx.residuals, xproj.dtype, residual_fail)
+        ctx.cell, ctx.cu = cell, cu
+        ctx.save_for_backward(xproj, a, h0 if h0 is not None else torch.empty(0), states)
+        ctx.has_h0 = h0 is not None
+        return H
+
+    @staticmethod
+    def backward(ctx, dH):
+        xproj, a, h0, states = ctx.saved_tensors
+        h0 = h0 if ctx.has_h0 else None
+        cell, cu = ctx.cell, ctx.cu
+        Bn, T, G, d_h = xproj.shape
+        n_seqs = 0 if cu is None else cu.numel() - 1
+        rows = Bn if cu is None else n_seqs
+        dxproj = torch.empty_like(xproj)
+        da = torch.empty((G, d_h), dtype=torch.float32, device=xproj.device)
+        dh0 = (torch.empty((rows, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
+               if ctx.needs_input_grad[2] else None)
+        n = B_.prn_backward_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, n_seqs=n_seqs)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
+        B_.prn_newton_backward(xproj, a, states, dH.to(xproj.dtype).contiguous(), dxproj, da, cell=cell, h0=h0,
+                               cu_seqlens=cu, dh0_out=dh0, workspace=ws)
+        return dxproj, da, dh0, None, None, None, None, None, None
+
+
+def newton_apply(xproj, a, K=None, *, cell: str, h0=None, cu_seqlens=None, picard_iters: int = 0,
+                 residual_fail=RESIDUAL_FAIL, gate=True):
+    """Differentiable Newton forward: H (B,T,d_h); gradients reach xproj, a
+    and h0 through the backward pass.  K = None resolves the measured K*(T)."""
+    xproj = xproj.contiguous()
+    Bn, T, _, _ = xproj.shape
+    if K is None:
+        from .kstar import load_table
+        K = resolve_k(T, load_table(cell))
+    cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
+    return _NewtonFunction.apply(xproj, a.contiguous(), _contig(h0), cell, int(K), cu, int(picard_iters),
+                                 residual_fail, gate)
+
+
+class _ProjFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, W, bias, cell):
+        ctx.save_for_backward(x, W)
+        ctx.has_bias = bias is not None
+        return input_proj(x, W, bias, cell=cell)
+
+    @staticmethod
+    def backward(ctx, dxp):
+        x, W = ctx.saved_tensors
+        Bn, T, G, d_h = dxp.shape
+        g = dxp.reshape(Bn * T, G * d_h).float()
+        dx = (g @ W.float()).reshape(x.shape).to(x.dtype)
+        dW = (g.t() @ x.reshape(Bn * T, -1).float()).to(W.dtype)
+        dbias = g.sum(0) if ctx.has_bias else None
+        return dx, dW, dbias, None
+
+
+def input_proj_apply(x, W, bias=None, *, cell: str):
+    """Differentiable projection: xproj = x W^T + bias on the matrix cores,
+    gradients by plain matrix products."""
+    return _ProjFunction.apply(x.contiguous(), W.contiguous(),
+                               None if bias is None else bias.to(torch.float32).contiguous(), cell)
