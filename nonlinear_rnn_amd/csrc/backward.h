@@ -404,6 +404,26 @@ k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storag
   }
 }
 
+// First level of the dL/da reduction: slice z of the units (per = units per
+// slice) summed for every (gate, channel) in a fixed order; out is
+// (n_slices, G, d_h).  k_bw_da_reduce then sums the slices.
+template <int G>
+__global__ void __launch_bounds__(256) k_bw_da_partial(const float* __restrict__ dap, int64_t n_units, int64_t per,
+                                                       int64_t d_h, float* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1), y = threadIdx.x / kWave;
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+  const int g = blockIdx.y;
+  const int64_t z = blockIdx.z, u0 = z * per, u1 = imin(n_units, u0 + per);
+  __shared__ float sh[4][kWave];
+  float s = 0.0f;
+  if (ch < d_h) {
+    for (int64_t u = u0 + y; u < u1; u += 4) s += dap[(u * G + g) * d_h + ch];
+  }
+  sh[y][lane] = s;
+  __syncthreads();
+  if (y == 0 && ch < d_h) out[(z * G + g) * d_h + ch] = ((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane];
+}
+
 // dL/da = sum of the n_units per-chunk partials (units = B * n_ch), for every
 // (gate, channel): 4 waves take every 4th unit in order, then add in order.
 template <int G>

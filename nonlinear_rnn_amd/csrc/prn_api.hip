@@ -140,11 +140,16 @@ int bw_chunk(int cell, int64_t n_chains, bool sp) {
   if (!sp) return kLC;
   return (cell == PRN_CELL_DIAG_GRU && n_chains < kSpManyChains ? kBwLsFew : kBwLs) * kBwNW;
 }
+// dL/da is reduced from per-chunk partials in two fixed-order levels: up to
+// kDaSlices slices of chunks, then the slices (one level with only
+// G x d_h/64 workgroups took 70 us at the long LSTM shape).
+constexpr int64_t kDaSlices = 64;
+
 struct PlanBw {
   bool sp;
   int lc;  // steps per chunk
   int64_t n_ch, n_tiles, n_chains;
-  size_t words_off, n_words, agg_off, pre_off, carry_off, da_off, total;
+  size_t words_off, n_words, agg_off, pre_off, carry_off, da_off, dslice_off, total;
 };
 
 PlanBw plan_bw(const prn_params* p, const Shape& sh) {
@@ -170,7 +175,8 @@ PlanBw plan_bw(const prn_params* p, const Shape& sh) {
     off = pl.carry_off + align_up(units * sh.S * 4);
   }
   pl.da_off = off;
-  pl.total = pl.da_off + align_up(units * sh.G * 4);
+  pl.dslice_off = pl.da_off + align_up(units * sh.G * 4);
+  pl.total = pl.dslice_off + align_up(size_t(kDaSlices) * sh.G * p->d_h * 4);
   return pl;
 }
 
@@ -448,8 +454,14 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
       prn::k_bw_fix<C, DT, kLS, kNW><<<grid, block, 0, st>>>(xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h,
                                                              p->n_seqs, pl.n_ch, carry, dxproj, dh0, dap);
     }
+    float* dsl_part = reinterpret_cast<float*>(ws + pl.dslice_off);
+    const int64_t n_units = p->B * pl.n_ch;
+    const int64_t per = (n_units + kDaSlices - 1) / kDaSlices;
+    const int64_t n_slices = (n_units + per - 1) / per;
+    prn::k_bw_da_partial<G><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(G), unsigned(n_slices)), 256, 0, st>>>(
+        dap, n_units, per, p->d_h, dsl_part);
     prn::k_bw_da_reduce<G><<<dim3(unsigned((p->d_h + 63) / 64), unsigned(G)), 256, 0, st>>>(
-        dap, p->B * pl.n_ch, p->d_h, da);
+        dsl_part, n_slices, p->d_h, da);
   } else {
     prn::k_zero_f32<<<unsigned((G * p->d_h + 255) / 256), 256, 0, st>>>(da, G * p->d_h);
     if (dh0 && !sh.ragged) {
