@@ -181,6 +181,27 @@ prn_status prn_newton_backward(const void* xproj, const prn_params* params, cons
  * invalid params; see prn_last_error). */
 size_t prn_backward_workspace_bytes(const prn_params* params);
 
+/* One T = 1 step for B independent slots: the serving decode step (FAQs,
+ * "How do I pass recurrent state between decode steps?": a fixed-size carry
+ * (slots, d_h) per layer; prefill with the sequential or Newton forward, then
+ * decode_wx + decode_step for each T = 1 token; "train() vs eval()": T = 1
+ * decode).  The token's projection and the cell step are fused:
+ *   xproj_g = x W_g^T + bias_g (fp32 sums, rounded to the storage dtype as
+ *             prn_input_proj's output is), s' = f(state_in, xproj).
+ *   x          (B, d_in) storage dtype, 16-byte aligned; d_in % 4 == 0 (fp32) or
+ *              % 8 == 0 (bf16), else PRN_ERR_UNSUPPORTED
+ *   W, bias    as for prn_input_proj
+ *   state_in   (B, S, d_h) storage dtype, the carry, or NULL for zeros
+ *   state_out  (B, S, d_h) storage dtype: the new carry; must not alias state_in
+ *              (callers ping-pong two buffers)
+ *   h_out      (B, d_h) storage dtype, or NULL
+ * params: cell, dtype, B = slots, T = 1, d_in, d_h, a, stream.  One kernel
+ * launch, no workspace, no memory set: it can be captured in a HIP graph with
+ * its buffers pinned.  The result equals prn_input_proj + prn_sequential_forward
+ * on the same token up to the summation order of the projection. */
+prn_status prn_decode_step(const void* x, const void* W, const float* bias, const prn_params* params,
+                           const void* state_in, void* state_out, void* h_out);
+
 /* Host-side check of ragged offsets (the validate_cu_seqlens contract of
  * the shapes/layout page): cu_host has n_seqs + 1 entries, cu[0] = 0,
  * non-decreasing, cu[n_seqs] = N.  cu_host is a HOST pointer. */

@@ -27,8 +27,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # every symbol include/prn.h declares
 EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_workspace_bytes",
-           "prn_newton_backward", "prn_backward_workspace_bytes", "prn_validate_cu_seqlens", "prn_last_error",
-           "prn_version")
+           "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_validate_cu_seqlens",
+           "prn_last_error", "prn_version")
 
 
 class PrnError(RuntimeError):
@@ -76,12 +76,13 @@ def lib() -> ctypes.CDLL:
         L.prn_workspace_bytes.restype = ctypes.c_size_t
         L.prn_newton_backward.argtypes = [vp, P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.prn_backward_workspace_bytes.argtypes = [P]
+        L.prn_decode_step.argtypes = [vp, vp, vp, P, vp, vp, vp]
         L.prn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
         for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_newton_backward",
-                     "prn_validate_cu_seqlens"):
+                     "prn_decode_step", "prn_validate_cu_seqlens"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -260,3 +261,27 @@ def prn_newton_backward(xproj, a, states, dH, dxproj_out, da_out, *, cell: str, 
     p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, workspace=workspace, stream=stream)
     _check(lib().prn_newton_backward(_ptr(xproj), ctypes.byref(p), _ptr(h0), _ptr(cu_seqlens), _ptr(states),
                                      _ptr(dH), _ptr(dstate_last), _ptr(dxproj_out), _ptr(da_out), _ptr(dh0_out)))
+
+
+def prn_decode_step(x, W, bias, a, state_out, *, cell: str, state_in=None, h_out=None, stream=None) -> None:
+    """One T = 1 step for B slots: x (B, d_in), W (G*d_h, d_in), bias (G*d_h) fp32 or None,
+    state_in / state_out (B, S, d_h) (distinct buffers), h_out (B, d_h) or None."""
+    _dev(x, "x")
+    _dev(W, "W", x.dtype)
+    _dev(bias, "bias", torch.float32)
+    _dev(a, "a", torch.float32)
+    _dev(state_out, "state_out", x.dtype)
+    _dev(state_in, "state_in", x.dtype)
+    _dev(h_out, "h_out", x.dtype)
+    Bn, d_in = x.shape
+    G, S = GATES[cell], STATE[cell]
+    d_h = W.shape[0] // G
+    if W.shape != (G * d_h, d_in) or a.shape != (G, d_h) or state_out.shape != (Bn, S, d_h):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} W {tuple(W.shape)} state_out {tuple(state_out.shape)}")
+    if state_in is not None and state_in.shape != (Bn, S, d_h):
+        raise ValueError("state_in must match state_out")
+    if h_out is not None and h_out.shape != (Bn, d_h):
+        raise ValueError("h_out must be (B, d_h)")
+    p = make_params(cell, x.dtype, Bn, 1, d_h, d_in=d_in, a=a, stream=stream)
+    _check(lib().prn_decode_step(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(state_in), _ptr(state_out),
+                                 _ptr(h_out)))

@@ -13,6 +13,7 @@
 #include <type_traits>
 
 #include "backward.h"
+#include "decode.h"
 #include "newton_kernels.h"
 #include "newton_sp.h"
 #include "proj.h"
@@ -479,6 +480,42 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
 }  // namespace
 
 extern "C" {
+
+prn_status prn_decode_step(const void* x, const void* W, const float* bias, const prn_params* p,
+                           const void* state_in, void* state_out, void* h_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (p->T != 1) return fail(PRN_ERR_INVALID_ARG, "a decode step has T = 1, got T=%lld", (long long)p->T);
+  if (sh.ragged) return fail(PRN_ERR_INVALID_ARG, "a decode step takes slots (B), not a ragged pack");
+  if (p->d_in < 1) return fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
+  if (!x || !W || !p->a || !state_out) return fail(PRN_ERR_INVALID_ARG, "x, W, a or state_out is NULL");
+  const int vec = p->dtype == PRN_F32 ? 4 : 8;
+  if (p->d_in % vec != 0)
+    return fail(PRN_ERR_UNSUPPORTED, "decode step needs d_in %% %d == 0 for this storage dtype", vec);
+  if (misaligned(x, 16) || misaligned(W, 16) || misaligned(bias, 4) || misaligned(p->a, 4) ||
+      misaligned(state_in, sh.elt) || misaligned(state_out, sh.elt) || misaligned(h_out, sh.elt))
+    return fail(PRN_ERR_INVALID_ARG, "x and W must be 16-byte aligned, the rest to their element size");
+  if (state_in && state_in == state_out) return fail(PRN_ERR_INVALID_ARG, "state_in and state_out alias");
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const dim3 grid(unsigned((p->d_h + 63) / 64), unsigned(p->B));
+  auto go = [&](auto cell, auto dt) {
+    using C = decltype(cell);
+    constexpr int DT = decltype(dt)::value;
+    using T = typename prn::Storage<DT>::T;
+    prn::k_decode<C, DT><<<grid, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(W), bias, p->a,
+                                               p->d_in, p->d_h, static_cast<const T*>(state_in),
+                                               static_cast<T*>(state_out), static_cast<T*>(h_out));
+  };
+  using F32 = std::integral_constant<int, prn::kF32>;
+  using BF16 = std::integral_constant<int, prn::kBF16>;
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32) go(prn::CellGRU{}, F32{}); else go(prn::CellGRU{}, BF16{});
+  } else {
+    if (p->dtype == PRN_F32) go(prn::CellLSTM{}, F32{}); else go(prn::CellLSTM{}, BF16{});
+  }
+  return launched("prn_decode_step");
+}
 
 size_t prn_backward_workspace_bytes(const prn_params* p) {
   Shape sh;

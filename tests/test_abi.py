@@ -175,3 +175,24 @@ def test_committed_kstar_table_is_well_formed():
         ks = [tab[T] for T in sorted(tab)]
         assert ks and all(k >= 1 for k in ks) and ks == sorted(ks)
         assert prn.resolve_k(1, tab) == ks[0] and prn.resolve_k(10 ** 7, tab) == ks[-1]
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(T=100, a=FAKE), {}, B.PRN_ERR_INVALID_ARG),                     # a decode step has T = 1
+    (dict(T=1, a=FAKE, n_seqs=2, B=1), {}, B.PRN_ERR_INVALID_ARG),        # no ragged packs
+    (dict(T=1, a=None), {}, B.PRN_ERR_INVALID_ARG),
+    (dict(T=1, a=FAKE), dict(x=None), B.PRN_ERR_INVALID_ARG),
+    (dict(T=1, a=FAKE), dict(so=None), B.PRN_ERR_INVALID_ARG),
+    (dict(T=1, a=FAKE, d_in=6), {}, B.PRN_ERR_UNSUPPORTED),               # fp32 needs d_in % 4 == 0
+    (dict(T=1, a=FAKE, dtype=1, d_in=12), {}, B.PRN_ERR_UNSUPPORTED),     # bf16 needs d_in % 8 == 0
+    (dict(T=1, a=FAKE), dict(x=FAKE + 4), B.PRN_ERR_INVALID_ARG),         # x must be 16-byte aligned
+    (dict(T=1, a=FAKE), dict(si=FAKE + 4096, so=FAKE + 4096), B.PRN_ERR_INVALID_ARG),   # aliasing carry
+    (dict(T=1, a=FAKE, d_in=0), {}, B.PRN_ERR_INVALID_ARG),
+])
+def test_decode_step_rejects_bad_arguments_before_launch(kw, args, status):
+    p = _params(**kw)
+    a = dict(x=FAKE, W=FAKE, bias=None, si=None, so=FAKE + 8192, h=None)
+    a.update(args)
+    st = B.lib().prn_decode_step(a["x"], a["W"], a["bias"], ctypes.byref(p), a["si"], a["so"], a["h"])
+    assert st == status, B.prn_last_error()
+    assert B.prn_last_error()
