@@ -166,8 +166,17 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 // iteration 1 linearises at H^(1)_{t-1} = f(0 (h0 at a head), x_{t-1})
 // rather than at 0; it needs the projected inputs of one step before each
 // wave's sub-chunk, and r_0 is the residual of H^(1).
+// Waves per SIMD the compiler must leave room for: two for the longest
+// chunk (LS = 16, fp32 LSTM), whose register need otherwise lands a few
+// registers above 256 (the states_out instance: 264, 20 bytes of spills under
+// the cap) and halves the resident waves; no constraint otherwise.
+template <class C, int DT, int LS>
+constexpr int sp_min_waves() {
+  return (C::S == 2 && DT == kF32 && LS >= 16) ? 2 : 1;
+}
+
 template <class C, int DT, int LS, int NW, bool WS, bool PIC>
-__global__ void __launch_bounds__(kWave * NW)
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(sp_min_waves<C, DT, LS>())))
 k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
             int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
@@ -366,6 +375,17 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 
     // ---- fix-up of iteration k+1, linearisation of iteration k+2 ----
     const bool last = (k == K - 1);
+    // The output addresses are formed at the stores: an opaque copy of the
+    // bases per iteration keeps the compiler from hoisting LS 64-bit
+    // addresses out of the iteration loop, which would hold their registers
+    // through every iteration (fp32 LSTM at LS = 12: 236 -> 213 VGPRs, which
+    // is what lets LS = 16 fit two waves per SIMD).  The fp32 GRU fits three
+    // waves per SIMD either way and measured faster with the hoisted form.
+    typename ST::T* hq = hp;
+    typename ST::T* sq = sp;
+    typename ST::T* lq = slast;
+    int64_t dq = d_h;
+    if constexpr (!(S == 1 && DT == kF32)) asm volatile("" : "+v"(hq), "+v"(sq), "+s"(lq), "+s"(dq));
     acc = Map::identity();
     rmax = 0;
     float s[S];
@@ -399,10 +419,10 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           xs_get(j, xj);
           C::f(xj, pr, cf.as, cf.a, fv);
           if (ch_ok) {
-            hp[j * d_h] = ST::pack(s[S - 1]);
+            hq[j * dq] = ST::pack(s[S - 1]);
             if constexpr (WS) {
 #pragma unroll
-              for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
+              for (int q = 0; q < S; ++q) sq[(j * S + q) * dq] = ST::pack(s[q]);
             }
           }
 #pragma unroll
@@ -414,7 +434,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         }
         if (slast && ch_ok && (t0 + LS == T || sg.next == t0 + LS)) {
 #pragma unroll
-          for (int q = 0; q < S; ++q) slast[(sg.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+          for (int q = 0; q < S; ++q) lq[(sg.seg * S + q) * dq + ch] = ST::pack(s[q]);
         }
       }
     } else if (wact) {
@@ -441,14 +461,14 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           } else {
             C::f(xj, p, cf.as, cf.a, fv);
             if (ch_ok) {
-              hp[j * d_h] = ST::pack(s[S - 1]);
+              hq[j * dq] = ST::pack(s[S - 1]);
               if constexpr (WS) {
 #pragma unroll
-                for (int q = 0; q < S; ++q) sp[(j * S + q) * d_h] = ST::pack(s[q]);
+                for (int q = 0; q < S; ++q) sq[(j * S + q) * dq] = ST::pack(s[q]);
               }
               if (slast && st.last(t, T)) {
 #pragma unroll
-                for (int q = 0; q < S; ++q) slast[(st.seg * S + q) * d_h + ch] = ST::pack(s[q]);
+                for (int q = 0; q < S; ++q) lq[(st.seg * S + q) * dq + ch] = ST::pack(s[q]);
               }
             }
           }

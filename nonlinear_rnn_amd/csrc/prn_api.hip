@@ -46,23 +46,23 @@ constexpr int kScanSeg = 16;
 // the kernel when few chains (rows x 64-channel tiles) run side by side:
 // every chunk of a chain waits on the look-back of the chunks before it.
 // Measured at the long LSTM shape (8 chains): LS = 6, 8, 10, 12 took 1.00,
-// 0.97, 0.86, 0.78 ms; LS = 14 no longer fits 256 registers and took
-// 1.1 ms.  The GRU takes LS = 16 below 64 chains (4 chains: 0.25 -> 0.18
-// ms against LS = 8) and LS = 12 above (128 chains: 0.96 -> 0.91 ms;
-// LS = 16 took 1.05 ms there).
+// 0.97, 0.86, 0.78 ms; once the output addresses stopped being hoisted out
+// of the iteration loop (236 -> 213 registers at LS = 12), LS = 14 and 16
+// fit too: 0.756 and 0.713 ms (LS = 16 under a two-waves-per-SIMD register
+// cap, no spills).  A Picard sweep takes the same LS = 16 (0.78 ms at K = 2,
+// against 0.92 ms at LS = 10).  The GRU takes LS = 16 below 64 chains
+// (4 chains: 0.25 -> 0.18 ms against LS = 8) and LS = 12 above (128 chains:
+// 0.96 -> 0.91 ms; LS = 16 took 1.05 ms there).
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
-// keeps LS = 8 to stay within 256, and the bf16 GRU with many chains keeps
-// LS = 8 so that three workgroups still fit a CU (measured at 16 x 16384 x
-// 512: LS = 12 took 1.31 ms against 1.20 ms).
-// With a Picard sweep the fp32 LSTM at LS = 12 needs 258 registers (one wave
-// per SIMD); it takes LS = 10.
+// keeps LS = 8 (LS = 12 already needs 256 registers, LS = 16 spills); the
+// bf16 GRU with many chains takes LS = 10, the longest chunk that keeps four
+// waves per SIMD (122 registers, 35 KB of LDS) -- measured at 16 x 16384 x
+// 512: LS = 8 / 10 took 1.06 / 0.97 ms.
 constexpr int kSpNW = 4;
-constexpr int kSpLsLstm = 12, kSpLsLstmPicard = 10, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12,
-              kSpLsGruManyBf16 = 8;
+constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
 constexpr int64_t kSpManyChains = 64;
-int sp_ls(int cell, int dtype, int64_t n_chains, int picard) {
-  if (cell != PRN_CELL_DIAG_GRU)
-    return dtype == PRN_BF16 ? kSpLsLstmBf16 : (picard > 0 ? kSpLsLstmPicard : kSpLsLstm);
+int sp_ls(int cell, int dtype, int64_t n_chains) {
+  if (cell != PRN_CELL_DIAG_GRU) return dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm;
   if (n_chains < kSpManyChains) return kSpLsGruFew;
   return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
 }
@@ -219,7 +219,7 @@ PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
   PlanSp pl{};
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
-  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains, p->picard_iters);
+  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains);
   const int lc = pl.ls * kSpNW;
   pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_wg = pl.n_ch * pl.n_chains;
@@ -359,8 +359,6 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
         launch(std::integral_constant<int, kSpLsLstmBf16>{});
-      else if (pl.ls == kSpLsLstmPicard)
-        launch(std::integral_constant<int, kSpLsLstmPicard>{});
       else
         launch(std::integral_constant<int, kSpLsLstm>{});
     } else {
