@@ -131,6 +131,7 @@ def main() -> int:
     ap.add_argument("--K", type=int, default=None, help="override the workload's Newton depth")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing the T = 1 decode step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size reference for byte counters)")
@@ -238,13 +239,70 @@ def main() -> int:
         t_bw = np.array([e[0].elapsed_time(e[1]) for e in bev])
         bw_ms = float(t_bw.mean())
         bw_bytes = algorithmic_backward_bytes(w)
-        backward = {"kernels": "k_bw_reduce + k_tp_scan + k_bw_fix + k_bw_da_reduce (prn_newton_backward)",
+        backward = {"kernels": "k_bw_sp + k_bw_da_partial + k_bw_da_reduce (prn_newton_backward)",
                     "ms_mean": bw_ms, "ms_min": float(t_bw.min()), "tokens_per_s": w.tokens / (bw_ms * 1e-3),
                     "roofline": {"bound": "hbm", "achieved": bw_bytes / (bw_ms * 1e-3) / 1e9,
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": bw_bytes / (bw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                  "traffic": profiled_traffic("k_bw_sp", w.name), "algorithmic_bytes": bw_bytes}}
         print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
+
+    decode = None
+    if not args.no_decode:
+        # the serving step: one token for each of 64 slots per call (projection + cell fused), ping-pong carries
+        slots, n_tok = 64, 64
+        gen = torch.Generator(device=dev).manual_seed(2)
+        xd = torch.randn((n_tok, slots, w.d_in), generator=gen, device=dev).to(dt)
+        carry = [torch.zeros((slots, w.S, w.d_h), dtype=dt, device=dev) for _ in range(2)]
+        hd = torch.empty((slots, w.d_h), dtype=dt, device=dev)
+
+        def dstep(i):
+            B.prn_decode_step(xd[i % n_tok], W, bias, a, carry[(i + 1) % 2], cell=w.cell, state_in=carry[i % 2],
+                              h_out=hd, stream=stream)
+        for i in range(8):
+            dstep(i)
+        n_calls = 4 * n_tok
+        dev0, dev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        dev0.record(stream)
+        for i in range(n_calls):
+            dstep(i)
+        dev1.record(stream)
+        torch.cuda.synchronize()
+        us_eager = dev0.elapsed_time(dev1) * 1e3 / n_calls   # includes the Python call per token
+        # a serving loop replays captured steps: n_tok steps in one graph, replayed 4 times
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_tok):
+                B.prn_decode_step(xd[i], W, bias, a, carry[(i + 1) % 2], cell=w.cell, state_in=carry[i % 2],
+                                  h_out=hd)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_tok):
+                B.prn_decode_step(xd[i], W, bias, a, carry[(i + 1) % 2], cell=w.cell, state_in=carry[i % 2],
+                                  h_out=hd)
+        graph.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.current_stream()
+        dev0.record(gs)
+        for _ in range(4):
+            graph.replay()
+        dev1.record(gs)
+        torch.cuda.synchronize()
+        us = dev0.elapsed_time(dev1) * 1e3 / (4 * n_tok)
+        elt = 4 if w.dtype == "f32" else 2
+        dbytes = elt * (w.G * w.d_h * w.d_in + slots * w.d_in + 2 * slots * w.S * w.d_h + slots * w.d_h) \
+            + 4 * 2 * w.G * w.d_h
+        decode = {"kernel": "k_decode (prn_decode_step)", "slots": slots, "us_per_step": us,
+                  "us_per_step_eager": us_eager,
+                  "tokens_per_s": slots / (us * 1e-6),
+                  "roofline": {"bound": "hbm", "achieved": dbytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+                               "unit": "GB/s", "frac": dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                               "traffic": None, "algorithmic_bytes": dbytes}}
+        print(f"[bench] decode timed ({n_calls} calls)", file=sys.stderr, flush=True)
 
     residuals = res.cpu().tolist()
     ms_step = wall * 1e3 / args.steps
@@ -288,6 +346,7 @@ def main() -> int:
         "newton_tokens_per_s": w.tokens / (newton_ms * 1e-3),
         "residuals": residuals,
         "backward": backward,
+        "decode": decode,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -188,9 +188,9 @@ size_t prn_backward_workspace_bytes(const prn_params* params);
  * decode).  The token's projection and the cell step are fused:
  *   xproj_g = x W_g^T + bias_g (fp32 sums, rounded to the storage dtype as
  *             prn_input_proj's output is), s' = f(state_in, xproj).
- *   x          (B, d_in) storage dtype, 16-byte aligned; d_in % 4 == 0 (fp32) or
- *              % 8 == 0 (bf16), else PRN_ERR_UNSUPPORTED
- *   W, bias    as for prn_input_proj
+ *   x          (B, d_in) storage dtype
+ *   W, bias    (G*d_h, d_in) storage dtype and (G*d_h) fp32 or NULL, as for
+ *              prn_input_proj
  *   state_in   (B, S, d_h) storage dtype, the carry, or NULL for zeros
  *   state_out  (B, S, d_h) storage dtype: the new carry; must not alias state_in
  *              (callers ping-pong two buffers)
@@ -198,7 +198,10 @@ size_t prn_backward_workspace_bytes(const prn_params* params);
  * params: cell, dtype, B = slots, T = 1, d_in, d_h, a, stream.  One kernel
  * launch, no workspace, no memory set: it can be captured in a HIP graph with
  * its buffers pinned.  The result equals prn_input_proj + prn_sequential_forward
- * on the same token up to the summation order of the projection. */
+ * on the same token up to the summation order of the projection.
+ * Errors (nothing is launched): PRN_ERR_INVALID_ARG for T != 1, a ragged pack
+ * (n_seqs > 0), d_in < 1, NULL x / W / a / state_out, a pointer not aligned
+ * to its element size, or state_in == state_out. */
 prn_status prn_decode_step(const void* x, const void* W, const float* bias, const prn_params* params,
                            const void* state_in, void* state_out, void* h_out);
 

@@ -340,7 +340,11 @@ k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storag
 #pragma unroll
     for (int v = NW - 2; v >= 0; --v) tot = compose(part[v][lane], tot);
     float cin[S];
-    lookback_carry<S>(rec, base, rchunk, tot, lane, spin_limit, agg_first, cin);
+    // four records in flight per batch (not the forward's eight): with eight
+    // the fp32 LSTM instance needs 148 registers, three waves per SIMD and so
+    // one 8-wave workgroup per CU; with four, 124 and two workgroups
+    // (measured: 0.98 -> 0.74 ms at 2 x 131072 x 256)
+    lookback_carry<S, 4>(rec, base, rchunk, tot, lane, spin_limit, agg_first, cin);
 #pragma unroll
     for (int q = 0; q < S; ++q) carry_sh[q][lane] = cin[q];
     // what leaves the chunk towards earlier ones goes out before the barrier,

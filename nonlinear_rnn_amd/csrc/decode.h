@@ -3,65 +3,100 @@
 // token's input projection then one cell step): projection and cell fused
 // in one launch.
 //
-// A workgroup takes 64 channels of one slot; its four waves each sum a
-// quarter of d_in for all G gates (lane = channel, 16-byte loads along the
-// weight row), the quarters are added in a fixed order through LDS with the
-// bias, the projected value is rounded to the storage dtype (as the
-// projection's output would be), and wave 0 steps the cell from the carry.
+// One wave takes one channel and a group of 16 slots.  Lanes run along d_in
+// (each weight row and each token is read in coalesced 64-element pieces),
+// and every lane keeps a partial sum for each of the 4 x 16 (gate, slot)
+// outputs (the GRU's three gates padded to four).  A transpose-reduce
+// butterfly (at stage m a lane keeps the half of its partials selected by
+// its lane bit m and adds its xor-m partner's copy of that half: 63
+// shuffle-adds in all) leaves lane l with the complete sum of output l.
+// The sum gets its bias, is rounded to the storage dtype (as the
+// projection's output would be), and lanes 0..15 gather their slot's gates
+// and step the cell from the carry.  Waves are independent: no LDS, no
+// barrier.
 #pragma once
 
 #include "newton_kernels.h"
 
 namespace prn {
 
+constexpr int kDecodeSlots = 16;  // slots per wave
+constexpr int kDecodeWaves = 4;   // channels (waves) per workgroup
+
 template <class C, int DT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kWave * kDecodeWaves)
 k_decode(const typename Storage<DT>::T* __restrict__ x, const typename Storage<DT>::T* __restrict__ W,
-         const float* __restrict__ bias, const float* __restrict__ a, int64_t d_in, int64_t d_h,
+         const float* __restrict__ bias, const float* __restrict__ a, int64_t n_slots, int64_t d_in, int64_t d_h,
          const typename Storage<DT>::T* __restrict__ sin, typename Storage<DT>::T* __restrict__ sout,
          typename Storage<DT>::T* __restrict__ hout) {
   using ST = Storage<DT>;
-  constexpr int G = C::G, S = C::S;
-  constexpr int VE = 16 / sizeof(typename ST::T);  // elements per 16-byte load
-  const int lane = threadIdx.x & (kWave - 1), part = threadIdx.x / kWave;
-  const int64_t ch_l = static_cast<int64_t>(blockIdx.x) * kWave + lane;
-  const bool ch_ok = ch_l < d_h;
-  const int64_t ch = ch_ok ? ch_l : d_h - 1;
-  const int64_t slot = blockIdx.y;
-  __shared__ float red[4][G][kWave];
+  constexpr int G = C::G, S = C::S, GP = 4, SB = kDecodeSlots;
+  static_assert(G <= GP && GP * SB == kWave, "one output per lane after the reduction");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * kDecodeWaves + threadIdx.x / kWave;
+  if (ch >= d_h) return;  // whole wave
+  const int64_t s0 = static_cast<int64_t>(blockIdx.y) * SB;
+  const int n_s = static_cast<int>(imin(SB, n_slots - s0));
 
-  // this wave's quarter of the reduction dimension, in whole 16-byte vectors
-  const int64_t nvec = d_in / VE;
-  const int64_t v0 = part * nvec / 4, v1 = (part + 1) * nvec / 4;
-  const typename ST::T* xr = x + slot * d_in;
-  float acc[G];
+  // partial dot products: p[g * SB + s] over this lane's k = lane, lane + 64,
+  // ...; U row pieces per round, their loads issued together (the loop is
+  // bound by load latency, not by the multiply-adds).  The loads carry no
+  // guard (a guard per load becomes a branch per load, which serialises
+  // them): a k past d_in reads the last column with a zero weight, a slot
+  // past the last one rereads the last slot, whose outputs nobody stores.
+  constexpr int U = 4;
+  float p[GP * SB];
 #pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-  for (int64_t v = v0; v < v1; ++v) {
-    float xv[VE];
+  for (int i = 0; i < GP * SB; ++i) p[i] = 0.0f;
+  for (int64_t k0 = lane; k0 < d_in; k0 += U * kWave) {
+    float wv[U][G], xv[U][SB];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) xv[e] = ST::load(xr + v * VE + e);
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u * kWave;
+      const bool ok = k < d_in;
+      const int64_t kc = ok ? k : d_in - 1;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const typename ST::T* wr = W + (g * d_h + ch) * d_in + v * VE;
+      for (int g = 0; g < G; ++g) {
+        const float v = ST::load(W + (g * d_h + ch) * d_in + kc);
+        wv[u][g] = ok ? v : 0.0f;
+      }
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g] = fmaf(xv[e], ST::load(wr + e), acc[g]);
+      for (int s = 0; s < SB; ++s) xv[u][s] = ST::load(x + (s0 + imin(s, n_s - 1)) * d_in + kc);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int s = 0; s < SB; ++s) p[g * SB + s] = fmaf(wv[u][g], xv[u][s], p[g * SB + s]);
+  }
+  // transpose-reduce: after the stage with offset m, lane l holds n = m
+  // partials, those of the outputs whose bit log2(m) equals l's bit log2(m)
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) {
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      const float keep = hi ? p[i + m] : p[i];
+      const float send = hi ? p[i] : p[i + m];
+      p[i] = keep + __shfl_xor(send, m, kWave);
     }
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) red[part][g][lane] = acc[g];
-  __syncthreads();
-  if (part != 0 || !ch_ok) return;
-
-  ChanCoef<C> cf;
-  cf.load(a, d_h, ch);
+  // lane l = g * SB + s holds the projected value of gate g, slot s
+  const int g_l = lane / SB;
+  float v = p[0];
+  if (g_l < G) {
+    if (bias) v += bias[g_l * d_h + ch];
+    v = ST::round(v);
+  }
   float xs[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float v = ((red[0][g][lane] + red[1][g][lane]) + red[2][g][lane]) + red[3][g][lane];
-    if (bias) v += bias[g * d_h + ch];
-    xs[g] = ST::round(v) * C::scale(g);
-  }
+  for (int g = 0; g < G; ++g) xs[g] = __shfl(v, g * SB + (lane & (SB - 1)), kWave) * C::scale(g);
+  if (lane >= n_s) return;  // lanes 0..n_s-1: one slot each
+
+  const int64_t slot = s0 + lane;
+  ChanCoef<C> cf;
+  cf.load(a, d_h, ch);
   float s[S], o[S];
 #pragma unroll
   for (int q = 0; q < S; ++q) s[q] = 0.0f;

@@ -90,11 +90,11 @@ struct SpRecords {
 // latencies overlapped) and applied to the prefix.  A run that ends at an
 // unpublished chunk is consumed as far as it goes before polling again.
 // Chunk 0 of a chain has carry 0 (its first step is a segment head, J = 0).
-template <int S>
+template <int S, int RB = 8>
 __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t base, int64_t chunk,
                                                const Aff<S>& tot, int lane, unsigned spin_limit, bool agg_first, float* cin) {
   using Map = Aff<S>;
-  constexpr int NC = S * S + S, RB = 8;
+  constexpr int NC = S * S + S;
 #pragma unroll
   for (int q = 0; q < S; ++q) cin[q] = 0.0f;
   if (chunk == 0) return;

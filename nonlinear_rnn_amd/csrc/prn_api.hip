@@ -488,22 +488,21 @@ prn_status prn_decode_step(const void* x, const void* W, const float* bias, cons
   if (sh.ragged) return fail(PRN_ERR_INVALID_ARG, "a decode step takes slots (B), not a ragged pack");
   if (p->d_in < 1) return fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
   if (!x || !W || !p->a || !state_out) return fail(PRN_ERR_INVALID_ARG, "x, W, a or state_out is NULL");
-  const int vec = p->dtype == PRN_F32 ? 4 : 8;
-  if (p->d_in % vec != 0)
-    return fail(PRN_ERR_UNSUPPORTED, "decode step needs d_in %% %d == 0 for this storage dtype", vec);
-  if (misaligned(x, 16) || misaligned(W, 16) || misaligned(bias, 4) || misaligned(p->a, 4) ||
+  if (misaligned(x, sh.elt) || misaligned(W, sh.elt) || misaligned(bias, 4) || misaligned(p->a, 4) ||
       misaligned(state_in, sh.elt) || misaligned(state_out, sh.elt) || misaligned(h_out, sh.elt))
-    return fail(PRN_ERR_INVALID_ARG, "x and W must be 16-byte aligned, the rest to their element size");
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   if (state_in && state_in == state_out) return fail(PRN_ERR_INVALID_ARG, "state_in and state_out alias");
   hipStream_t st = static_cast<hipStream_t>(p->stream);
-  const dim3 grid(unsigned((p->d_h + 63) / 64), unsigned(p->B));
+  // one wave per (channel, group of 16 slots); 4 channels per workgroup
+  const dim3 grid(unsigned((p->d_h + prn::kDecodeWaves - 1) / prn::kDecodeWaves),
+                  unsigned((p->B + prn::kDecodeSlots - 1) / prn::kDecodeSlots));
   auto go = [&](auto cell, auto dt) {
     using C = decltype(cell);
     constexpr int DT = decltype(dt)::value;
     using T = typename prn::Storage<DT>::T;
-    prn::k_decode<C, DT><<<grid, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(W), bias, p->a,
-                                               p->d_in, p->d_h, static_cast<const T*>(state_in),
-                                               static_cast<T*>(state_out), static_cast<T*>(h_out));
+    prn::k_decode<C, DT><<<grid, 64 * prn::kDecodeWaves, 0, st>>>(
+        static_cast<const T*>(x), static_cast<const T*>(W), bias, p->a, p->B, p->d_in, p->d_h,
+        static_cast<const T*>(state_in), static_cast<T*>(state_out), static_cast<T*>(h_out));
   };
   using F32 = std::integral_constant<int, prn::kF32>;
   using BF16 = std::integral_constant<int, prn::kBF16>;

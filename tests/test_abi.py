@@ -183,9 +183,8 @@ def test_committed_kstar_table_is_well_formed():
     (dict(T=1, a=None), {}, B.PRN_ERR_INVALID_ARG),
     (dict(T=1, a=FAKE), dict(x=None), B.PRN_ERR_INVALID_ARG),
     (dict(T=1, a=FAKE), dict(so=None), B.PRN_ERR_INVALID_ARG),
-    (dict(T=1, a=FAKE, d_in=6), {}, B.PRN_ERR_UNSUPPORTED),               # fp32 needs d_in % 4 == 0
-    (dict(T=1, a=FAKE, dtype=1, d_in=12), {}, B.PRN_ERR_UNSUPPORTED),     # bf16 needs d_in % 8 == 0
-    (dict(T=1, a=FAKE), dict(x=FAKE + 4), B.PRN_ERR_INVALID_ARG),         # x must be 16-byte aligned
+    (dict(T=1, a=FAKE), dict(x=FAKE + 2), B.PRN_ERR_INVALID_ARG),         # fp32 x not 4-byte aligned
+    (dict(T=1, a=FAKE, dtype=1), dict(W=FAKE + 1), B.PRN_ERR_INVALID_ARG),  # bf16 W not 2-byte aligned
     (dict(T=1, a=FAKE), dict(si=FAKE + 4096, so=FAKE + 4096), B.PRN_ERR_INVALID_ARG),   # aliasing carry
     (dict(T=1, a=FAKE, d_in=0), {}, B.PRN_ERR_INVALID_ARG),
 ])

@@ -51,13 +51,18 @@ def run_decode(cell, dtype, x, W, bias, a, s0, with_h=True):
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-@pytest.mark.parametrize("dtype,d_in,d_h", [("f32", 36, 130), ("bf16", 40, 130), ("f32", 4, 64),
-                                            ("bf16", 512, 1000), ("f32", 1024, 257)])
+@pytest.mark.parametrize("dtype,slots,d_in,d_h", [("f32", 5, 36, 130), ("bf16", 5, 40, 130), ("f32", 16, 4, 64),
+                                                  ("bf16", 37, 512, 1000), ("f32", 3, 1024, 257),
+                                                  ("f32", 33, 7, 6), ("bf16", 17, 13, 70), ("f32", 1, 1, 1),
+                                                  ("f32", 64, 256, 256)])
 @pytest.mark.parametrize("with_state", [True, False])
-def test_decode_step_matches_oracle(cell, dtype, d_in, d_h, with_state):
-    say(f"[case] decode {cell} {dtype} d_in={d_in} d_h={d_h} state={with_state}")
+def test_decode_step_matches_oracle(cell, dtype, slots, d_in, d_h, with_state):
+    """Slot counts around the 16-slot group (1, 3, 5, 16, 17, 33, 37, 64),
+    channel counts around the 4-channel workgroup, d_in around the 64-lane
+    row piece (1, 4, 7, 13, 36, 40, 256, 512, 1024)."""
+    say(f"[case] decode {cell} {dtype} slots={slots} d_in={d_in} d_h={d_h} state={with_state}")
     G, S = GS[cell]
-    x, W, bias, a, s0 = inputs(cell, dtype, 5, d_in, d_h, seed=d_in * 7 + d_h)
+    x, W, bias, a, s0 = inputs(cell, dtype, slots, d_in, d_h, seed=d_in * 7 + d_h)
     s0 = s0 if with_state else None
     sout, h = run_decode(cell, dtype, x, W, bias, a, s0)
     # x, W and s0 hold values the storage dtype represents exactly (oracle rounding.store)
