@@ -116,10 +116,17 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
             el = time.perf_counter() - t0
             if el > budget_s:
                 break
+        # the oracle's sequential unroll (the definition Newton approximates) on the same sample
+        t1 = time.perf_counter()
+        onewton.sequential(w.cell, xp, inp["a"].astype(np.float64), cu_seqlens=cu)
+        el_seq = time.perf_counter() - t1
     tok = reps * ws.tokens
     return {"value": tok / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} x (B=1, T={T_s}, all {w.d_h} channels, K={w.K}) of {w.name}: "
-                      f"numpy float64 projection + Newton, 1 thread, {el:.1f} s"}
+                      f"numpy float64 projection + Newton, 1 thread, {el:.1f} s",
+            "sequential_unroll": {"value": ws.tokens / el_seq, "unit": "tokens/s", "cores": 1,
+                                  "sample": f"1 x the same sample, the oracle's sequential unroll "
+                                            f"(numpy float64), 1 thread, {el_seq:.1f} s"}}
 
 
 def main() -> int:
@@ -210,6 +217,18 @@ def main() -> int:
     t_newt = np.array([e[1].elapsed_time(e[2]) for e in evs])
     t_step = np.array([e[0].elapsed_time(e[2]) for e in evs])
     print(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    # the same steps with the 256 MB last-level cache (MALL) flushed before each one by writing
+    # a 1 GiB buffer, so that a working set that fits the cache is read from HBM again
+    flush = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.zero_()
+        step(fev[i])
+    torch.cuda.synchronize()
+    del flush
+    t_newt_fl = np.array([e[1].elapsed_time(e[2]) for e in fev])
+    t_proj_fl = np.array([e[0].elapsed_time(e[1]) for e in fev])
 
     backward = None
     if not args.no_backward:
@@ -344,10 +363,16 @@ def main() -> int:
         "breakdown_ms": {"proj_mean": proj_ms, "newton_mean": newton_ms, "newton_median": float(np.median(t_newt)),
                          "newton_min": float(t_newt.min()), "step_event_mean": float(t_step.mean())},
         "newton_tokens_per_s": w.tokens / (newton_ms * 1e-3),
+        "breakdown_ms_mall_flushed": {"proj_mean": float(t_proj_fl.mean()), "newton_mean": float(t_newt_fl.mean()),
+                                      "newton_median": float(np.median(t_newt_fl)),
+                                      "newton_min": float(t_newt_fl.min()),
+                                      "newton_hbm_frac": alg_bytes / (float(t_newt_fl.mean()) * 1e-3) / 1e9
+                                      / HBM_PEAK_GBPS},
         "residuals": residuals,
         "backward": backward,
         "decode": decode,
         "device": torch.cuda.get_device_name(0),
+        "hip_runtime": torch.version.hip,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)

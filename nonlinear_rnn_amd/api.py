@@ -183,27 +183,37 @@ def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol
 # The train-mode forward + backward of one diagonal layer (FAQs, "train() vs
 # eval()"; shapes/layout page, the train forward+backward surface): the
 # Newton forward keeps its trajectory (states_out) and the backward is
-# prn_newton_backward at that trajectory.  The projection's own gradients
-# are plain matrix products of dL/dxproj, left to torch's BLAS.
+# prn_newton_backward at that trajectory.  With recompute=True (the pages'
+# NewtonConfig(recompute=True) for long sequences) the forward keeps only
+# its inputs and the backward runs the forward again to rebuild the
+# trajectory: (B, T, S, d_h) less memory held between the passes, one more
+# forward in the backward.  The projection's own gradients are plain matrix
+# products of dL/dxproj, left to torch's BLAS.
+
+def _forward_states(xproj, a, h0, cell, K, cu, picard_iters, with_states):
+    Bn, T, G, d_h = xproj.shape
+    n_seqs = 0 if cu is None else cu.numel() - 1
+    H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
+    states = (torch.empty((Bn, T, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
+              if with_states else None)
+    res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
+    n = B_.prn_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, K, n_seqs=n_seqs, picard_iters=picard_iters)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
+    B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=h0, cu_seqlens=cu, residual_out=res,
+                          states_out=states, workspace=ws, picard_iters=picard_iters)
+    return H, states, res
+
 
 class _NewtonFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, xproj, a, h0, cell, K, cu, picard_iters, residual_fail, gate):
-        Bn, T, G, d_h = xproj.shape
-        S = B_.STATE[cell]
-        n_seqs = 0 if cu is None else cu.numel() - 1
-        H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
-        states = torch.empty((Bn, T, S, d_h), dtype=xproj.dtype, device=xproj.device)
-        res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
-        n = B_.prn_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, K, n_seqs=n_seqs, picard_iters=picard_iters)
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
-        B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=h0, cu_seqlens=cu, residual_out=res,
-                              states_out=states, workspace=ws, picard_iters=picard_iters)
+    def forward(ctx, xproj, a, h0, cell, K, cu, picard_iters, residual_fail, gate, recompute):
+        H, states, res = _forward_states(xproj, a, h0, cell, K, cu, picard_iters, not recompute)
         ctx.residuals = res.cpu().tolist()
         if gate:
             gate_residual(ctx.residuals, xproj.dtype, residual_fail)
-        ctx.cell, ctx.cu = cell, cu
-        ctx.save_for_backward(xproj, a, h0 if h0 is not None else torch.empty(0), states)
+        ctx.cell, ctx.cu, ctx.K, ctx.picard_iters, ctx.recompute = cell, cu, K, picard_iters, recompute
+        ctx.save_for_backward(xproj, a, h0 if h0 is not None else torch.empty(0),
+                              states if states is not None else torch.empty(0))
         ctx.has_h0 = h0 is not None
         return H
 
@@ -212,6 +222,8 @@ class _NewtonFunction(torch.autograd.Function):
         xproj, a, h0, states = ctx.saved_tensors
         h0 = h0 if ctx.has_h0 else None
         cell, cu = ctx.cell, ctx.cu
+        if ctx.recompute:
+            _, states, _ = _forward_states(xproj, a, h0, cell, ctx.K, cu, ctx.picard_iters, True)
         Bn, T, G, d_h = xproj.shape
         n_seqs = 0 if cu is None else cu.numel() - 1
         rows = Bn if cu is None else n_seqs
@@ -223,13 +235,16 @@ class _NewtonFunction(torch.autograd.Function):
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
         B_.prn_newton_backward(xproj, a, states, dH.to(xproj.dtype).contiguous(), dxproj, da, cell=cell, h0=h0,
                                cu_seqlens=cu, dh0_out=dh0, workspace=ws)
-        return dxproj, da, dh0, None, None, None, None, None, None
+        return dxproj, da, dh0, None, None, None, None, None, None, None
 
 
 def newton_apply(xproj, a, K=None, *, cell: str, h0=None, cu_seqlens=None, picard_iters: int = 0,
-                 residual_fail=RESIDUAL_FAIL, gate=True):
+                 residual_fail=RESIDUAL_FAIL, gate=True, recompute: bool = False):
     """Differentiable Newton forward: H (B,T,d_h); gradients reach xproj, a
-    and h0 through the backward pass.  K = None resolves the measured K*(T)."""
+    and h0 through the backward pass.  K = None resolves the measured K*(T).
+    recompute=True keeps no trajectory between the passes and rebuilds it in
+    the backward (the same kernels, so the same trajectory up to the
+    look-back's run-to-run rounding, ~1e-7)."""
     xproj = xproj.contiguous()
     Bn, T, _, _ = xproj.shape
     if K is None:
@@ -237,7 +252,7 @@ def newton_apply(xproj, a, K=None, *, cell: str, h0=None, cu_seqlens=None, picar
         K = resolve_k(T, load_table(cell))
     cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
     return _NewtonFunction.apply(xproj, a.contiguous(), _contig(h0), cell, int(K), cu, int(picard_iters),
-                                 residual_fail, gate)
+                                 residual_fail, gate, bool(recompute))
 
 
 class _ProjFunction(torch.autograd.Function):

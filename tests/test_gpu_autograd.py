@@ -77,3 +77,30 @@ def test_autograd_gradient_is_the_unrolls_at_kstar():
     e = rel(to_f64(xproj.grad), dxp)
     say(f"  gradient vs the unroll's: {e:.1e}")
     assert e <= 1e-3
+
+
+@pytest.mark.parametrize("cell,cu", [("lstm", None), ("gru", [0, 200, 200, 700, 900])])
+def test_recompute_gives_the_stored_trajectory_gradients(cell, cu):
+    """recompute=True rebuilds the trajectory in the backward: gradients equal
+    those of the stored-trajectory backward up to the look-back's run-to-run
+    rounding."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    G, S = (3, 1) if cell == "gru" else (4, 2)
+    Bn = 2 if cu is None else 1
+    T, d_h = 900, 80
+    rows = Bn if cu is None else len(cu) - 1
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32)
+    xp0 = torch.randn((Bn, T, G, d_h), generator=g, device="cuda")
+    a0 = torch.rand((G, d_h), generator=g, device="cuda") - 0.5
+    h00 = 0.5 * torch.randn((rows, S, d_h), generator=g, device="cuda")
+    wgt = torch.randn((Bn, T, d_h), generator=g, device="cuda")
+    grads = []
+    for rc in (False, True):
+        xp, a, h0 = (t.clone().requires_grad_() for t in (xp0, a0, h00))
+        H = prn.newton_apply(xp, a, 3, cell=cell, h0=h0, cu_seqlens=cu_t, recompute=rc)
+        (H * wgt).sum().backward()
+        grads.append([to_f64(t.grad) for t in (xp, a, h0)])
+    for name, u, v in zip(("xproj", "a", "h0"), *grads):
+        e = rel(u, v)
+        say(f"  recompute vs stored, {cell} {name}: {e:.1e}")
+        assert e <= 1e-5
