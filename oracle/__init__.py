@@ -13,6 +13,8 @@ Plain NumPy in float64, written to be checked by eye:
            residual max|F(H)|
   backward gradients through the recurrence: the reverse-time adjoint
            recurrence at a given trajectory
+  headmix  the head-mix GRU (dense d_head x d_head recurrent blocks): cell,
+           Jacobian blocks, unroll and Newton
   scan     exact (rational) affine-map composition, every bracketing, and
            the chunked three-phase scan
   rounding storage-dtype rounding (fp32, bf16 round-to-nearest-even)
@@ -22,4 +24,4 @@ the "Numerics contract" page, and the shapes/layout page on contiguity and
 ragged packs) it follows, or which definition it writes out where the pages
 leave the step open.
 """
-from . import backward, cells, newton, proj, rounding, scan  # noqa: F401
+from . import backward, cells, headmix, newton, proj, rounding, scan  # noqa: F401
