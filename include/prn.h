@@ -205,6 +205,31 @@ size_t prn_backward_workspace_bytes(const prn_params* params);
 prn_status prn_decode_step(const void* x, const void* W, const float* bias, const prn_params* params,
                            const void* state_in, void* state_out, void* h_out);
 
+/* ---- Head-mix GRU (shapes/layout page, support table: the GRU with
+ * mix='head'; FAQs, memory notes: heads of d_head channels).  Reading: the
+ * hidden width splits into n_heads = d_h / d_head heads, and each gate's
+ * recurrent term becomes a dense d_head x d_head block per head:
+ *   z = sig(x_z + A_z h)  r = sig(x_r + A_r h)  c = tanh(x_c + A_c (r * h))
+ *   h' = (1 - z) * h + z * c         (A_g h: each head's block times its slice)
+ * Newton as for the diagonal cells, with dense Jacobian blocks per head.
+ *   A          (3, n_heads, d_head, d_head) fp32, gate order z, r, c; A[g][k][i][j]
+ *              multiplies channel j of head k into channel i (row-major blocks)
+ *   xproj      (B, T, 3, d_h) fp32, as for the diagonal GRU
+ *   h0         (B, d_h) fp32 or NULL (zeros)
+ *   H_out      (B, T, d_h) fp32
+ * params: cell = PRN_CELL_DIAG_GRU, dtype = PRN_F32, B, T, d_h, n_seqs = 0,
+ * state_last_out ((B, d_h) or NULL), workspace, stream; a, states_out and
+ * picard_iters are not used (states_out / picard_iters must be 0).
+ * Supported: d_head = 16, fp32, rectangular batches (the pages' head-mix
+ * fused path takes no ragged pack); anything else is PRN_ERR_UNSUPPORTED.
+ * Errors as for prn_newton_forward; residual_out as there (K + 1 values). */
+size_t prn_head_workspace_bytes(const prn_params* params, int32_t d_head, int32_t K);
+prn_status prn_head_newton_forward(const void* xproj, const prn_params* params, const float* A, int32_t d_head,
+                                   const void* h0, int32_t K, void* H_out, float* residual_out);
+/* The unroll h_t = f(h_{t-1}, x_t) of the head-mix GRU; no workspace. */
+prn_status prn_head_sequential_forward(const void* xproj, const prn_params* params, const float* A,
+                                       int32_t d_head, const void* h0, void* H_out);
+
 /* Host-side check of ragged offsets (the validate_cu_seqlens contract of
  * the shapes/layout page): cu_host has n_seqs + 1 entries, cu[0] = 0,
  * non-decreasing, cu[n_seqs] = N.  cu_host is a HOST pointer. */

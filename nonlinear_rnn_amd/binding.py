@@ -27,7 +27,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # every symbol include/prn.h declares
 EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_workspace_bytes",
-           "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_validate_cu_seqlens",
+           "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_head_newton_forward",
+           "prn_head_sequential_forward", "prn_head_workspace_bytes", "prn_validate_cu_seqlens",
            "prn_last_error", "prn_version")
 
 
@@ -77,12 +78,17 @@ def lib() -> ctypes.CDLL:
         L.prn_newton_backward.argtypes = [vp, P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.prn_backward_workspace_bytes.argtypes = [P]
         L.prn_decode_step.argtypes = [vp, vp, vp, P, vp, vp, vp]
+        L.prn_head_newton_forward.argtypes = [vp, P, vp, i32, vp, i32, vp, vp]
+        L.prn_head_sequential_forward.argtypes = [vp, P, vp, i32, vp, vp]
+        L.prn_head_workspace_bytes.argtypes = [P, i32, i32]
+        L.prn_head_workspace_bytes.restype = ctypes.c_size_t
         L.prn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
         for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_newton_backward",
-                     "prn_decode_step", "prn_validate_cu_seqlens"):
+                     "prn_decode_step", "prn_head_newton_forward", "prn_head_sequential_forward",
+                     "prn_validate_cu_seqlens"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -285,3 +291,41 @@ def prn_decode_step(x, W, bias, a, state_out, *, cell: str, state_in=None, h_out
     p = make_params(cell, x.dtype, Bn, 1, d_h, d_in=d_in, a=a, stream=stream)
     _check(lib().prn_decode_step(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(state_in), _ptr(state_out),
                                  _ptr(h_out)))
+
+
+def _head_common(xproj, A, H_out, h0, state_last_out, d_head):
+    for t, n in ((xproj, "xproj"), (A, "A"), (H_out, "H_out"), (h0, "h0"), (state_last_out, "state_last_out")):
+        _dev(t, n, torch.float32)
+    Bn, T, G, d_h = xproj.shape
+    if G != 3 or d_h % d_head or A.shape != (3, d_h // d_head, d_head, d_head) or H_out.shape != (Bn, T, d_h):
+        raise ValueError(f"shape mismatch: xproj {tuple(xproj.shape)} A {tuple(A.shape)} H_out {tuple(H_out.shape)}")
+    for t, n in ((h0, "h0"), (state_last_out, "state_last_out")):
+        if t is not None and t.shape != (Bn, d_h):
+            raise ValueError(f"{n} must be (B, d_h)")
+    return Bn, T, d_h
+
+
+def prn_head_workspace_bytes(B: int, T: int, d_h: int, K: int, d_head: int = 16) -> int:
+    p = make_params("gru", torch.float32, B, T, d_h)
+    n = int(lib().prn_head_workspace_bytes(ctypes.byref(p), d_head, K))
+    if n == 0 and T > 0 and prn_last_error():
+        raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
+    return n
+
+
+def prn_head_newton_forward(xproj, A, K: int, H_out, *, d_head: int = 16, h0=None, residual_out=None,
+                            state_last_out=None, workspace=None, stream=None) -> None:
+    """Head-mix GRU Newton forward: xproj (B,T,3,d_h), A (3, d_h/d_head, d_head, d_head), fp32."""
+    Bn, T, d_h = _head_common(xproj, A, H_out, h0, state_last_out, d_head)
+    _dev(residual_out, "residual_out", torch.float32)
+    p = make_params("gru", torch.float32, Bn, T, d_h, state_last_out=state_last_out, workspace=workspace,
+                    stream=stream)
+    _check(lib().prn_head_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(A), d_head, _ptr(h0), int(K),
+                                         _ptr(H_out), _ptr(residual_out)))
+
+
+def prn_head_sequential_forward(xproj, A, H_out, *, d_head: int = 16, h0=None, state_last_out=None,
+                                stream=None) -> None:
+    Bn, T, d_h = _head_common(xproj, A, H_out, h0, state_last_out, d_head)
+    p = make_params("gru", torch.float32, Bn, T, d_h, state_last_out=state_last_out, stream=stream)
+    _check(lib().prn_head_sequential_forward(_ptr(xproj), ctypes.byref(p), _ptr(A), d_head, _ptr(h0), _ptr(H_out)))

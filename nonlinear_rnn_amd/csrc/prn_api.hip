@@ -14,6 +14,7 @@
 
 #include "backward.h"
 #include "decode.h"
+#include "headmix.h"
 #include "newton_kernels.h"
 #include "newton_sp.h"
 #include "proj.h"
@@ -475,6 +476,43 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
   return launched("prn_newton_backward");
 }
 
+// ---- head-mix GRU (dense d_head x d_head recurrent blocks) ----
+struct PlanHm {
+  int64_t n_heads, n_ch, n_wg;
+  size_t iter_off, n_iter, agg_off, carry_off, rpart_off, total;
+};
+
+PlanHm plan_hm(const prn_params* p, int K) {
+  PlanHm pl{};
+  pl.n_heads = p->d_h / prn::kHmD;
+  pl.n_ch = (p->T + prn::kHmChunk - 1) / prn::kHmChunk;
+  pl.n_wg = p->B * pl.n_heads * pl.n_ch;
+  pl.n_iter = size_t(std::min(K - 1, 2));  // ping-pong iterates H^(1..K-1); H^(K) goes to H_out
+  const size_t it = align_up(size_t(p->B) * p->T * p->d_h * 4);
+  pl.iter_off = 0;
+  pl.agg_off = pl.n_iter * it;
+  pl.carry_off = pl.agg_off + align_up(size_t(pl.n_wg) * prn::kHmNC * 4);
+  pl.rpart_off = pl.carry_off + align_up(size_t(pl.n_wg) * prn::kHmD * 4);
+  pl.total = pl.rpart_off + align_up(size_t(K + 1) * pl.n_wg * 4);
+  return pl;
+}
+
+// Head-mix support: the GRU, fp32 storage, rectangular batches (the pages'
+// head-mix fused path takes no ragged pack), d_head = 16.
+prn_status check_head(const prn_params* p, Shape* sh, int32_t d_head) {
+  prn_status s = check_common(p, sh);
+  if (s != PRN_OK) return s;
+  if (p->cell != PRN_CELL_DIAG_GRU) return fail(PRN_ERR_UNSUPPORTED, "head-mix blocks are built for the GRU cell");
+  if (p->dtype != PRN_F32) return fail(PRN_ERR_UNSUPPORTED, "head-mix runs with fp32 storage only");
+  if (p->n_seqs != 0) return fail(PRN_ERR_UNSUPPORTED, "head-mix takes rectangular batches, not a ragged pack");
+  if (d_head != prn::kHmD) return fail(PRN_ERR_UNSUPPORTED, "d_head = %d: head-mix is built for d_head = 16", d_head);
+  if (p->d_h % d_head != 0) return fail(PRN_ERR_INVALID_ARG, "d_h = %lld is not a multiple of d_head", (long long)p->d_h);
+  if (p->d_h / d_head > kMaxGrid) return fail(PRN_ERR_UNSUPPORTED, "more than %lld heads", (long long)kMaxGrid);
+  if (p->states_out || p->picard_iters)
+    return fail(PRN_ERR_UNSUPPORTED, "head-mix has no states_out or Picard sweep");
+  return PRN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -643,6 +681,91 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias, const
     return fail(PRN_ERR_UNSUPPORTED, "input projection too large");
   prn::launch_proj(p->dtype == PRN_BF16, x, W, bias, xproj_out, M, N, Kd, static_cast<hipStream_t>(p->stream));
   return launched("prn_input_proj");
+}
+
+size_t prn_head_workspace_bytes(const prn_params* p, int32_t d_head, int32_t K) {
+  Shape sh;
+  if (check_head(p, &sh, d_head) != PRN_OK) return 0;
+  if (K < 1) {
+    fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+    return 0;
+  }
+  return p->T > 0 ? plan_hm(p, K).total : 0;
+}
+
+prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const float* A, int32_t d_head,
+                                   const void* h0, int32_t K, void* H_out, float* residual_out) {
+  Shape sh;
+  prn_status s = check_head(p, &sh, d_head);
+  if (s != PRN_OK) return s;
+  if (!A) return fail(PRN_ERR_INVALID_ARG, "the recurrent blocks A are NULL");
+  if (misaligned(A, 4)) return fail(PRN_ERR_INVALID_ARG, "A is not 4-byte aligned");
+  if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+  if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
+  if (misaligned(xproj, 4) || misaligned(h0, 4) || misaligned(H_out, 4) || misaligned(p->state_last_out, 4) ||
+      misaligned(residual_out, 4))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const float* h0f = static_cast<const float*>(h0);
+  float* slast = static_cast<float*>(p->state_last_out);
+  if (p->T == 0) {
+    if (residual_out) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(residual_out, K + 1);
+    if (slast) {
+      const int64_t n = p->B * p->d_h;
+      prn::k_copy_or_zero<float><<<unsigned((n + 255) / 256), 256, 0, st>>>(h0f, slast, n);
+    }
+    return launched("prn_head_newton_forward");
+  }
+  const PlanHm pl = plan_hm(p, K);
+  if (!p->workspace || p->workspace_bytes < pl.total)
+    return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
+                p->workspace, pl.total);
+  if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+    return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  char* ws = static_cast<char*>(p->workspace);
+  float* iter[2] = {reinterpret_cast<float*>(ws + pl.iter_off),
+                    reinterpret_cast<float*>(ws + pl.iter_off + align_up(size_t(p->B) * p->T * p->d_h * 4))};
+  float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
+  float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
+  float* rpart = residual_out ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
+  const float* xp = static_cast<const float*>(xproj);
+  float* Hout = static_cast<float*>(H_out);
+  const dim3 grid(unsigned(pl.n_ch), unsigned(pl.n_heads), unsigned(p->B));
+  const dim3 sgrid(unsigned(pl.n_heads), unsigned(p->B));
+  const float* Hprev = nullptr;
+  for (int k = 0; k < K; ++k) {
+    float* Hk = (k == K - 1) ? Hout : iter[k % 2];
+    prn::k_hm_reduce<true><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, p->T, p->d_h, pl.n_ch, agg,
+                                                rpart ? rpart + k * pl.n_wg : nullptr);
+    prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
+    prn::k_hm_fix<<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, carry, p->T, p->d_h, pl.n_ch, Hk,
+                                       k == K - 1 ? slast : nullptr);
+    Hprev = Hk;
+  }
+  if (rpart) {
+    prn::k_hm_reduce<false><<<grid, 64, 0, st>>>(xp, A, h0f, Hout, p->T, p->d_h, pl.n_ch, nullptr,
+                                                 rpart + K * pl.n_wg);
+    prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, residual_out);
+  }
+  return launched("prn_head_newton_forward");
+}
+
+prn_status prn_head_sequential_forward(const void* xproj, const prn_params* p, const float* A, int32_t d_head,
+                                       const void* h0, void* H_out) {
+  Shape sh;
+  prn_status s = check_head(p, &sh, d_head);
+  if (s != PRN_OK) return s;
+  if (!A) return fail(PRN_ERR_INVALID_ARG, "the recurrent blocks A are NULL");
+  if (misaligned(A, 4)) return fail(PRN_ERR_INVALID_ARG, "A is not 4-byte aligned");
+  if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
+  if (misaligned(xproj, 4) || misaligned(h0, 4) || misaligned(H_out, 4) || misaligned(p->state_last_out, 4))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const dim3 sgrid(unsigned(p->d_h / prn::kHmD), unsigned(p->B));
+  prn::k_hm_sequential<<<sgrid, 64, 0, st>>>(static_cast<const float*>(xproj), A, static_cast<const float*>(h0),
+                                             p->T, p->d_h, static_cast<float*>(H_out),
+                                             static_cast<float*>(p->state_last_out));
+  return launched("prn_head_sequential_forward");
 }
 
 }  // extern "C"

@@ -195,3 +195,33 @@ def test_decode_step_rejects_bad_arguments_before_launch(kw, args, status):
     st = B.lib().prn_decode_step(a["x"], a["W"], a["bias"], ctypes.byref(p), a["si"], a["so"], a["h"])
     assert st == status, B.prn_last_error()
     assert B.prn_last_error()
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(cell=1, a=None), {}, B.PRN_ERR_UNSUPPORTED),                   # LSTM head-mix is not built
+    (dict(dtype=1, a=None), {}, B.PRN_ERR_UNSUPPORTED),                  # bf16 head-mix is not built
+    (dict(B=1, n_seqs=2, a=None), {}, B.PRN_ERR_UNSUPPORTED),            # no ragged pack for head-mix
+    (dict(a=None), dict(d_head=8), B.PRN_ERR_UNSUPPORTED),
+    (dict(a=None, d_h=24), {}, B.PRN_ERR_INVALID_ARG),                   # d_h not a multiple of d_head
+    (dict(a=None, d_h=32), dict(A=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=None, d_h=32), dict(K=0), B.PRN_ERR_INVALID_ARG),
+    (dict(a=None, d_h=32), dict(A=FAKE + 2), B.PRN_ERR_INVALID_ARG),
+    (dict(a=None, d_h=32), {}, B.PRN_ERR_WORKSPACE),                     # no workspace
+    (dict(a=None, d_h=32, states_out=FAKE), {}, B.PRN_ERR_UNSUPPORTED),
+])
+def test_head_newton_forward_rejects_bad_arguments_before_launch(kw, args, status):
+    p = _params(**kw)
+    a = dict(xproj=FAKE, A=FAKE, d_head=16, h0=None, K=3, H=FAKE, res=None)
+    a.update(args)
+    st = B.lib().prn_head_newton_forward(a["xproj"], ctypes.byref(p), a["A"], a["d_head"], a["h0"], a["K"], a["H"],
+                                         a["res"])
+    assert st == status, B.prn_last_error()
+    assert B.prn_last_error()
+
+
+def test_head_workspace_bytes():
+    w3 = B.prn_head_workspace_bytes(2, 1000, 64, 3)
+    w1 = B.prn_head_workspace_bytes(2, 1000, 64, 1)
+    assert w3 > w1 > 0 and w3 % 256 == 0
+    p = _params(d_h=64, dtype=1)
+    assert B.lib().prn_head_workspace_bytes(ctypes.byref(p), 16, 3) == 0 and B.prn_last_error()
