@@ -82,6 +82,60 @@ def profiled_traffic(kernel: str, workload: str):
         return None
 
 
+VALU_F32_PEAK_TFLOPS = 157.3
+
+
+def headmix_flops(Bn: int, T: int, d_h: int, K: int, d: int = 16) -> float:
+    """Arithmetic of the head-mix Newton forward per (step, head), counted as
+    2 flops per multiply-add: each iteration's chunk reduce applies J to the
+    running 16 x 16 map (three block products, 3 * 2 d^3) and to its vector
+    (three block matrix-vector products), and evaluates the gates (three
+    more); the fix-up evaluates the gates and applies J to a vector again;
+    the final residual pass evaluates the gates once more."""
+    mv = 2 * d * d
+    per_iter = 3 * 2 * d ** 3 + 3 * mv + 3 * mv + 3 * mv + 3 * mv
+    return float(Bn) * T * (d_h // d) * (K * per_iter + 3 * mv)
+
+
+def bench_headmix(torch, B, dev, steps: int, warmup: int, Bn: int = 8, T: int = 4096) -> dict:
+    """Head-mix GRU (16 x 16 blocks, 16 heads, d_h = 256), K = 3, at B x T:
+    the Newton forward and the unroll, timed with HIP events on the stream."""
+    d_h, K = 256, 3
+    g = torch.Generator(device=dev).manual_seed(4)
+    xp = torch.randn((Bn, T, 3, d_h), generator=g, device=dev)
+    A = (torch.rand((3, d_h // 16, 16, 16), generator=g, device=dev) - 0.5) / 4.0
+    H = torch.empty((Bn, T, d_h), device=dev)
+    res = torch.zeros(K + 1, device=dev)
+    ws = torch.empty(B.prn_head_workspace_bytes(Bn, T, d_h, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    t_n = timed(lambda: B.prn_head_newton_forward(xp, A, K, H, residual_out=res, workspace=ws, stream=stream))
+    Hs = torch.empty_like(H)
+    t_s = timed(lambda: B.prn_head_sequential_forward(xp, A, Hs, stream=stream))
+    ms = float(t_n.mean())
+    fl = headmix_flops(Bn, T, d_h, K)
+    return {"config": {"cell": "head-mix GRU", "B": Bn, "T": T, "d_h": d_h, "d_head": 16, "K": K},
+            "kernels": "k_hm_reduce + k_hm_scan + k_hm_fix per iteration (prn_head_newton_forward)",
+            "newton_ms_mean": ms, "newton_ms_min": float(t_n.min()), "tokens_per_s": Bn * T / (ms * 1e-3),
+            "sequential_ms_mean": float(t_s.mean()), "speedup_vs_unroll": float(t_s.mean()) / ms,
+            "max_abs_vs_unroll": float((H - Hs).abs().max()), "residual_K": float(res[-1]),
+            "roofline": {"bound": "alu", "achieved": fl / (ms * 1e-3) / 1e12, "peak": VALU_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / VALU_F32_PEAK_TFLOPS,
+                         "traffic": None, "algorithmic_flops": fl}}
+
+
 def proj_flops(w) -> float:
     return 2.0 * w.tokens * w.G * w.d_h * w.d_in
 
@@ -139,6 +193,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the T = 1 decode step")
+    ap.add_argument("--no-headmix", action="store_true", help="skip timing the head-mix GRU")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size reference for byte counters)")
@@ -323,6 +378,13 @@ def main() -> int:
                                "traffic": None, "algorithmic_bytes": dbytes}}
         print(f"[bench] decode timed ({n_calls} calls)", file=sys.stderr, flush=True)
 
+    headmix = None
+    if not args.no_headmix:
+        n = max(3, min(args.steps, 10))
+        # the GRU workload's shape, and one long sequence (few chains: the regime parallel Newton is for)
+        headmix = {"batch": bench_headmix(torch, B, dev, n, 2), "long": bench_headmix(torch, B, dev, n, 2, 1, 32768)}
+        print("[bench] head-mix timed", file=sys.stderr, flush=True)
+
     residuals = res.cpu().tolist()
     ms_step = wall * 1e3 / args.steps
     value = w.tokens / (wall / args.steps)
@@ -371,6 +433,7 @@ def main() -> int:
         "residuals": residuals,
         "backward": backward,
         "decode": decode,
+        "headmix": headmix,
         "device": torch.cuda.get_device_name(0),
         "hip_runtime": torch.version.hip,
     }

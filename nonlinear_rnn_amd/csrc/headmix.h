@@ -11,11 +11,15 @@
 // diag(delta) (A_r X)) for a vector or a 16 x 16 matrix X: three products
 // with the constant blocks.
 //
-// Lane layout (one wave per (row, head, chunk)): lane = 4 i + q holds
-// channel i of the head, and columns 4q..4q+3 of a 16 x 16 map.  Vectors are
-// held by all four lanes of a channel.  A matrix-vector product takes its
-// operand's four columns by shuffles and sums the row over the four lanes;
-// a matrix-matrix product reads the right operand from a 16 x 16 LDS tile.
+// Lane layouts (one wave per (row, head, chunk)).  Vectors: lane = 4 i + q
+// holds channel i of the head (all four lanes of a channel hold it); a
+// matrix-vector product takes its operand's four columns q by shuffles and
+// sums the row over the four lanes.  Maps: the chunk's running 16 x 16 map
+// lives in the output layout of v_mfma_f32_16x16x4_f32 (lane L holds rows
+// 4 (L / 16) .. + 3 of column L % 16).  A block product X M is four such
+// instructions; in instruction p lane L supplies X[L % 16][4 (L / 16) + p]
+// and M[4 (L / 16) + p][L % 16], which is M's own register p, so the
+// running map never moves between lanes.
 //
 // Schedule per Newton iteration k (three phases over chunks of kHmChunk
 // steps): k_hm_reduce linearises at H^(k-1) and composes each chunk's maps
@@ -29,24 +33,44 @@
 namespace prn {
 
 constexpr int kHmD = 16;       // d_head
-constexpr int kHmChunk = 64;   // steps per chunk
+constexpr int kHmChunk = 32;   // steps per chunk
+constexpr int kHmSeqBlock = 64;  // steps of inputs the unroll stages at a time
+
+typedef __attribute__((ext_vector_type(4))) float hm_f4;
 constexpr int kHmNC = kHmD * kHmD + kHmD;  // floats of one chunk aggregate (M row-major, then v)
 
 struct HmBlocks {
-  float row[3][kHmD];  // A_g[i][0..15]: the full row (matrix-matrix products)
-  float quad[3][4];    // A_g[i][4q..4q+3]: this lane's columns (matrix-vector products)
+  float quad[3][4];  // A_g[i][4q..4q+3]: this lane's columns (matrix-vector products)
+  float mf[3][4];    // A_g[L % 16][4 (L / 16) + p]: the operand of block-product instruction p
 };
 
-__device__ __forceinline__ void hm_load_blocks(const float* A, int64_t n_heads, int64_t head, int i, int q,
+__device__ __forceinline__ void hm_load_blocks(const float* A, int64_t n_heads, int64_t head, int lane,
                                                HmBlocks& blk) {
+  const int i = lane >> 2, q = lane & 3, mr = lane & 15, mk = 4 * (lane >> 4);
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
-    const float* base = A + ((g * n_heads + head) * kHmD + i) * kHmD;
+    const float* base = A + (g * n_heads + head) * kHmD * kHmD;
 #pragma unroll
-    for (int m = 0; m < kHmD; ++m) blk.row[g][m] = base[m];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) blk.quad[g][u] = base[4 * q + u];
+    for (int u = 0; u < 4; ++u) {
+      blk.quad[g][u] = base[i * kHmD + 4 * q + u];
+      blk.mf[g][u] = base[mr * kHmD + mk + u];
+    }
   }
+}
+
+// X M for the constant block X (operands xm) and M in the product layout
+__device__ __forceinline__ hm_f4 hm_blockmul(const float* xm, const hm_f4& m) {
+  hm_f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xm[p], m[p], acc, 0, 0, 0);
+  return acc;
+}
+
+// a per-channel vector (vector layout) read at rows 4 (L / 16) + r
+__device__ __forceinline__ hm_f4 hm_rows(float c, int lane) {
+  const int r0 = 4 * (lane >> 4);
+  return {__shfl(c, 4 * (r0 + 0), kWave), __shfl(c, 4 * (r0 + 1), kWave), __shfl(c, 4 * (r0 + 2), kWave),
+          __shfl(c, 4 * (r0 + 3), kWave)};
 }
 
 // sum over the four lanes of a channel
@@ -62,20 +86,6 @@ __device__ __forceinline__ float hm_matvec(const float* aq, float v, int q) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) s = fmaf(aq[u], __shfl(v, 4 * (4 * q + u), kWave), s);
   return hm_rowsum(s);
-}
-
-// (A X)[i][4q..4q+3] with X in LDS (row-major 16 x 16)
-__device__ __forceinline__ void hm_matmat(const float* arow, const float* X, int q, float* out) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) out[c] = 0.0f;
-#pragma unroll
-  for (int m = 0; m < kHmD; ++m) {
-    const float4 x = *reinterpret_cast<const float4*>(X + m * kHmD + 4 * q);
-    out[0] = fmaf(arow[m], x.x, out[0]);
-    out[1] = fmaf(arow[m], x.y, out[1]);
-    out[2] = fmaf(arow[m], x.z, out[2]);
-    out[3] = fmaf(arow[m], x.w, out[3]);
-  }
 }
 
 // one cell evaluation at h (the channel's previous state) with inputs x[3]:
@@ -109,20 +119,34 @@ __device__ __forceinline__ float hm_jvec(const HmBlocks& blk, const HmLin& l, fl
   return fmaf(l.gamma, y2, fmaf(l.beta, y3, l.alpha * d));
 }
 
-// inputs of step t for channel ch: x_z, x_r, x_c
-__device__ __forceinline__ void hm_load_x(const float* xproj, int64_t b, int64_t t, int64_t T, int64_t d_h,
-                                          int64_t ch, float* x) {
-  const float* p = xproj + ((b * T + t) * 3) * d_h + ch;
-#pragma unroll
-  for (int g = 0; g < 3; ++g) x[g] = p[g * d_h];
-}
-
-// previous state of step t under the iterate Hprev (zero iterate if null),
-// h0 (zero if null) at t = 0
-__device__ __forceinline__ float hm_prev(const float* Hprev, const float* h0, int64_t b, int64_t t, int64_t T,
-                                         int64_t d_h, int64_t ch) {
-  if (t == 0) return h0 ? h0[b * d_h + ch] : 0.0f;
-  return Hprev ? Hprev[(b * T + t - 1) * d_h + ch] : 0.0f;
+// The chunk's inputs and previous-iterate states staged in LDS with all
+// loads in flight at once (a load per step would put a memory round trip
+// on every step of the serial chain): xs[j][g][i] = x_g of step t0 + j,
+// hs[j][i] = the state before step t0 + j under Hprev (hs[0]: h0 at t = 0),
+// hs[n][i] = Hprev at the chunk's last step.
+struct HmStage {
+  float xs[kHmChunk][3][kHmD];
+  float hs[kHmChunk + 1][kHmD];
+};
+__device__ __forceinline__ void hm_stage(HmStage& sm, const float* xproj, const float* Hprev, const float* h0,
+                                         int64_t b, int64_t head, int64_t t0, int n, int64_t T, int64_t d_h,
+                                         int lane) {
+  const float* xb = xproj + ((b * T + t0) * 3) * d_h + head * kHmD;
+#pragma unroll 8
+  for (int e = lane; e < n * 3 * kHmD; e += kWave) {
+    const int j = e / (3 * kHmD), r = e - j * 3 * kHmD, g = r / kHmD, i = r - g * kHmD;
+    sm.xs[j][g][i] = xb[(static_cast<int64_t>(j) * 3 + g) * d_h + i];
+  }
+#pragma unroll 4
+  for (int e = lane; e < (n + 1) * kHmD; e += kWave) {
+    const int j = e / kHmD, i = e - j * kHmD;
+    const int64_t t = t0 + j - 1;  // the step whose state this is
+    float v = 0.0f;
+    if (t < 0) v = h0 ? h0[b * d_h + head * kHmD + i] : 0.0f;
+    else if (Hprev) v = Hprev[(b * T + t) * d_h + head * kHmD + i];
+    sm.hs[j][i] = v;
+  }
+  __syncthreads();
 }
 
 // Phase 1 (COMPOSE) or the residual pass (!COMPOSE): linearise every step
@@ -137,51 +161,51 @@ k_hm_reduce(const float* __restrict__ xproj, const float* __restrict__ A, const 
   const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
   const int64_t chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int64_t n_heads = gridDim.y;
-  const int64_t ch = head * kHmD + i;
-  __shared__ __attribute__((aligned(16))) float Mt[kHmD * kHmD];
-  __shared__ __attribute__((aligned(16))) float Wt[kHmD * kHmD];
+  __shared__ HmStage sm;
   HmBlocks blk;
-  hm_load_blocks(A, n_heads, head, i, q, blk);
-  const int64_t t0 = chunk * kHmChunk, t1 = imin(T, t0 + kHmChunk);
-  float M[4], v = 0.0f;
+  hm_load_blocks(A, n_heads, head, lane, blk);
+  const int64_t t0 = chunk * kHmChunk;
+  const int n = static_cast<int>(imin(T - t0, kHmChunk));
+  hm_stage(sm, xproj, Hprev, h0, b, head, t0, n, T, d_h, lane);
+  const int mr = lane & 15, mk = 4 * (lane >> 4);  // product layout: rows mk..mk+3 of column mr
+  hm_f4 M;
+  float v = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) M[c] = (4 * q + c == i) ? 1.0f : 0.0f;
+  for (int r = 0; r < 4; ++r) M[r] = (mk + r == mr) ? 1.0f : 0.0f;
   unsigned rmax = 0;
-  for (int64_t t = t0; t < t1; ++t) {
-    float x[3];
-    hm_load_x(xproj, b, t, T, d_h, ch, x);
-    const float prev = hm_prev(Hprev, h0, b, t, T, d_h, ch);
-    const float cur = Hprev ? Hprev[(b * T + t) * d_h + ch] : 0.0f;
+  for (int j = 0; j < n; ++j) {
+    const int64_t t = t0 + j;
+    const float x[3] = {sm.xs[j][0][i], sm.xs[j][1][i], sm.xs[j][2][i]};
+    const float prev = sm.hs[j][i];
+    const float cur = sm.hs[j + 1][i];
     const HmLin l = hm_linearise(blk, x, prev, q);
     rmax = rmax_bits(rmax, cur - l.fv);
     if constexpr (COMPOSE) {
       if (t == 0) {  // the sequence's first step: J = 0
 #pragma unroll
-        for (int c = 0; c < 4; ++c) M[c] = 0.0f;
+        for (int r = 0; r < 4; ++r) M[r] = 0.0f;
         v = l.fv;
       } else {
-        // M <- J M
+        // M <- J M = alpha M + beta (A_z M) + gamma A_c (rho M + delta (A_r M))
+        const hm_f4 y3 = hm_blockmul(blk.mf[0], M);
+        const hm_f4 y1 = hm_blockmul(blk.mf[1], M);
+        const hm_f4 rho = hm_rows(l.rho, lane), del = hm_rows(l.delta, lane);
+        hm_f4 W;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) Mt[i * kHmD + 4 * q + c] = M[c];
-        __syncthreads();
-        float y3[4], y1[4], y2[4];
-        hm_matmat(blk.row[0], Mt, q, y3);
-        hm_matmat(blk.row[1], Mt, q, y1);
+        for (int r = 0; r < 4; ++r) W[r] = fmaf(del[r], y1[r], rho[r] * M[r]);
+        const hm_f4 y2 = hm_blockmul(blk.mf[2], W);
+        const hm_f4 al = hm_rows(l.alpha, lane), be = hm_rows(l.beta, lane), ga = hm_rows(l.gamma, lane);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) Wt[i * kHmD + 4 * q + c] = fmaf(l.delta, y1[c], l.rho * M[c]);
-        __syncthreads();
-        hm_matmat(blk.row[2], Wt, q, y2);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) M[c] = fmaf(l.gamma, y2[c], fmaf(l.beta, y3[c], l.alpha * M[c]));
+        for (int r = 0; r < 4; ++r) M[r] = fmaf(ga[r], y2[r], fmaf(be[r], y3[r], al[r] * M[r]));
         // v <- J v + f - J prev = f + J (v - prev)
         v = l.fv + hm_jvec(blk, l, v - prev, q);
-        __syncthreads();  // Mt and Wt are rewritten at the next step
       }
     }
   }
   if constexpr (COMPOSE) {
     float* out = agg + ((b * n_heads + head) * n_ch + chunk) * kHmNC;
-    *reinterpret_cast<float4*>(out + i * kHmD + 4 * q) = make_float4(M[0], M[1], M[2], M[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(mk + r) * kHmD + mr] = M[r];
     if (q == 0) out[kHmD * kHmD + i] = v;
   }
   if (rpart) {
@@ -236,19 +260,22 @@ k_hm_fix(const float* __restrict__ xproj, const float* __restrict__ A, const flo
   const int64_t chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int64_t n_heads = gridDim.y;
   const int64_t ch = head * kHmD + i;
+  __shared__ HmStage sm;
   HmBlocks blk;
-  hm_load_blocks(A, n_heads, head, i, q, blk);
-  const int64_t t0 = chunk * kHmChunk, t1 = imin(T, t0 + kHmChunk);
+  hm_load_blocks(A, n_heads, head, lane, blk);
+  const int64_t t0 = chunk * kHmChunk;
+  const int n = static_cast<int>(imin(T - t0, kHmChunk));
+  hm_stage(sm, xproj, Hprev, h0, b, head, t0, n, T, d_h, lane);
   float s = carry[((b * n_heads + head) * n_ch + chunk) * kHmD + i];
-  for (int64_t t = t0; t < t1; ++t) {
-    float x[3];
-    hm_load_x(xproj, b, t, T, d_h, ch, x);
-    const float prev = hm_prev(Hprev, h0, b, t, T, d_h, ch);
+  for (int j = 0; j < n; ++j) {
+    const int64_t t = t0 + j;
+    const float x[3] = {sm.xs[j][0][i], sm.xs[j][1][i], sm.xs[j][2][i]};
+    const float prev = sm.hs[j][i];
     const HmLin l = hm_linearise(blk, x, prev, q);
     s = (t == 0) ? l.fv : l.fv + hm_jvec(blk, l, s - prev, q);
     if (q == 0) Hout[(b * T + t) * d_h + ch] = s;
   }
-  if (slast && t1 == T && q == 0) slast[b * d_h + ch] = s;
+  if (slast && t0 + n == T && q == 0) slast[b * d_h + ch] = s;
 }
 
 // The sequential unroll: one wave per (row, head), h_t = f(h_(t-1), x_t).
@@ -258,14 +285,26 @@ k_hm_sequential(const float* __restrict__ xproj, const float* __restrict__ A, co
   const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
   const int64_t head = blockIdx.x, b = blockIdx.y, n_heads = gridDim.x;
   const int64_t ch = head * kHmD + i;
+  __shared__ float xs[kHmSeqBlock][3][kHmD];
   HmBlocks blk;
-  hm_load_blocks(A, n_heads, head, i, q, blk);
+  hm_load_blocks(A, n_heads, head, lane, blk);
   float h = h0 ? h0[b * d_h + ch] : 0.0f;
-  for (int64_t t = 0; t < T; ++t) {
-    float x[3];
-    hm_load_x(xproj, b, t, T, d_h, ch, x);
-    h = hm_linearise(blk, x, h, q).fv;
-    if (q == 0) Hout[(b * T + t) * d_h + ch] = h;
+  for (int64_t t0 = 0; t0 < T; t0 += kHmSeqBlock) {
+    // the next block's inputs, all loads in flight at once
+    const int n = static_cast<int>(imin(T - t0, kHmSeqBlock));
+    const float* xb = xproj + ((b * T + t0) * 3) * d_h + head * kHmD;
+    __syncthreads();  // the previous block's reads are done
+#pragma unroll 8
+    for (int e = lane; e < n * 3 * kHmD; e += kWave) {
+      const int j = e / (3 * kHmD), r = e - j * 3 * kHmD, g = r / kHmD, c = r - g * kHmD;
+      xs[j][g][c] = xb[(static_cast<int64_t>(j) * 3 + g) * d_h + c];
+    }
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      const float x[3] = {xs[j][0][i], xs[j][1][i], xs[j][2][i]};
+      h = hm_linearise(blk, x, h, q).fv;
+      if (q == 0) Hout[(b * T + t0 + j) * d_h + ch] = h;
+    }
   }
   if (slast && q == 0) slast[b * d_h + ch] = h;
 }
