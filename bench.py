@@ -49,14 +49,21 @@ def algorithmic_backward_bytes(w) -> float:
     return float(w.tokens) * w.d_h * (2 * w.G + w.S + 1) * elt
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; a profile taken from other sources is stale."""
-    import glob
+# the sources each profiled kernel is built and launched from
+KERNEL_SOURCES = {
+    "k_newton_sp": ["prn_device.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
+    "k_bw_sp": ["prn_device.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
+    "k_proj": ["proj.h", "proj.hip"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the HIP sources a kernel is built from; a profile taken from other sources is stale."""
     import hashlib
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "nonlinear_rnn_amd", "csrc", "*"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "nonlinear_rnn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -74,7 +81,7 @@ def profiled_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_hash") != kernel_source_hash():
+    if fields.get("source_hash") != kernel_source_hash(kernel):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"].split()[0])
