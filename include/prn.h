@@ -214,9 +214,10 @@ prn_status prn_decode_step(const void* x, const void* W, const float* bias, cons
  * Newton as for the diagonal cells, with dense Jacobian blocks per head.
  *   A          (3, n_heads, d_head, d_head) fp32, gate order z, r, c; A[g][k][i][j]
  *              multiplies channel j of head k into channel i (row-major blocks)
- *   xproj      (B, T, 3, d_h) fp32, as for the diagonal GRU
- *   h0         (B, d_h) fp32 or NULL (zeros)
- *   H_out      (B, T, d_h) fp32
+ *   xproj      (B, T, 3, d_h) fp32, as for the diagonal GRU; 16-byte aligned
+ *   h0         (B, d_h) fp32 or NULL (zeros); 16-byte aligned
+ *   H_out      (B, T, d_h) fp32; 16-byte aligned (the Newton forward reads
+ *              and writes it in 4-channel vectors)
  * params: cell = PRN_CELL_DIAG_GRU, dtype = PRN_F32, B, T, d_h, n_seqs = 0,
  * state_last_out ((B, d_h) or NULL), workspace, stream; a, states_out and
  * picard_iters are not used (states_out / picard_iters must be 0).

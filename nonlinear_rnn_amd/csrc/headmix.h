@@ -22,10 +22,11 @@
 // running map never moves between lanes.
 //
 // Schedule per Newton iteration k (three phases over chunks of kHmChunk
-// steps): k_hm_reduce linearises at H^(k-1) and composes each chunk's maps
-// (and reduces r_(k-1) on the way); k_hm_scan carries across the chunks of
-// one (row, head) serially; k_hm_fix replays each chunk from its carry and
-// writes H^(k).  A last k_hm_reduce without composition gives r_K.
+// steps): k_hm_pass<kHmReduce> linearises at H^(k-1) and composes each
+// chunk's maps (and reduces r_(k-1) on the way); k_hm_scan carries across
+// the chunks of one (row, head) serially; k_hm_pass<kHmFix> replays each
+// chunk from its carry and writes H^(k).  A last k_hm_pass<kHmResidual>
+// gives r_K.
 #pragma once
 
 #include "newton_kernels.h"
@@ -119,96 +120,173 @@ __device__ __forceinline__ float hm_jvec(const HmBlocks& blk, const HmLin& l, fl
   return fmaf(l.gamma, y2, fmaf(l.beta, y3, l.alpha * d));
 }
 
-// The chunk's inputs and previous-iterate states staged in LDS with all
-// loads in flight at once (a load per step would put a memory round trip
-// on every step of the serial chain): xs[j][g][i] = x_g of step t0 + j,
-// hs[j][i] = the state before step t0 + j under Hprev (hs[0]: h0 at t = 0),
-// hs[n][i] = Hprev at the chunk's last step.
-struct HmStage {
-  float xs[kHmChunk][3][kHmD];
-  float hs[kHmChunk + 1][kHmD];
+// ---- the Newton passes over one chunk of one (row, head) ----
+//
+// Phase A, per block of 16 steps: the linearisation of every step is
+// independent (the previous states come from the previous iterate), so the
+// gate pre-activations of the block are block products too: with P the
+// 16 x 16 matrix of previous states (channels x steps) in the product
+// layout, U_z = A_z P, U_r = A_r P and U_c = A_c (R * P) are four
+// matrix-core instructions each, and the per-(channel, step) coefficients
+// f, alpha, beta, gamma, rho, delta (and P itself) go to LDS as
+// [coefficient][step][channel].  The residual max |H_t - f_t| is reduced
+// here.  Phase B walks the block's steps serially: the chunk map
+// M <- J M on the matrix cores (rows of the coefficients read back as
+// 16-byte LDS words), and the vector chain d <- f + J (d - prev) in the
+// vector layout, whose matrix-vector products read their operand from a
+// 16-float LDS vector (one 16-byte read per lane) instead of shuffles.
+enum HmMode { kHmReduce = 0, kHmFix = 1, kHmResidual = 2 };
+constexpr int kHmBlk = 16;  // steps per block of phase A
+enum { kCf = 0, kCalpha, kCbeta, kCgamma, kCrho, kCdelta, kCprev, kNCoef };
+
+struct HmShared {
+  __attribute__((aligned(16))) float cf[kNCoef][kHmBlk][kHmD];
+  __attribute__((aligned(16))) float dv[kHmD];
+  __attribute__((aligned(16))) float wv[kHmD];
 };
-__device__ __forceinline__ void hm_stage(HmStage& sm, const float* xproj, const float* Hprev, const float* h0,
-                                         int64_t b, int64_t head, int64_t t0, int n, int64_t T, int64_t d_h,
-                                         int lane) {
-  const float* xb = xproj + ((b * T + t0) * 3) * d_h + head * kHmD;
-#pragma unroll 8
-  for (int e = lane; e < n * 3 * kHmD; e += kWave) {
-    const int j = e / (3 * kHmD), r = e - j * 3 * kHmD, g = r / kHmD, i = r - g * kHmD;
-    sm.xs[j][g][i] = xb[(static_cast<int64_t>(j) * 3 + g) * d_h + i];
+
+__device__ __forceinline__ hm_f4 hm_ld4(const float* p) { return *reinterpret_cast<const hm_f4*>(p); }
+
+// phase A for steps jb .. jb + 15 of the chunk (lane L: step jb + L % 16,
+// channels 4 (L / 16) .. + 3 of the head); steps at or past n are computed
+// on clamped inputs and ignored
+template <bool RES>
+__device__ __forceinline__ void hm_phase_a(const HmBlocks& blk, const float* xproj, const float* Hprev,
+                                           const float* h0, int64_t b, int64_t head, int64_t t0, int jb, int n,
+                                           int64_t T, int64_t d_h, int lane, HmShared& sh, unsigned& rmax) {
+  const int col = lane & 15, mk = 4 * (lane >> 4);
+  const int j = jb + col;
+  const bool valid = j < n;
+  const int64_t t = t0 + (valid ? j : n - 1);
+  const int64_t c0 = head * kHmD + mk;
+  const float* xp = xproj + ((b * T + t) * 3) * d_h + c0;
+  const hm_f4 xz = hm_ld4(xp), xr = hm_ld4(xp + d_h), xc = hm_ld4(xp + 2 * d_h);
+  hm_f4 P = {0.0f, 0.0f, 0.0f, 0.0f}, cur = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (Hprev) {
+    cur = hm_ld4(Hprev + (b * T + t) * d_h + c0);
+    if (t > 0) P = hm_ld4(Hprev + (b * T + t - 1) * d_h + c0);
   }
-#pragma unroll 4
-  for (int e = lane; e < (n + 1) * kHmD; e += kWave) {
-    const int j = e / kHmD, i = e - j * kHmD;
-    const int64_t t = t0 + j - 1;  // the step whose state this is
-    float v = 0.0f;
-    if (t < 0) v = h0 ? h0[b * d_h + head * kHmD + i] : 0.0f;
-    else if (Hprev) v = Hprev[(b * T + t) * d_h + head * kHmD + i];
-    sm.hs[j][i] = v;
+  if (t == 0 && h0) P = hm_ld4(h0 + b * d_h + c0);
+  else if (t == 0) P = hm_f4{0.0f, 0.0f, 0.0f, 0.0f};
+  const hm_f4 uz = hm_blockmul(blk.mf[0], P), ur = hm_blockmul(blk.mf[1], P);
+  hm_f4 z, rr, rh;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    z[r] = sig_s(kSigScale * (xz[r] + uz[r]));
+    rr[r] = sig_s(kSigScale * (xr[r] + ur[r]));
+    rh[r] = rr[r] * P[r];
   }
-  __syncthreads();
+  const hm_f4 uc = hm_blockmul(blk.mf[2], rh);
+  hm_f4 fv, al, be, ga, de;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float c = tanh_s(kTanhScale * (xc[r] + uc[r]));
+    fv[r] = fmaf(z[r], c - P[r], P[r]);
+    al[r] = 1.0f - z[r];
+    be[r] = (c - P[r]) * z[r] * (1.0f - z[r]);
+    ga[r] = z[r] * fmaf(-c, c, 1.0f);
+    de[r] = P[r] * rr[r] * (1.0f - rr[r]);
+    if (RES && valid) rmax = rmax_bits(rmax, cur[r] - fv[r]);
+  }
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCf][col][mk]) = fv;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCalpha][col][mk]) = al;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCbeta][col][mk]) = be;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCgamma][col][mk]) = ga;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCrho][col][mk]) = rr;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCdelta][col][mk]) = de;
+  *reinterpret_cast<hm_f4*>(&sh.cf[kCprev][col][mk]) = P;
 }
 
-// Phase 1 (COMPOSE) or the residual pass (!COMPOSE): linearise every step
-// of the chunk at Hprev; r = max |Hprev_t - f(prev_t)| (Hprev = 0 when null);
-// with COMPOSE also the chunk aggregate (M, v) of the maps
-// h -> J_t h + f_t - J_t prev_t, J_0 := 0.
-template <bool COMPOSE>
+// sum_u a[u] * x[4q + u] over the channel's four lanes, x a 16-float LDS vector
+__device__ __forceinline__ float hm_matvec_lds(const float* aq, const float* x, int q) {
+  const hm_f4 v = hm_ld4(x + 4 * q);
+  return hm_rowsum(fmaf(aq[3], v[3], fmaf(aq[2], v[2], fmaf(aq[1], v[1], aq[0] * v[0]))));
+}
+
+// one step of the vector chain, vector layout (channel i = L / 4):
+// returns f + J (d - prev) for step s of the block
+__device__ __forceinline__ float hm_chain_step(const HmBlocks& blk, HmShared& sh, int s, float d, int i, int q) {
+  const float dl = d - sh.cf[kCprev][s][i];
+  if (q == 0) sh.dv[i] = dl;
+  __syncthreads();
+  const float y3 = hm_matvec_lds(blk.quad[0], sh.dv, q);
+  const float y1 = hm_matvec_lds(blk.quad[1], sh.dv, q);
+  const float w = fmaf(sh.cf[kCdelta][s][i], y1, sh.cf[kCrho][s][i] * dl);
+  if (q == 0) sh.wv[i] = w;
+  __syncthreads();
+  const float y2 = hm_matvec_lds(blk.quad[2], sh.wv, q);
+  return sh.cf[kCf][s][i] +
+         fmaf(sh.cf[kCgamma][s][i], y2, fmaf(sh.cf[kCbeta][s][i], y3, sh.cf[kCalpha][s][i] * dl));
+}
+
+// kHmReduce: compose the chunk's maps (M, v) into agg, and reduce r_(k-1)
+//   (max |Hprev_t - f_t|, Hprev = 0 when null) into rpart;
+// kHmFix: replay the chunk from its carry, H_t = f_t + J_t (H_(t-1) -
+//   prev_t), into Hout (and the row's final state into slast);
+// kHmResidual: only the residual of Hprev.
+// J_0 := 0 (the map of a sequence's first step is constant, f_0).
+template <int MODE>
 __global__ void __launch_bounds__(kWave)
-k_hm_reduce(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
-            const float* __restrict__ Hprev, int64_t T, int64_t d_h, int64_t n_ch, float* __restrict__ agg,
-            float* __restrict__ rpart) {
+k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
+          const float* __restrict__ Hprev, const float* __restrict__ carry, int64_t T, int64_t d_h, int64_t n_ch,
+          float* __restrict__ agg, float* __restrict__ rpart, float* __restrict__ Hout, float* __restrict__ slast) {
   const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
+  const int mr = lane & 15, mk = 4 * (lane >> 4);  // product layout: rows mk..mk+3 of column mr
   const int64_t chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int64_t n_heads = gridDim.y;
-  __shared__ HmStage sm;
+  __shared__ HmShared sh;
   HmBlocks blk;
   hm_load_blocks(A, n_heads, head, lane, blk);
   const int64_t t0 = chunk * kHmChunk;
   const int n = static_cast<int>(imin(T - t0, kHmChunk));
-  hm_stage(sm, xproj, Hprev, h0, b, head, t0, n, T, d_h, lane);
-  const int mr = lane & 15, mk = 4 * (lane >> 4);  // product layout: rows mk..mk+3 of column mr
   hm_f4 M;
-  float v = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) M[r] = (mk + r == mr) ? 1.0f : 0.0f;
+  float d = 0.0f;  // kHmReduce: the map's offset v; kHmFix: the state
+  if (MODE == kHmFix) d = carry[((b * n_heads + head) * n_ch + chunk) * kHmD + i];
   unsigned rmax = 0;
-  for (int j = 0; j < n; ++j) {
-    const int64_t t = t0 + j;
-    const float x[3] = {sm.xs[j][0][i], sm.xs[j][1][i], sm.xs[j][2][i]};
-    const float prev = sm.hs[j][i];
-    const float cur = sm.hs[j + 1][i];
-    const HmLin l = hm_linearise(blk, x, prev, q);
-    rmax = rmax_bits(rmax, cur - l.fv);
-    if constexpr (COMPOSE) {
-      if (t == 0) {  // the sequence's first step: J = 0
+  for (int jb = 0; jb < n; jb += kHmBlk) {
+    hm_phase_a<MODE != kHmFix>(blk, xproj, Hprev, h0, b, head, t0, jb, n, T, d_h, lane, sh, rmax);
+    __syncthreads();
+    if constexpr (MODE != kHmResidual) {
+      const int nb = static_cast<int>(imin(n - jb, kHmBlk));
+      for (int s = 0; s < nb; ++s) {
+        if (t0 + jb + s == 0) {  // the sequence's first step: J = 0
+          if constexpr (MODE == kHmReduce) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) M[r] = 0.0f;
-        v = l.fv;
-      } else {
-        // M <- J M = alpha M + beta (A_z M) + gamma A_c (rho M + delta (A_r M))
-        const hm_f4 y3 = hm_blockmul(blk.mf[0], M);
-        const hm_f4 y1 = hm_blockmul(blk.mf[1], M);
-        const hm_f4 rho = hm_rows(l.rho, lane), del = hm_rows(l.delta, lane);
-        hm_f4 W;
+            for (int r = 0; r < 4; ++r) M[r] = 0.0f;
+          }
+          d = sh.cf[kCf][s][i];
+        } else {
+          if constexpr (MODE == kHmReduce) {
+            // M <- J M = alpha M + beta (A_z M) + gamma A_c (rho M + delta (A_r M))
+            const hm_f4 y3 = hm_blockmul(blk.mf[0], M);
+            const hm_f4 y1 = hm_blockmul(blk.mf[1], M);
+            const hm_f4 rho = hm_ld4(&sh.cf[kCrho][s][mk]), del = hm_ld4(&sh.cf[kCdelta][s][mk]);
+            hm_f4 W;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) W[r] = fmaf(del[r], y1[r], rho[r] * M[r]);
-        const hm_f4 y2 = hm_blockmul(blk.mf[2], W);
-        const hm_f4 al = hm_rows(l.alpha, lane), be = hm_rows(l.beta, lane), ga = hm_rows(l.gamma, lane);
+            for (int r = 0; r < 4; ++r) W[r] = fmaf(del[r], y1[r], rho[r] * M[r]);
+            const hm_f4 y2 = hm_blockmul(blk.mf[2], W);
+            const hm_f4 al = hm_ld4(&sh.cf[kCalpha][s][mk]), be = hm_ld4(&sh.cf[kCbeta][s][mk]),
+                        ga = hm_ld4(&sh.cf[kCgamma][s][mk]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) M[r] = fmaf(ga[r], y2[r], fmaf(be[r], y3[r], al[r] * M[r]));
-        // v <- J v + f - J prev = f + J (v - prev)
-        v = l.fv + hm_jvec(blk, l, v - prev, q);
+            for (int r = 0; r < 4; ++r) M[r] = fmaf(ga[r], y2[r], fmaf(be[r], y3[r], al[r] * M[r]));
+          }
+          d = hm_chain_step(blk, sh, s, d, i, q);
+        }
+        if (MODE == kHmFix && q == 0) Hout[(b * T + t0 + jb + s) * d_h + head * kHmD + i] = d;
       }
     }
+    __syncthreads();  // the coefficients are rewritten by the next block
   }
-  if constexpr (COMPOSE) {
+  if constexpr (MODE == kHmReduce) {
     float* out = agg + ((b * n_heads + head) * n_ch + chunk) * kHmNC;
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[(mk + r) * kHmD + mr] = M[r];
-    if (q == 0) out[kHmD * kHmD + i] = v;
+    if (q == 0) out[kHmD * kHmD + i] = d;
   }
-  if (rpart) {
+  if (MODE == kHmFix && slast && t0 + n == T && q == 0) slast[b * d_h + head * kHmD + i] = d;
+  if (MODE != kHmFix && rpart) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, kWave)));
     if (lane == 0) rpart[(b * n_heads + head) * n_ch + chunk] = rmax_finish(rmax);
@@ -247,35 +325,6 @@ k_hm_scan(const float* __restrict__ agg, int64_t n_ch, float* __restrict__ carry
       }
     }
   }
-}
-
-// Phase 3: replay each chunk from its carry with the maps of the old
-// linearisation point Hprev: H_t = f_t + J_t (H_(t-1) - prev_t) (H_0 = f_0),
-// written to Hout; the final state of each row to slast at the last step.
-__global__ void __launch_bounds__(kWave)
-k_hm_fix(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
-         const float* __restrict__ Hprev, const float* __restrict__ carry, int64_t T, int64_t d_h, int64_t n_ch,
-         float* __restrict__ Hout, float* __restrict__ slast) {
-  const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
-  const int64_t chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-  const int64_t n_heads = gridDim.y;
-  const int64_t ch = head * kHmD + i;
-  __shared__ HmStage sm;
-  HmBlocks blk;
-  hm_load_blocks(A, n_heads, head, lane, blk);
-  const int64_t t0 = chunk * kHmChunk;
-  const int n = static_cast<int>(imin(T - t0, kHmChunk));
-  hm_stage(sm, xproj, Hprev, h0, b, head, t0, n, T, d_h, lane);
-  float s = carry[((b * n_heads + head) * n_ch + chunk) * kHmD + i];
-  for (int j = 0; j < n; ++j) {
-    const int64_t t = t0 + j;
-    const float x[3] = {sm.xs[j][0][i], sm.xs[j][1][i], sm.xs[j][2][i]};
-    const float prev = sm.hs[j][i];
-    const HmLin l = hm_linearise(blk, x, prev, q);
-    s = (t == 0) ? l.fv : l.fv + hm_jvec(blk, l, s - prev, q);
-    if (q == 0) Hout[(b * T + t) * d_h + ch] = s;
-  }
-  if (slast && t0 + n == T && q == 0) slast[b * d_h + ch] = s;
 }
 
 // The sequential unroll: one wave per (row, head), h_t = f(h_(t-1), x_t).

@@ -702,8 +702,9 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
   if (misaligned(A, 4)) return fail(PRN_ERR_INVALID_ARG, "A is not 4-byte aligned");
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
   if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
-  if (misaligned(xproj, 4) || misaligned(h0, 4) || misaligned(H_out, 4) || misaligned(p->state_last_out, 4) ||
-      misaligned(residual_out, 4))
+  if (misaligned(xproj, 16) || misaligned(h0, 16) || misaligned(H_out, 16))
+    return fail(PRN_ERR_INVALID_ARG, "xproj, h0 and H_out must be 16-byte aligned (4-channel vector loads)");
+  if (misaligned(p->state_last_out, 4) || misaligned(residual_out, 4))
     return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   const float* h0f = static_cast<const float*>(h0);
@@ -735,16 +736,16 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
   const float* Hprev = nullptr;
   for (int k = 0; k < K; ++k) {
     float* Hk = (k == K - 1) ? Hout : iter[k % 2];
-    prn::k_hm_reduce<true><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, p->T, p->d_h, pl.n_ch, agg,
-                                                rpart ? rpart + k * pl.n_wg : nullptr);
+    prn::k_hm_pass<prn::kHmReduce><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, nullptr, p->T, p->d_h, pl.n_ch, agg,
+                                                        rpart ? rpart + k * pl.n_wg : nullptr, nullptr, nullptr);
     prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
-    prn::k_hm_fix<<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, carry, p->T, p->d_h, pl.n_ch, Hk,
-                                       k == K - 1 ? slast : nullptr);
+    prn::k_hm_pass<prn::kHmFix><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, carry, p->T, p->d_h, pl.n_ch, nullptr,
+                                                     nullptr, Hk, k == K - 1 ? slast : nullptr);
     Hprev = Hk;
   }
   if (rpart) {
-    prn::k_hm_reduce<false><<<grid, 64, 0, st>>>(xp, A, h0f, Hout, p->T, p->d_h, pl.n_ch, nullptr,
-                                                 rpart + K * pl.n_wg);
+    prn::k_hm_pass<prn::kHmResidual><<<grid, 64, 0, st>>>(xp, A, h0f, Hout, nullptr, p->T, p->d_h, pl.n_ch,
+                                                          nullptr, rpart + K * pl.n_wg, nullptr, nullptr);
     prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, residual_out);
   }
   return launched("prn_head_newton_forward");
