@@ -67,13 +67,6 @@ __device__ __forceinline__ hm_f4 hm_blockmul(const float* xm, const hm_f4& m) {
   return acc;
 }
 
-// a per-channel vector (vector layout) read at rows 4 (L / 16) + r
-__device__ __forceinline__ hm_f4 hm_rows(float c, int lane) {
-  const int r0 = 4 * (lane >> 4);
-  return {__shfl(c, 4 * (r0 + 0), kWave), __shfl(c, 4 * (r0 + 1), kWave), __shfl(c, 4 * (r0 + 2), kWave),
-          __shfl(c, 4 * (r0 + 3), kWave)};
-}
-
 // sum over the four lanes of a channel
 __device__ __forceinline__ float hm_rowsum(float x) {
   x += __shfl_xor(x, 1, kWave);
@@ -89,35 +82,12 @@ __device__ __forceinline__ float hm_matvec(const float* aq, float v, int q) {
   return hm_rowsum(s);
 }
 
-// one cell evaluation at h (the channel's previous state) with inputs x[3]:
-// f and the Jacobian's per-channel coefficients
-struct HmLin {
-  float fv, alpha, beta, gamma, rho, delta;
-};
-__device__ __forceinline__ HmLin hm_linearise(const HmBlocks& blk, const float* x, float h, int q) {
-  const float uz = x[0] + hm_matvec(blk.quad[0], h, q);
-  const float ur = x[1] + hm_matvec(blk.quad[1], h, q);
-  const float z = sig_s(kSigScale * uz);
-  const float r = sig_s(kSigScale * ur);
-  const float uc = x[2] + hm_matvec(blk.quad[2], r * h, q);
-  const float c = tanh_s(kTanhScale * uc);
-  HmLin l;
-  l.fv = fmaf(z, c - h, h);
-  l.alpha = 1.0f - z;
-  l.beta = (c - h) * z * (1.0f - z);
-  l.gamma = z * fmaf(-c, c, 1.0f);
-  l.rho = r;
-  l.delta = h * r * (1.0f - r);
-  return l;
-}
-
-// J d for a vector d held per channel
-__device__ __forceinline__ float hm_jvec(const HmBlocks& blk, const HmLin& l, float d, int q) {
-  const float y3 = hm_matvec(blk.quad[0], d, q);
-  const float y1 = hm_matvec(blk.quad[1], d, q);
-  const float w = fmaf(l.delta, y1, l.rho * d);
-  const float y2 = hm_matvec(blk.quad[2], w, q);
-  return fmaf(l.gamma, y2, fmaf(l.beta, y3, l.alpha * d));
+// one cell step h' = f(h, x) in the vector layout (the unroll)
+__device__ __forceinline__ float hm_step(const HmBlocks& blk, const float* x, float h, int q) {
+  const float z = sig_s(kSigScale * (x[0] + hm_matvec(blk.quad[0], h, q)));
+  const float r = sig_s(kSigScale * (x[1] + hm_matvec(blk.quad[1], h, q)));
+  const float c = tanh_s(kTanhScale * (x[2] + hm_matvec(blk.quad[2], r * h, q)));
+  return fmaf(z, c - h, h);
 }
 
 // ---- the Newton passes over one chunk of one (row, head) ----
@@ -327,6 +297,74 @@ k_hm_scan(const float* __restrict__ agg, int64_t n_ch, float* __restrict__ carry
   }
 }
 
+// Two-level carries for long chunk sequences: k_hm_group composes the
+// aggregates of each group of kHmGroup consecutive chunks (in parallel over
+// groups, the matrix products on the matrix cores), k_hm_scan then runs
+// over the groups, and k_hm_expand turns each group's incoming carry into
+// the carries of its chunks.  The serial chain is n_ch / kHmGroup + 2
+// kHmGroup steps long instead of n_ch.
+constexpr int kHmGroup = 16;
+
+// the map of the whole group: (M, v) <- (M_c, v_c) o (M, v), c in order
+__global__ void __launch_bounds__(kWave)
+k_hm_group(const float* __restrict__ agg, int64_t n_ch, int64_t n_groups, float* __restrict__ gagg) {
+  const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
+  const int mr = lane & 15, mk = 4 * (lane >> 4);
+  const int64_t g = blockIdx.x, head = blockIdx.y, b = blockIdx.z, n_heads = gridDim.y;
+  const float* a = agg + (b * n_heads + head) * n_ch * kHmNC;
+  __shared__ __attribute__((aligned(16))) float vs[kHmD];
+  const int64_t c0 = g * kHmGroup, c1 = imin(n_ch, c0 + kHmGroup);
+  hm_f4 M;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) M[r] = (mk + r == mr) ? 1.0f : 0.0f;
+  float v = 0.0f;
+  for (int64_t c = c0; c < c1; ++c) {
+    const float* ac = a + c * kHmNC;
+    const hm_f4 xm = hm_ld4(ac + mr * kHmD + mk);     // operands of M_c as the left factor
+    const hm_f4 row = hm_ld4(ac + i * kHmD + 4 * q);   // row i of M_c, columns 4q..4q+3
+    const float vc = ac[kHmD * kHmD + i];
+    hm_f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xm[p], M[p], acc, 0, 0, 0);
+    M = acc;
+    if (q == 0) vs[i] = v;
+    __syncthreads();
+    const hm_f4 vv = hm_ld4(vs + 4 * q);
+    v = hm_rowsum(fmaf(row[3], vv[3], fmaf(row[2], vv[2], fmaf(row[1], vv[1], row[0] * vv[0])))) + vc;
+    __syncthreads();  // vs is rewritten at the next chunk
+  }
+  float* out = gagg + ((b * n_heads + head) * n_groups + g) * kHmNC;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[(mk + r) * kHmD + mr] = M[r];
+  if (q == 0) out[kHmD * kHmD + i] = v;
+}
+
+// the carries of a group's chunks from the carry entering the group
+__global__ void __launch_bounds__(kWave)
+k_hm_expand(const float* __restrict__ agg, const float* __restrict__ gcarry, int64_t n_ch, int64_t n_groups,
+            float* __restrict__ carry) {
+  const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
+  const int64_t g = blockIdx.x, head = blockIdx.y, b = blockIdx.z, n_heads = gridDim.y;
+  const float* a = agg + (b * n_heads + head) * n_ch * kHmNC;
+  float* cout = carry + (b * n_heads + head) * n_ch * kHmD;
+  __shared__ __attribute__((aligned(16))) float ss[kHmD];
+  const int64_t c0 = g * kHmGroup, c1 = imin(n_ch, c0 + kHmGroup);
+  float s = gcarry[((b * n_heads + head) * n_groups + g) * kHmD + i];
+  for (int64_t c = c0; c < c1; ++c) {
+    const float* ac = a + c * kHmNC;
+    const hm_f4 row = hm_ld4(ac + i * kHmD + 4 * q);
+    const float vc = ac[kHmD * kHmD + i];
+    if (q == 0) {
+      cout[c * kHmD + i] = s;
+      ss[i] = s;
+    }
+    __syncthreads();
+    const hm_f4 sv = hm_ld4(ss + 4 * q);
+    s = hm_rowsum(fmaf(row[3], sv[3], fmaf(row[2], sv[2], fmaf(row[1], sv[1], row[0] * sv[0])))) + vc;
+    __syncthreads();
+  }
+}
+
 // The sequential unroll: one wave per (row, head), h_t = f(h_(t-1), x_t).
 __global__ void __launch_bounds__(kWave)
 k_hm_sequential(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
@@ -351,7 +389,7 @@ k_hm_sequential(const float* __restrict__ xproj, const float* __restrict__ A, co
     __syncthreads();
     for (int j = 0; j < n; ++j) {
       const float x[3] = {xs[j][0][i], xs[j][1][i], xs[j][2][i]};
-      h = hm_linearise(blk, x, h, q).fv;
+      h = hm_step(blk, x, h, q);
       if (q == 0) Hout[(b * T + t0 + j) * d_h + ch] = h;
     }
   }

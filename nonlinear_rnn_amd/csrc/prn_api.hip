@@ -478,8 +478,8 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
 
 // ---- head-mix GRU (dense d_head x d_head recurrent blocks) ----
 struct PlanHm {
-  int64_t n_heads, n_ch, n_wg;
-  size_t iter_off, n_iter, agg_off, carry_off, rpart_off, total;
+  int64_t n_heads, n_ch, n_wg, n_groups;  // n_groups = 0: one-level carries
+  size_t iter_off, n_iter, agg_off, carry_off, rpart_off, gagg_off, gcarry_off, total;
 };
 
 PlanHm plan_hm(const prn_params* p, int K) {
@@ -493,7 +493,12 @@ PlanHm plan_hm(const prn_params* p, int K) {
   pl.agg_off = pl.n_iter * it;
   pl.carry_off = pl.agg_off + align_up(size_t(pl.n_wg) * prn::kHmNC * 4);
   pl.rpart_off = pl.carry_off + align_up(size_t(pl.n_wg) * prn::kHmD * 4);
-  pl.total = pl.rpart_off + align_up(size_t(K + 1) * pl.n_wg * 4);
+  pl.gagg_off = pl.rpart_off + align_up(size_t(K + 1) * pl.n_wg * 4);
+  // two-level carries once the chunk chain is longer than two groups
+  pl.n_groups = pl.n_ch > 2 * prn::kHmGroup ? (pl.n_ch + prn::kHmGroup - 1) / prn::kHmGroup : 0;
+  const size_t ng = size_t(p->B) * pl.n_heads * pl.n_groups;
+  pl.gcarry_off = pl.gagg_off + align_up(ng * prn::kHmNC * 4);
+  pl.total = pl.gcarry_off + align_up(ng * prn::kHmD * 4);
   return pl;
 }
 
@@ -729,6 +734,8 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
   float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
   float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
   float* rpart = residual_out ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
+  float* gagg = reinterpret_cast<float*>(ws + pl.gagg_off);
+  float* gcarry = reinterpret_cast<float*>(ws + pl.gcarry_off);
   const float* xp = static_cast<const float*>(xproj);
   float* Hout = static_cast<float*>(H_out);
   const dim3 grid(unsigned(pl.n_ch), unsigned(pl.n_heads), unsigned(p->B));
@@ -738,7 +745,14 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
     float* Hk = (k == K - 1) ? Hout : iter[k % 2];
     prn::k_hm_pass<prn::kHmReduce><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, nullptr, p->T, p->d_h, pl.n_ch, agg,
                                                         rpart ? rpart + k * pl.n_wg : nullptr, nullptr, nullptr);
-    prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
+    if (pl.n_groups) {
+      const dim3 ggrid(unsigned(pl.n_groups), unsigned(pl.n_heads), unsigned(p->B));
+      prn::k_hm_group<<<ggrid, 64, 0, st>>>(agg, pl.n_ch, pl.n_groups, gagg);
+      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(gagg, pl.n_groups, gcarry);
+      prn::k_hm_expand<<<ggrid, 64, 0, st>>>(agg, gcarry, pl.n_ch, pl.n_groups, carry);
+    } else {
+      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
+    }
     prn::k_hm_pass<prn::kHmFix><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, carry, p->T, p->d_h, pl.n_ch, nullptr,
                                                      nullptr, Hk, k == K - 1 ? slast : nullptr);
     Hprev = Hk;

@@ -52,7 +52,10 @@ def gpu_sequential(xp, A, h0=None):
     return to_f64(H), to_f64(last)
 
 
-CASES = [(2, 200, 32, 1), (1, 64, 16, 2), (3, 1, 48, 3), (2, 1000, 64, 4), (1, 129, 128, 5)]
+# (B, T, d_h, seed): several 32-step chunks with a ragged tail, exactly one
+# chunk, T = 1, and 38 chunks (the two-level carries: three groups of 16
+# chunks, the last one partial)
+CASES = [(2, 200, 32, 1), (1, 64, 16, 2), (3, 1, 48, 3), (2, 1000, 64, 4), (1, 129, 128, 5), (2, 1189, 32, 6)]
 
 
 @pytest.mark.parametrize("Bn,T,d_h,seed", CASES)
