@@ -51,8 +51,8 @@ def algorithmic_backward_bytes(w) -> float:
 
 # the sources each profiled kernel is built and launched from
 KERNEL_SOURCES = {
-    "k_newton_sp": ["prn_device.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
-    "k_bw_sp": ["prn_device.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
+    "k_newton_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
+    "k_bw_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
     "k_proj": ["proj.h", "proj.hip"],
 }
 
@@ -200,6 +200,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the T = 1 decode step")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip timing the fused forward (projection inside the Newton kernel)")
     ap.add_argument("--no-headmix", action="store_true", help="skip timing the head-mix GRU")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -328,6 +330,39 @@ def main() -> int:
                                  "traffic": profiled_traffic("k_bw_sp", w.name), "algorithmic_bytes": bw_bytes}}
         print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
+    fused = None
+    if not args.no_fused:
+        # the same forward as one kernel: each Newton workgroup projects its own chunk on the matrix cores
+        Hf = torch.empty_like(H)
+        resf = torch.zeros_like(res)
+
+        def fstep():
+            B.prn_newton_forward_fused(x, W, bias, a, w.K, Hf, cell=w.cell, cu_seqlens=cu, residual_out=resf,
+                                       workspace=ws, stream=stream)
+        for _ in range(args.warmup):
+            fstep()
+        fev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            fev2[i][0].record(stream)
+            fstep()
+            fev2[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_fx = np.array([e[0].elapsed_time(e[1]) for e in fev2])
+        fx_ms = float(t_fx.mean())
+        ffl = proj_flops(w)
+        fused = {"kernel": "k_newton_sp, fused-projection instance (prn_newton_forward_fused)",
+                 "ms_mean": fx_ms, "ms_min": float(t_fx.min()), "tokens_per_s": w.tokens / (fx_ms * 1e-3),
+                 "speedup_vs_two_calls": float(t_step.mean()) / fx_ms,
+                 "max_abs_vs_two_calls": float((Hf.float() - H.float()).abs().max().item()),
+                 "residuals": resf.cpu().tolist(),
+                 "roofline": {"bound": "mfma", "achieved": ffl / (fx_ms * 1e-3) / 1e12,
+                              "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                              "frac": ffl / (fx_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+                              "traffic": None, "algorithmic_flops": ffl}}
+        del Hf
+        print(f"[bench] fused forward timed ({args.steps} calls)", file=sys.stderr, flush=True)
+
     decode = None
     if not args.no_decode:
         # the serving step: one token for each of 64 slots per call (projection + cell fused), ping-pong carries
@@ -439,6 +474,7 @@ def main() -> int:
                                       / HBM_PEAK_GBPS},
         "residuals": residuals,
         "backward": backward,
+        "fused": fused,
         "decode": decode,
         "headmix": headmix,
         "device": torch.cuda.get_device_name(0),

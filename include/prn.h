@@ -71,7 +71,7 @@ typedef struct {
   int32_t dtype;           /* PRN_F32 | PRN_BF16                                          */
   int64_t B;               /* batch rows; must be 1 for a ragged pack                     */
   int64_t T;               /* steps per row; for a ragged pack the total token count N    */
-  int64_t d_in;            /* input width (prn_input_proj only)                           */
+  int64_t d_in;            /* input width (the entry points that take x)                  */
   int64_t d_h;             /* hidden width = channels per gate                            */
   int64_t n_seqs;          /* 0: rectangular batch; > 0: segments in the ragged pack      */
   const float* a;          /* (G, d_h) fp32 diagonal recurrent weights, gate order above  */
@@ -130,14 +130,39 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* params, const
                               int32_t K, const int32_t* cu_seqlens, void* H_out,
                               float* residual_out);
 
+/* prn_input_proj followed by prn_newton_forward, in one kernel: each Newton
+ * workgroup computes its chunk's projected inputs on the matrix cores from x
+ * and W (FAQs "How do I pass recurrent state between decode steps?":
+ * decode_wx is this projection; shapes page: W_x), so the projected inputs
+ * never pass through device memory unless xproj_out asks for them.
+ *   x, W, bias as for prn_input_proj (d_in % 4 == 0 for fp32 storage,
+ *              % 8 for bf16; x and W 16-byte aligned)
+ *   h0, K, cu_seqlens, H_out, residual_out as for prn_newton_forward
+ *   xproj_out  NULL, or (B, T, G, d_h) storage dtype, 16-byte aligned: also
+ *              store the projected inputs (the backward pass needs them)
+ * The projected inputs are bitwise those prn_input_proj computes (same
+ * matrix-core instruction and summation order), so H_out and residual_out
+ * agree with prn_input_proj + prn_newton_forward up to the run-to-run
+ * rounding of the single-pass schedule.  params->d_in must be set and
+ * params->picard_iters must be 0 (else PRN_ERR_UNSUPPORTED); the single-pass
+ * schedule always runs (PRN_ALGO is not read).  Workspace:
+ * prn_workspace_bytes(params, K), which covers both forwards.  Errors as
+ * for prn_newton_forward and prn_input_proj. */
+prn_status prn_newton_forward_fused(const void* x, const void* W, const float* bias,
+                                    const prn_params* params, const void* h0, int32_t K,
+                                    const int32_t* cu_seqlens, void* H_out, float* residual_out,
+                                    void* xproj_out);
+
 /* Sequential unroll s_t = f(s_{t-1}, x_t) (the eval-mode path and the truth
  * the Newton result must match within tau).  Arguments as for
  * prn_newton_forward.  Uses no workspace. */
 prn_status prn_sequential_forward(const void* xproj, const prn_params* params, const void* h0,
                                   const int32_t* cu_seqlens, void* H_out);
 
-/* Bytes of workspace prn_newton_forward needs for these params and K
- * (0 on invalid params; see prn_last_error). */
+/* Bytes of workspace prn_newton_forward (and prn_newton_forward_fused)
+ * needs for these params and K.  0 on invalid params, with the reason in
+ * prn_last_error; the workspace-size queries clear that message first, so 0
+ * with an empty message means no workspace is needed (e.g. T = 0). */
 size_t prn_workspace_bytes(const prn_params* params, int32_t K);
 
 /* Backward pass: gradients of a loss L through the recurrence, the step a

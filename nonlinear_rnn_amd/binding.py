@@ -26,7 +26,8 @@ STATE = {"gru": 1, "lstm": 2}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # every symbol include/prn.h declares
-EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_workspace_bytes",
+EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "prn_sequential_forward",
+           "prn_workspace_bytes",
            "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_head_newton_forward",
            "prn_head_sequential_forward", "prn_head_workspace_bytes", "prn_validate_cu_seqlens",
            "prn_last_error", "prn_version")
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.prn_input_proj.argtypes = [vp, vp, vp, P, vp]
         L.prn_newton_forward.argtypes = [vp, P, vp, i32, vp, vp, vp]
+        L.prn_newton_forward_fused.argtypes = [vp, vp, vp, P, vp, i32, vp, vp, vp, vp]
         L.prn_sequential_forward.argtypes = [vp, P, vp, vp, vp]
         L.prn_workspace_bytes.argtypes = [P, i32]
         L.prn_workspace_bytes.restype = ctypes.c_size_t
@@ -86,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
-        for name in ("prn_input_proj", "prn_newton_forward", "prn_sequential_forward", "prn_newton_backward",
+        for name in ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "prn_sequential_forward",
+                     "prn_newton_backward",
                      "prn_decode_step", "prn_head_newton_forward", "prn_head_sequential_forward",
                      "prn_validate_cu_seqlens"):
             getattr(L, name).restype = ctypes.c_int
@@ -219,6 +222,47 @@ def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlen
                     states_out=states_out, workspace=workspace, stream=stream, picard_iters=picard_iters)
     _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
                                     _ptr(H_out), _ptr(residual_out)))
+
+
+def prn_newton_forward_fused(x, W, bias, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None,
+                             residual_out=None, xproj_out=None, state_last_out=None, states_out=None,
+                             workspace=None, stream=None) -> None:
+    """prn_input_proj + prn_newton_forward in one kernel: x (B,T,d_in), W (G*d_h, d_in), bias (G*d_h)
+    fp32 or None; xproj_out (B,T,G,d_h) optionally receives the projected inputs."""
+    _dev(x, "x")
+    _dev(W, "W", x.dtype)
+    _dev(bias, "bias", torch.float32)
+    _dev(a, "a", torch.float32)
+    _dev(H_out, "H_out", x.dtype)
+    _dev(h0, "h0", x.dtype)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(state_last_out, "state_last_out", x.dtype)
+    _dev(xproj_out, "xproj_out", x.dtype)
+    _dev(residual_out, "residual_out", torch.float32)
+    B, T, d_in = x.shape
+    G, S = GATES[cell], STATE[cell]
+    d_h = W.shape[0] // G
+    if W.shape != (G * d_h, d_in) or a.shape != (G, d_h) or H_out.shape != (B, T, d_h):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} W {tuple(W.shape)} a {tuple(a.shape)} "
+                         f"H_out {tuple(H_out.shape)}")
+    if bias is not None and bias.shape != (G * d_h,):
+        raise ValueError("bias must have G*d_h entries")
+    if xproj_out is not None and xproj_out.shape != (B, T, G, d_h):
+        raise ValueError(f"xproj_out must be {(B, T, G, d_h)}, got {tuple(xproj_out.shape)}")
+    _dev(states_out, "states_out", x.dtype)
+    if states_out is not None and states_out.shape != (B, T, S, d_h):
+        raise ValueError(f"states_out must be {(B, T, S, d_h)}, got {tuple(states_out.shape)}")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rows = B if cu_seqlens is None else n_seqs
+    for t, name in ((h0, "h0"), (state_last_out, "state_last_out")):
+        if t is not None and t.shape != (rows, S, d_h):
+            raise ValueError(f"{name} must be {(rows, S, d_h)}, got {tuple(t.shape)}")
+    if residual_out is not None and residual_out.numel() < K + 1:
+        raise ValueError("residual_out needs K + 1 entries")
+    p = make_params(cell, x.dtype, B, T, d_h, d_in=d_in, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
+                    states_out=states_out, workspace=workspace, stream=stream)
+    _check(lib().prn_newton_forward_fused(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(h0), K,
+                                          _ptr(cu_seqlens), _ptr(H_out), _ptr(residual_out), _ptr(xproj_out)))
 
 
 def prn_sequential_forward(xproj, a, H_out, *, cell: str, h0=None, cu_seqlens=None, state_last_out=None,

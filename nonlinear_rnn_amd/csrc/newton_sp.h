@@ -37,6 +37,7 @@
 // fences, which cost about 2 us per publication here.)
 #pragma once
 
+#include "fused_proj.h"
 #include "newton_kernels.h"
 
 namespace prn {
@@ -170,22 +171,40 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 // chunk (LS = 16, fp32 LSTM), whose register need otherwise lands a few
 // registers above 256 (the states_out instance: 264, 20 bytes of spills under
 // the cap) and halves the resident waves; no constraint otherwise.
-template <class C, int DT, int LS>
+// The fused-projection instances (FX) hold the projection's accumulators on
+// top of the Newton state and are capped the same way.
+template <class C, int DT, int LS, bool FX>
 constexpr int sp_min_waves() {
-  return (C::S == 2 && DT == kF32 && LS >= 16) ? 2 : 1;
+  return (FX || (C::S == 2 && DT == kF32 && LS >= 16)) ? 2 : 1;
 }
 
-template <class C, int DT, int LS, int NW, bool WS, bool PIC>
-__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(sp_min_waves<C, DT, LS>())))
+// LDS of the chunk's projected inputs; with the fused projection (FX) the
+// same memory first stages that projection's operands
+template <class C, int LS, int NW, bool FX>
+constexpr int sp_xsh_bytes() {
+  constexpr int xsh = LS * C::G * kWave * NW * 4;
+  if constexpr (FX) {
+    constexpr int st = FxGeom<C, LS, NW>::BYTES;
+    return st > xsh ? st : xsh;
+  } else {
+    return xsh;
+  }
+}
+
+// FX: the chunk's projected inputs are computed here from x and W on the
+// matrix cores (fused_tile) instead of being read from xproj.
+template <class C, int DT, int LS, int NW, bool WS, bool PIC, bool FX>
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(sp_min_waves<C, DT, LS, FX>())))
 k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ h0,
             const int32_t* __restrict__ cu, const float* __restrict__ a, int64_t T, int64_t d_h,
             int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
             typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
             typename Storage<DT>::T* __restrict__ sout, float* __restrict__ rpart, SpRecords rec,
-            unsigned spin_limit, bool agg_first) {
+            unsigned spin_limit, bool agg_first, FxArgs fx) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, LC = LS * NW;
+  static_assert(!(FX && PIC), "the Picard sweep reads the step before the chunk, which the fused tile lacks");
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform, kept in SGPRs
   __shared__ Map part[2][NW][kWave];
@@ -194,7 +213,8 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   __shared__ unsigned tk;
   // the chunk's scaled projected inputs, read-only after the first walk:
   // [step][gate][thread] (consecutive lanes, consecutive banks)
-  __shared__ float xsh[LS][G][kWave * NW];
+  __shared__ __attribute__((aligned(16))) float xraw[sp_xsh_bytes<C, LS, NW, FX>() / 4];
+  float(*xsh)[G][kWave * NW] = reinterpret_cast<float(*)[G][kWave * NW]>(xraw);
 
   if (threadIdx.x == 0) tk = atomicAdd(rec.ticket, 1u);
   __syncthreads();
@@ -212,6 +232,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   sg.init(cu, n_seqs, b, t0);
   // a full sub-chunk without a segment head needs no per-step guards
   const bool fast = n == LS && t0 != 0 && sg.start != t0 && sg.next >= t0 + LS;
+  if constexpr (FX) fused_tile<C, DT, LS, NW>(reinterpret_cast<uint8_t*>(xraw), fx, b, T, chunk * LC, tile, d_h, xsh);
 
   ChanCoef<C> cf;
   cf.load(a, d_h, ch);
@@ -248,12 +269,17 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   if (fast) {
     float xs[LS][G];
 #pragma unroll
-    for (int j = 0; j < LS; ++j) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    for (int j = 0; j < LS; ++j) {
+      if constexpr (FX)
+        xs_get(j, xs[j]);
+      else
+        load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    }
     float pm[S];
     if constexpr (PIC) picard_before(pm);
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
-      xs_put(j, xs[j]);
+      if constexpr (!FX) xs_put(j, xs[j]);
       float prev[S], fv[S];
 #pragma unroll
       for (int q = 0; q < S; ++q) prev[q] = PIC ? pm[q] : 0.0f;
@@ -277,8 +303,14 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   } else if (wact) {
     float xs[LS][G];
 #pragma unroll
-    for (int j = 0; j < LS; ++j)
-      if (j < n) load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+    for (int j = 0; j < LS; ++j) {
+      if (j < n) {
+        if constexpr (FX)
+          xs_get(j, xs[j]);
+        else
+          load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
+      }
+    }
     float pm[S];
     if constexpr (PIC) {
 #pragma unroll
@@ -289,7 +321,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       if (j < n) {
-        xs_put(j, xs[j]);
+        if constexpr (!FX) xs_put(j, xs[j]);
         const bool head = st.at(t0 + j);
         float prev[S], fv[S];
 #pragma unroll

@@ -67,6 +67,15 @@ int sp_ls(int cell, int dtype, int64_t n_chains) {
   if (n_chains < kSpManyChains) return kSpLsGruFew;
   return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
 }
+// With the projection fused into the Newton kernel, a chunk must be a
+// multiple of 32 steps (the projection's 32-row blocks): the GRU with many
+// chains takes 32-step chunks (8 per lane) where the unfused kernel takes
+// 48 or 40.
+constexpr int kFxLsGruMany = 8;
+int sp_ls_fused(int cell, int dtype, int64_t n_chains) {
+  if (cell == PRN_CELL_DIAG_GRU && n_chains >= kSpManyChains) return kFxLsGruMany;
+  return sp_ls(cell, dtype, n_chains);
+}
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
 // below this many independent chains, chunks publish their aggregate before
 // polling (measured: helps 4-32 chains, hurts 128)
@@ -216,11 +225,11 @@ struct PlanSp {
   size_t agg_off, pre_off, rpart_off, total;
 };
 
-PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
+PlanSp plan_sp(const prn_params* p, const Shape& sh, int K, bool fused = false) {
   PlanSp pl{};
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
-  pl.ls = sp_ls(p->cell, p->dtype, pl.n_chains);
+  pl.ls = fused ? sp_ls_fused(p->cell, p->dtype, pl.n_chains) : sp_ls(p->cell, p->dtype, pl.n_chains);
   const int lc = pl.ls * kSpNW;
   pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_wg = pl.n_ch * pl.n_chains;
@@ -237,6 +246,10 @@ PlanSp plan_sp(const prn_params* p, const Shape& sh, int K) {
 
 size_t workspace_needed(const prn_params* p, const Shape& sh, int K) {
   return use_three_phase() ? plan_tp(p, sh, K).total : plan_sp(p, sh, K).total;
+}
+// the fused forward always runs the single-pass schedule
+size_t fused_workspace_needed(const prn_params* p, const Shape& sh, int K) {
+  return p->T > 0 ? plan_sp(p, sh, K, true).total : 0;
 }
 
 prn_status launched(const char* what) {
@@ -319,13 +332,14 @@ prn_status newton_tp(const prn_params* p, const Shape& sh, const void* xproj_v, 
   return launched("prn_newton_forward");
 }
 
+// fx != NULL: the projection is fused into the Newton kernel (xproj_v unused)
 template <class C, int DT>
 prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, const void* h0_v, int K,
-                     const int32_t* cu, void* Hout_v, float* res) {
+                     const int32_t* cu, void* Hout_v, float* res, const prn::FxArgs* fx = nullptr) {
   using T = typename prn::Storage<DT>::T;
   constexpr int S = C::S;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
-  const PlanSp pl = plan_sp(p, sh, K);
+  const PlanSp pl = plan_sp(p, sh, K, fx != nullptr);
   const T* h0 = static_cast<const T*>(h0_v);
   T* slast = static_cast<T*>(p->state_last_out);
   char* ws = static_cast<char*>(p->workspace);
@@ -339,36 +353,52 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
     float* rpart = res ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
     prn::k_zero_u32<<<unsigned((pl.n_status + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_status));
-    auto launch = [&](auto ls) {
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    const prn::FxArgs fa = fx ? *fx : prn::FxArgs{nullptr, nullptr, nullptr, 0, nullptr};
+    auto launch = [&](auto ls, auto fxc) {
       constexpr int LS = decltype(ls)::value;
+      constexpr bool FX = decltype(fxc)::value;
       T* sout = static_cast<T*>(p->states_out);
       auto go = [&](auto ws, auto pic) {
-        prn::k_newton_sp<C, DT, LS, kSpNW, decltype(ws)::value, decltype(pic)::value>
+        prn::k_newton_sp<C, DT, LS, kSpNW, decltype(ws)::value, decltype(pic)::value, FX>
             <<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
                 static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles,
                 pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, kSpinLimit,
-                pl.n_chains < kAggFirstBelowChains);
+                pl.n_chains < kAggFirstBelowChains, fa);
       };
-      using T_ = std::true_type;
-      using F_ = std::false_type;
-      if (p->picard_iters > 0) {
+      if constexpr (FX) {
+        if (sout) go(T_{}, F_{}); else go(F_{}, F_{});
+      } else if (p->picard_iters > 0) {
         if (sout) go(T_{}, T_{}); else go(F_{}, T_{});
       } else {
         if (sout) go(T_{}, F_{}); else go(F_{}, F_{});
       }
     };
-    if constexpr (S == 2) {
+    if (fx) {
+      if constexpr (S == 2) {
+        if constexpr (DT == prn::kBF16)
+          launch(std::integral_constant<int, kSpLsLstmBf16>{}, T_{});
+        else
+          launch(std::integral_constant<int, kSpLsLstm>{}, T_{});
+      } else {
+        if (pl.ls == kSpLsGruFew)
+          launch(std::integral_constant<int, kSpLsGruFew>{}, T_{});
+        else
+          launch(std::integral_constant<int, kFxLsGruMany>{}, T_{});
+      }
+    } else if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsLstmBf16>{});
+        launch(std::integral_constant<int, kSpLsLstmBf16>{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsLstm>{});
+        launch(std::integral_constant<int, kSpLsLstm>{}, F_{});
     } else {
       if (pl.ls == kSpLsGruFew)
-        launch(std::integral_constant<int, kSpLsGruFew>{});
+        launch(std::integral_constant<int, kSpLsGruFew>{}, F_{});
       else if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsGruManyBf16>{});
+        launch(std::integral_constant<int, kSpLsGruManyBf16>{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsGruMany>{});
+        launch(std::integral_constant<int, kSpLsGruMany>{}, F_{});
     }
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
@@ -558,6 +588,7 @@ prn_status prn_decode_step(const void* x, const void* W, const float* bias, cons
 }
 
 size_t prn_backward_workspace_bytes(const prn_params* p) {
+  g_err.clear();  // a 0 result with no message means no workspace is needed
   Shape sh;
   if (check_common(p, &sh) != PRN_OK) return 0;
   return plan_bw(p, sh).total;
@@ -619,13 +650,15 @@ prn_status prn_validate_cu_seqlens(const int32_t* cu, int64_t n_seqs, int64_t N)
 }
 
 size_t prn_workspace_bytes(const prn_params* p, int32_t K) {
+  g_err.clear();  // a 0 result with no message means no workspace is needed
   Shape sh;
   if (check_common(p, &sh) != PRN_OK) return 0;
   if (K < 1) {
     fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
     return 0;
   }
-  return workspace_needed(p, sh, K);
+  const size_t a = workspace_needed(p, sh, K), b = fused_workspace_needed(p, sh, K);
+  return a > b ? a : b;
 }
 
 prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void* h0, int32_t K,
@@ -653,6 +686,42 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void
   }
   if (p->dtype == PRN_F32) return newton<prn::CellLSTM, prn::kF32>(p, sh, xproj, h0, K, cu, H_out, residual_out);
   return newton<prn::CellLSTM, prn::kBF16>(p, sh, xproj, h0, K, cu, H_out, residual_out);
+}
+
+prn_status prn_newton_forward_fused(const void* x, const void* W, const float* bias, const prn_params* p,
+                                    const void* h0, int32_t K, const int32_t* cu, void* H_out, float* residual_out,
+                                    void* xproj_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+  if (p->picard_iters < 0) return fail(PRN_ERR_INVALID_ARG, "picard_iters must be >= 0");
+  if (p->picard_iters > 0)
+    return fail(PRN_ERR_UNSUPPORTED, "the fused forward has no Picard sweep (use prn_input_proj + prn_newton_forward)");
+  if (p->d_in < 1) return fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
+  if (p->T > 0 && (!x || !W)) return fail(PRN_ERR_INVALID_ARG, "x or W is NULL");
+  if ((s = check_newton_args(p, sh, x, h0, cu, H_out)) != PRN_OK) return s;
+  if (misaligned(x, 16) || misaligned(W, 16) || misaligned(xproj_out, 16) || misaligned(bias, 4))
+    return fail(PRN_ERR_INVALID_ARG, "x, W and xproj_out must be 16-byte aligned, bias 4-byte aligned");
+  if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
+  const int kvec = p->dtype == PRN_F32 ? 4 : 8;
+  if (p->d_in % kvec != 0)
+    return fail(PRN_ERR_UNSUPPORTED, "the fused projection needs d_in %% %d == 0 for this storage dtype", kvec);
+  const size_t need = fused_workspace_needed(p, sh, K);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
+                p->workspace, need);
+  if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+    return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  const prn::FxArgs fx{x, W, bias, p->d_in, xproj_out};
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32)
+      return newton_sp<prn::CellGRU, prn::kF32>(p, sh, nullptr, h0, K, cu, H_out, residual_out, &fx);
+    return newton_sp<prn::CellGRU, prn::kBF16>(p, sh, nullptr, h0, K, cu, H_out, residual_out, &fx);
+  }
+  if (p->dtype == PRN_F32)
+    return newton_sp<prn::CellLSTM, prn::kF32>(p, sh, nullptr, h0, K, cu, H_out, residual_out, &fx);
+  return newton_sp<prn::CellLSTM, prn::kBF16>(p, sh, nullptr, h0, K, cu, H_out, residual_out, &fx);
 }
 
 prn_status prn_sequential_forward(const void* xproj, const prn_params* p, const void* h0, const int32_t* cu,
@@ -689,6 +758,7 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias, const
 }
 
 size_t prn_head_workspace_bytes(const prn_params* p, int32_t d_head, int32_t K) {
+  g_err.clear();  // a 0 result with no message means no workspace is needed
   Shape sh;
   if (check_head(p, &sh, d_head) != PRN_OK) return 0;
   if (K < 1) {

@@ -98,5 +98,32 @@ def small_inputs(w: Workload, seed: int = 0) -> dict:
     return make_inputs(w, seed=seed)
 
 
-__all__ = ["prn", "say", "to_dev", "to_f64", "gpu_run", "gpu_sequential", "oracle_newton", "oracle_sequential",
+
+
+def gpu_run_fused(w: Workload, inp: dict, K: int, *, h0=None, cu=None, with_xproj=True, with_state=True):
+    """prn_newton_forward_fused through the C ABI (projection inside the Newton
+    kernel).  Returns dict(xproj (or None), H, res (K+1), last)."""
+    dt = TORCH_DT[w.dtype]
+    x = to_dev(inp["x"], w.dtype)
+    W = to_dev(inp["W"], w.dtype)
+    bias = torch.from_numpy(inp["bias"]).cuda()
+    a = torch.from_numpy(inp["a"]).cuda()
+    cu = inp["cu_seqlens"] if cu is None else cu
+    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    n_seqs = 0 if cu is None else len(cu) - 1
+    rows = w.B if cu is None else n_seqs
+    H = torch.empty((w.B, w.T, w.d_h), dtype=dt, device="cuda")
+    res = torch.full((K + 1,), -1.0, dtype=torch.float32, device="cuda")
+    last = torch.empty((rows, w.S, w.d_h), dtype=dt, device="cuda") if with_state else None
+    xproj = torch.empty((w.B, w.T, w.G, w.d_h), dtype=dt, device="cuda") if with_xproj else None
+    h0_d = None if h0 is None else to_dev(h0, w.dtype)
+    ws_n = B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, K, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    B.prn_newton_forward_fused(x, W, bias, a, K, H, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, residual_out=res,
+                               xproj_out=xproj, state_last_out=last, workspace=ws)
+    torch.cuda.synchronize()
+    return {"xproj": xproj, "H": H, "res": res.cpu().numpy().astype(np.float64), "last": last}
+
+
+__all__ = ["prn", "say", "to_dev", "to_f64", "gpu_run", "gpu_run_fused", "gpu_sequential", "oracle_newton", "oracle_sequential",
            "tol", "small_inputs", "TORCH_DT"]
