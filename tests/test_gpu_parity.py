@@ -285,3 +285,29 @@ def test_single_pass_and_three_phase_agree(w, monkeypatch):
     o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
     assert (o1["H"].float() - o2["H"].float()).abs().max().item() <= tol(w, 1e-5)
     assert np.all(np.abs(o1["res"] - o2["res"]) <= tol(w, 2e-5) + 1e-3 * o2["res"])
+
+
+@pytest.mark.parametrize("dtype,d_in,d_h,cell", [("f32", 36, 80, "lstm"), ("bf16", 40, 72, "gru"),
+                                                 ("f32", 256, 256, "lstm")])
+def test_large_projection_with_ragged_tiles(dtype, d_in, d_h, cell):
+    """Projections large enough for the 256 x 256 direct-to-LDS tiles, with a
+    partial last row tile, a partial last column tile and a partial last K
+    stage (rows past M / N load the last row, chunks past K a zero chunk):
+    every output against the fp64 product."""
+    w = Workload("proj_large", cell, 1, 262144 + 77, d_in, d_h, dtype, 1)
+    say(f"[case] large projection {w}")
+    inp = small_inputs(w)
+    x = to_dev(inp["x"], dtype)
+    W = to_dev(inp["W"], dtype)
+    bias = torch.from_numpy(inp["bias"]).cuda()
+    xproj = torch.full((w.B, w.T, w.G, w.d_h), float("nan"), dtype=TORCH_DT[dtype], device="cuda")
+    prn.binding.prn_input_proj(x, W, bias, xproj, cell=cell)
+    torch.cuda.synchronize()
+    got = to_f64(xproj)
+    ref = oproj.input_proj(oround.load(inp["x"], dtype), oround.load(inp["W"], dtype),
+                           inp["bias"].astype(np.float64), w.G)
+    assert np.all(np.isfinite(got))
+    if dtype == "f32":
+        assert np.abs(got - ref).max() <= 1e-5
+    else:
+        assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-4)
