@@ -53,8 +53,17 @@ def algorithmic_backward_bytes(w) -> float:
 KERNEL_SOURCES = {
     "k_newton_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
     "k_bw_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
+    "k_newton_sp_fused": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
     "k_proj": ["proj.h", "proj.hip"],
+    "k_proj_dl": ["proj.h", "proj.hip"],
 }
+
+
+def proj_kernel(w) -> str:
+    """The projection kernel prn_input_proj launches for this workload: 256 x 256
+    direct-to-LDS tiles once there are at least 1024 of them, else 128 x 128 tiles."""
+    tiles = -(-w.B * w.T // 256) * -(-w.G * w.d_h // 256)
+    return "k_proj_dl" if tiles >= 1024 else "k_proj"
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -359,7 +368,7 @@ def main() -> int:
                  "roofline": {"bound": "mfma", "achieved": ffl / (fx_ms * 1e-3) / 1e12,
                               "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                               "frac": ffl / (fx_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-                              "traffic": None, "algorithmic_flops": ffl}}
+                              "traffic": profiled_traffic("k_newton_sp_fused", w.name), "algorithmic_flops": ffl}}
         del Hf
         print(f"[bench] fused forward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
@@ -440,9 +449,10 @@ def main() -> int:
                    "algorithmic_bytes": alg_bytes}
     roof_newton["frac"] = roof_newton["achieved"] / roof_newton["peak"]
     fl = proj_flops(w)
-    roof_proj = {"kernel": "k_proj (prn_input_proj)", "bound": "mfma",
+    pk = proj_kernel(w)
+    roof_proj = {"kernel": f"{pk} (prn_input_proj)", "bound": "mfma",
                  "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                 "traffic": profiled_traffic("k_proj", w.name), "algorithmic_flops": fl}
+                 "traffic": profiled_traffic(pk, w.name), "algorithmic_flops": fl}
     roof_proj["frac"] = roof_proj["achieved"] / roof_proj["peak"]
     dominant = roof_newton if newton_ms >= proj_ms else roof_proj
 
