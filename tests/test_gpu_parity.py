@@ -287,14 +287,18 @@ def test_single_pass_and_three_phase_agree(w, monkeypatch):
     assert np.all(np.abs(o1["res"] - o2["res"]) <= tol(w, 2e-5) + 1e-3 * o2["res"])
 
 
-@pytest.mark.parametrize("dtype,d_in,d_h,cell", [("f32", 36, 80, "lstm"), ("bf16", 40, 72, "gru"),
-                                                 ("f32", 256, 256, "lstm")])
-def test_large_projection_with_ragged_tiles(dtype, d_in, d_h, cell):
-    """Projections large enough for the 256 x 256 direct-to-LDS tiles, with a
+@pytest.mark.parametrize("dtype,T,d_in,d_h,cell", [("f32", 262144 + 77, 36, 80, "lstm"),
+                                                   ("bf16", 262144 + 77, 40, 72, "gru"),
+                                                   ("f32", 262144 + 77, 256, 256, "lstm"),
+                                                   ("f32", 262144, 128, 64, "lstm"),
+                                                   ("bf16", 262144, 64, 64, "lstm")])
+def test_large_projection_with_ragged_tiles(dtype, T, d_in, d_h, cell):
+    """Projections large enough for the 256 x 256 direct-to-LDS tiles: with a
     partial last row tile, a partial last column tile and a partial last K
-    stage (rows past M / N load the last row, chunks past K a zero chunk):
-    every output against the fp64 product."""
-    w = Workload("proj_large", cell, 1, 262144 + 77, d_in, d_h, dtype, 1)
+    stage (the guarded instance: rows past M / N load the last row, chunks
+    past K a zero chunk), and exactly tiled (the unguarded instance): every
+    output against the fp64 product."""
+    w = Workload("proj_large", cell, 1, T, d_in, d_h, dtype, 1)
     say(f"[case] large projection {w}")
     inp = small_inputs(w)
     x = to_dev(inp["x"], dtype)
