@@ -55,15 +55,14 @@ KERNEL_SOURCES = {
     "k_bw_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
     "k_newton_sp_fused": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
     "k_proj": ["proj.h", "proj.hip"],
-    "k_proj_dl": ["proj.h", "proj.hip"],
 }
 
 
-def proj_kernel(w) -> str:
-    """The projection kernel prn_input_proj launches for this workload: 256 x 256
-    direct-to-LDS tiles once there are at least 1024 of them, else 128 x 128 tiles."""
+def proj_tiles(w) -> str:
+    """The tile shape prn_input_proj uses for this workload: 256 x 256 once there
+    are at least 1024 such tiles, else 128 x 128."""
     tiles = -(-w.B * w.T // 256) * -(-w.G * w.d_h // 256)
-    return "k_proj_dl" if tiles >= 1024 else "k_proj"
+    return "256x256" if tiles >= 1024 else "128x128"
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -449,10 +448,9 @@ def main() -> int:
                    "algorithmic_bytes": alg_bytes}
     roof_newton["frac"] = roof_newton["achieved"] / roof_newton["peak"]
     fl = proj_flops(w)
-    pk = proj_kernel(w)
-    roof_proj = {"kernel": f"{pk} (prn_input_proj)", "bound": "mfma",
+    roof_proj = {"kernel": f"k_proj, {proj_tiles(w)} tiles (prn_input_proj)", "bound": "mfma",
                  "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                 "traffic": profiled_traffic(pk, w.name), "algorithmic_flops": fl}
+                 "traffic": profiled_traffic("k_proj", w.name), "algorithmic_flops": fl}
     roof_proj["frac"] = roof_proj["achieved"] / roof_proj["peak"]
     dominant = roof_newton if newton_ms >= proj_ms else roof_proj
 
