@@ -113,14 +113,7 @@ def gate_residual(residuals, dtype, residual_fail=RESIDUAL_FAIL, residual_warn=N
         warnings.warn(f"newton_residual_high: max|F(H)| = {rK:.3e} > {warn:.1e}", RuntimeWarning, stacklevel=3)
 
 
-def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_table=None,
-                   residual_fail=RESIDUAL_FAIL, residual_warn=None, gate=True, return_state=False):
-    """Parallel Newton forward.  Returns (H (B,T,d_h), residuals [r_0..r_K] on
-    the host[, final states]).  K may be None: then it comes from k_table, or
-    from the cell's measured K*(T) table (nonlinear_rnn_amd/kstar_table.json)."""
-    xproj = xproj.contiguous()
-    a = a.to(torch.float32).contiguous()
-    Bn, T, _, d_h = xproj.shape
+def _resolve_depth(K, k_table, T: int, cell: str) -> int:
     if K is None and k_table is None:
         # max_iters=None: the measured K*(T) envelope of this cell (FAQs,
         # "How many Newton iterations should I use?")
@@ -130,7 +123,18 @@ def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_tabl
         K = resolve_k(T, k_table)
     if K is None or int(K) < 1:
         raise ValueError("K must be >= 1")
-    K = int(K)
+    return int(K)
+
+
+def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_table=None,
+                   residual_fail=RESIDUAL_FAIL, residual_warn=None, gate=True, return_state=False):
+    """Parallel Newton forward.  Returns (H (B,T,d_h), residuals [r_0..r_K] on
+    the host[, final states]).  K may be None: then it comes from k_table, or
+    from the cell's measured K*(T) table (nonlinear_rnn_amd/kstar_table.json)."""
+    xproj = xproj.contiguous()
+    a = a.to(torch.float32).contiguous()
+    Bn, T, _, d_h = xproj.shape
+    K = _resolve_depth(K, k_table, T, cell)
     cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
     n_seqs = 0 if cu is None else cu.numel() - 1
     rows = Bn if cu is None else n_seqs
@@ -160,9 +164,46 @@ def sequential_forward(xproj, a, *, cell: str, h0=None, cu_seqlens=None, return_
     return (H, st) if return_state else H
 
 
-def forward(x, W, bias, a, K=3, *, cell: str, **kw):
-    """Projection + Newton: the train-mode forward of one diagonal layer."""
+def forward(x, W, bias, a, K=3, *, cell: str, fused: bool = False, **kw):
+    """Projection + Newton: the train-mode forward of one diagonal layer.
+    fused=True runs both in one kernel (each Newton workgroup projects its own
+    chunk; same results up to the single-pass schedule's run-to-run rounding)."""
+    if fused:
+        return forward_fused(x, W, bias, a, K, cell=cell, **kw)
     return newton_forward(input_proj(x, W, bias, cell=cell), a, K, cell=cell, **kw)
+
+
+def forward_fused(x, W, bias, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_table=None,
+                  residual_fail=RESIDUAL_FAIL, residual_warn=None, gate=True, return_state=False,
+                  return_xproj=False):
+    """prn_newton_forward_fused behind the same contract as newton_forward.
+    Returns (H, residuals[, final states][, xproj])."""
+    x, W = x.contiguous(), W.contiguous()
+    bias = None if bias is None else bias.to(torch.float32).contiguous()
+    a = a.to(torch.float32).contiguous()
+    Bn, T, _ = x.shape
+    d_h = W.shape[0] // B_.GATES[cell]
+    K = _resolve_depth(K, k_table, T, cell)
+    cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, x.device)
+    n_seqs = 0 if cu is None else cu.numel() - 1
+    rows = Bn if cu is None else n_seqs
+    H = torch.empty((Bn, T, d_h), dtype=x.dtype, device=x.device)
+    res = torch.zeros(K + 1, dtype=torch.float32, device=x.device)
+    st = (torch.empty((rows, B_.STATE[cell], d_h), dtype=x.dtype, device=x.device) if return_state else None)
+    xp = (torch.empty((Bn, T, B_.GATES[cell], d_h), dtype=x.dtype, device=x.device) if return_xproj else None)
+    n = B_.prn_workspace_bytes(cell, x.dtype, Bn, T, d_h, K, n_seqs=n_seqs)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    B_.prn_newton_forward_fused(x, W, bias, a, K, H, cell=cell, h0=_contig(h0), cu_seqlens=cu, residual_out=res,
+                                xproj_out=xp, state_last_out=st, workspace=ws)
+    residuals = res.cpu().tolist()   # the one host sync of a forward
+    if gate:
+        gate_residual(residuals, x.dtype, residual_fail, residual_warn)
+    out = (H, residuals)
+    if return_state:
+        out += (st,)
+    if return_xproj:
+        out += (xp,)
+    return out
 
 
 def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol=None,

@@ -187,3 +187,34 @@ def test_fused_full_size_sampled_parity(name):
     assert d <= tol(w, 1e-5)
     assert err <= tol(w, 1e-5)
     assert np.all(np.abs(out["res"] - two["res"]) <= tol(w, 1e-5) + 1e-4 * two["res"])
+
+
+def test_api_forward_fused_matches_two_calls_and_gates():
+    """The Python-level contract around the fused entry point: same results as
+    the two-call forward, the final state and stored xproj on request, K from
+    a per-T table, strided inputs copied, and the divergence gate."""
+    from nonlinear_rnn_amd import api
+    w = Workload("lstm_api", "lstm", 2, 500, 24, 70, "f32", 3)
+    say(f"[case] api fused forward {w}")
+    inp = small_inputs(w)
+    x = torch.from_numpy(inp["x"]).cuda()
+    W = torch.from_numpy(inp["W"]).cuda()
+    bias = torch.from_numpy(inp["bias"]).cuda()
+    a = torch.from_numpy(inp["a"]).cuda()
+    H2, r2, st2 = api.forward(x, W, bias, a, 3, cell="lstm", return_state=True)
+    H1, r1, st1, xp = api.forward(x, W, bias, a, 3, cell="lstm", fused=True, return_state=True, return_xproj=True)
+    assert (H1 - H2).abs().max().item() <= 1e-6 and (st1 - st2).abs().max().item() <= 1e-6
+    assert np.allclose(r1, r2, rtol=1e-5, atol=1e-6)
+    assert torch.equal(xp, api.input_proj(x, W, bias, cell="lstm"))
+    Ht, rt = api.forward(x, W, bias, a, None, cell="lstm", fused=True, k_table={64: 2, 1024: 4})
+    assert len(rt) == 5   # T = 500 -> K = 4
+    # a strided view of x (every other feature of a wider tensor) is copied first
+    xw = torch.zeros((2, 500, 48), device="cuda")
+    xw[:, :, ::2] = x
+    Hs, _ = api.forward(xw[:, :, ::2], W, bias, a, 3, cell="lstm", fused=True)
+    assert (Hs - H1).abs().max().item() <= 1e-6
+    # non-finite input: the residual gate raises
+    xn = x.clone()
+    xn[1, 100, 3] = float("nan")
+    with pytest.raises(api.NewtonDivergenceError):
+        api.forward(xn, W, bias, a, 3, cell="lstm", fused=True)
