@@ -90,6 +90,46 @@ def test_newton_forward_rejects_pack_inconsistency():
     assert B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None) == B.PRN_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(a=FAKE), dict(x=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(W=None), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(K=0), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE, d_in=0), dict(), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE, d_in=6), dict(), B.PRN_ERR_UNSUPPORTED),                 # fp32 needs d_in % 4 == 0
+    (dict(a=FAKE, dtype=1, d_in=4), dict(), B.PRN_ERR_UNSUPPORTED),        # bf16 needs d_in % 8 == 0
+    (dict(a=FAKE, picard_iters=1), dict(), B.PRN_ERR_UNSUPPORTED),
+    (dict(a=FAKE), dict(x=FAKE + 8), B.PRN_ERR_INVALID_ARG),                 # 16-byte alignment
+    (dict(a=FAKE), dict(xproj_out=FAKE + 4), B.PRN_ERR_INVALID_ARG),
+    (dict(a=FAKE), dict(), B.PRN_ERR_WORKSPACE),                             # no workspace given
+    (dict(a=FAKE, workspace=FAKE, workspace_bytes=16), dict(), B.PRN_ERR_WORKSPACE),
+    (dict(a=None), dict(), B.PRN_ERR_INVALID_ARG),
+])
+def test_fused_forward_rejects_bad_arguments_before_launch(kw, args, status):
+    p = _params(**kw)
+    a = dict(x=FAKE, W=FAKE, K=3, xproj_out=None)
+    a.update(args)
+    st = B.lib().prn_newton_forward_fused(a["x"], a["W"], None, ctypes.byref(p), None, a["K"], None, FAKE, None,
+                                          a["xproj_out"])
+    assert st == status, B.prn_last_error()
+    assert B.prn_last_error()
+
+
+def test_workspace_bytes_cover_the_fused_forward():
+    """prn_workspace_bytes sizes the workspace of both forwards (the fused GRU
+    with many chains runs shorter chunks, hence more chunk records).  Only the
+    rejection path runs: a too-small workspace reports the size it needs."""
+    for cell, Bn in (("gru", 128), ("lstm", 2), ("gru", 2)):
+        p = _params(cell=B.CELLS[cell], B=Bn, T=4096, d_h=256, a=FAKE, workspace=FAKE, workspace_bytes=16)
+        n = B.lib().prn_workspace_bytes(ctypes.byref(p), 3)
+        st = B.lib().prn_newton_forward_fused(FAKE, FAKE, None, ctypes.byref(p), None, 3, None, FAKE, None, None)
+        assert st == B.PRN_ERR_WORKSPACE
+        need = int(re.search(r"; (\d+) bytes needed", B.prn_last_error()).group(1))
+        st = B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None)
+        assert st == B.PRN_ERR_WORKSPACE
+        need_unfused = int(re.search(r"; (\d+) bytes needed", B.prn_last_error()).group(1))
+        assert n >= need and n >= need_unfused and n == max(need, need_unfused)
+
+
 def test_input_proj_rejects_unsupported_shapes():
     p = _params(d_in=6)   # fp32 needs d_in % 4 == 0
     assert B.lib().prn_input_proj(FAKE, FAKE, None, ctypes.byref(p), FAKE) == B.PRN_ERR_UNSUPPORTED
