@@ -70,13 +70,8 @@ __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0, 0, 0,
 // LDS position of chunk kv of row r
 __device__ __forceinline__ int lds_pos(int r, int kv) { return kv ^ ((r / RPG) & (CPR - 1)); }
 
-// round to nearest even; NaN stays a quiet NaN (branch-free)
-__device__ __forceinline__ uint16_t bf16_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t q = (u >> 16) | 0x40u;
-  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? q : r);
-}
+// round to nearest even (v_cvt_pk_bf16_f32); NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t bf16_rne(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 
 template <int WR, int WC>
 struct Tile {
