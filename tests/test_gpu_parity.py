@@ -315,3 +315,42 @@ def test_large_projection_with_ragged_tiles(dtype, T, d_in, d_h, cell):
         assert np.abs(got - ref).max() <= 1e-5
     else:
         assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-4)
+
+
+def test_device_bf16_rounding_matches_the_oracle_bitwise():
+    """bf16 storage rounding on the device (v_cvt_pk_bf16_f32) against the
+    oracle's round-to-nearest-even, bit for bit.  The projection with an
+    identity W computes xproj = x + bias exactly in fp32 (one exact product,
+    then one fp32 addition) and rounds it once, so crafted x and bias put the
+    fp32 sums on exact ties (either parity of the kept bit), just beside
+    them, at random, and past the largest bf16 value (overflow to Inf)."""
+    rng = np.random.default_rng(11)
+    d_h, G, T = 64, 3, 256
+    N = G * d_h
+    e = rng.integers(-20, 20, size=N)                      # binade of column n's x values
+    kind = np.arange(N) % 6
+    scale = np.exp2(e.astype(np.float64))
+    half_ulp = scale * 2.0 ** -8                             # bf16 keeps 8 significant bits
+    bias = np.where(kind == 0, half_ulp, np.where(kind == 1, -half_ulp,
+                    np.where(kind == 2, half_ulp * (1 + 2.0 ** -12), np.where(kind == 3, half_ulp * (1 - 2.0 ** -12),
+                    rng.standard_normal(N) * scale))))
+    mant = 1.0 + rng.integers(0, 128, size=(T, N)) / 128.0   # 8 significant bits: exact in bf16
+    sign = np.where(rng.random((T, N)) < 0.5, -1.0, 1.0)
+    x = sign * mant * scale
+    big = np.array([0x7F7F0000, 0x7F7E0000], dtype=np.uint32).view(np.float32).astype(np.float64)  # bf16 max, next below
+    x[:, kind == 5] = np.where(rng.random((T, int((kind == 5).sum()))) < 0.5, big[0], big[1])
+    bias[kind == 5] = np.where(np.arange(int((kind == 5).sum())) % 2 == 0, 3.0e35, 1.0e36)
+    x32 = x.astype(np.float32)
+    b32 = bias.astype(np.float32)
+    assert np.array_equal(oround.bf16_round(x32), x32.astype(np.float64))   # x is exactly bf16
+    xd = torch.from_numpy(x32.reshape(1, T, N)).to(torch.bfloat16).cuda()
+    Wd = torch.eye(N, dtype=torch.float32).to(torch.bfloat16).cuda()
+    xproj = torch.empty((1, T, G, d_h), dtype=torch.bfloat16, device="cuda")
+    prn.binding.prn_input_proj(xd, Wd, torch.from_numpy(b32).cuda(), xproj, cell="gru")
+    torch.cuda.synchronize()
+    got = xproj.reshape(T, N).view(torch.int16).cpu().numpy().view(np.uint16)
+    ref64 = oround.bf16_round((x32 + b32).astype(np.float64))   # fp32 sum, then round to bf16
+    ref = (ref64.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.isinf(ref64[:, kind == 5]).any() and not np.isinf(ref64[:, kind == 5]).all()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]:#06x} want {ref[tuple(bad[0])]:#06x}"
