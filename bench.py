@@ -60,9 +60,9 @@ KERNEL_SOURCES = {
 
 def proj_tiles(w) -> str:
     """The tile shape prn_input_proj uses for this workload: 256 x 256 once there
-    are at least 1024 such tiles, else 128 x 128."""
+    are at least 768 such tiles, else 128 x 128."""
     tiles = -(-w.B * w.T // 256) * -(-w.G * w.d_h // 256)
-    return "256x256" if tiles >= 1024 else "128x128"
+    return "256x256" if tiles >= 768 else "128x128"
 
 
 def kernel_source_hash(kernel: str) -> str:
