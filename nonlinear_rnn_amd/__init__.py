@@ -7,10 +7,11 @@ agreement check.
 """
 from .binding import (  # noqa: F401
     EXPORTS, PrnError, lib, prn_backward_workspace_bytes, prn_input_proj, prn_last_error, prn_newton_backward,
-    prn_newton_forward, prn_sequential_forward, prn_validate_cu_seqlens, prn_version, prn_workspace_bytes,
+    prn_newton_forward, prn_newton_forward_fused, prn_sequential_forward, prn_validate_cu_seqlens, prn_version,
+    prn_workspace_bytes,
 )
 from .api import (  # noqa: F401
     AGREEMENT_ATOL, AgreementError, AgreementReport, NewtonDivergenceError, RESIDUAL_FAIL, RESIDUAL_WARN,
-    forward, gate_residual, input_proj, input_proj_apply, newton_apply, newton_forward, resolve_k,
+    forward, forward_fused, gate_residual, input_proj, input_proj_apply, newton_apply, newton_forward, resolve_k,
     sequential_forward, validate_cu_seqlens, verify_agreement,
 )
