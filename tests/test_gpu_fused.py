@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (gpu_run, gpu_run_fused, oracle_newton, oracle_sequential, say, small_inputs, to_f64,
+from gpu_helpers import (gpu_run, gpu_run_fused, oracle_newton, oracle_sequential, say, small_inputs, to_dev, to_f64,
                          tol, TORCH_DT)
 from nonlinear_rnn_amd import binding as B
 from oracle import proj as oproj
@@ -218,3 +218,40 @@ def test_api_forward_fused_matches_two_calls_and_gates():
     xn[1, 100, 3] = float("nan")
     with pytest.raises(api.NewtonDivergenceError):
         api.forward(xn, W, bias, a, 3, cell="lstm", fused=True)
+
+
+@pytest.mark.parametrize("cell,dtype", [("lstm", "f32"), ("gru", "f32"), ("lstm", "bf16")])
+def test_fused_states_out_matches_two_call_trajectory(cell, dtype):
+    """The fused instance that also writes every state (the trajectory the
+    backward pass takes) against prn_newton_forward's states_out, ragged pack
+    with h0 included."""
+    w = Workload(f"{cell}_states", cell, 1, 900, 16, 72, dtype, 3)
+    cu = np.array([0, 100, 100, 433, 900], dtype=np.int32)
+    wp = w.scaled(n_seqs=len(cu) - 1)
+    say(f"[case] fused states_out {wp}")
+    inp = small_inputs(w)
+    dt = TORCH_DT[dtype]
+    x = to_dev(inp["x"], dtype)
+    W = to_dev(inp["W"], dtype)
+    bias = torch.from_numpy(inp["bias"]).cuda()
+    a = torch.from_numpy(inp["a"]).cuda()
+    h0 = to_dev(random_state(w, len(cu) - 1, seed=2), dtype)
+    cu_d = torch.from_numpy(cu).cuda()
+    ws = torch.empty(B.prn_workspace_bytes(cell, dt, 1, w.T, w.d_h, 3, n_seqs=len(cu) - 1), dtype=torch.uint8,
+                     device="cuda")
+    xp = torch.empty((1, w.T, w.G, w.d_h), dtype=dt, device="cuda")
+    B.prn_input_proj(x, W, bias, xp, cell=cell)
+    outs = []
+    for fused in (False, True):
+        H = torch.empty((1, w.T, w.d_h), dtype=dt, device="cuda")
+        st = torch.empty((1, w.T, w.S, w.d_h), dtype=dt, device="cuda")
+        if fused:
+            B.prn_newton_forward_fused(x, W, bias, a, 3, H, cell=cell, h0=h0, cu_seqlens=cu_d, states_out=st,
+                                       workspace=ws)
+        else:
+            B.prn_newton_forward(xp, a, 3, H, cell=cell, h0=h0, cu_seqlens=cu_d, states_out=st, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((H, st))
+    lim = 1e-6 if dtype == "f32" else 1e-2
+    assert (outs[0][1].float() - outs[1][1].float()).abs().max().item() <= lim
+    assert torch.equal(outs[1][1][..., w.S - 1, :], outs[1][0])   # h part of the states is H_out
