@@ -280,10 +280,12 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       if constexpr (!FX) xs_put(j, xs[j]);
-      float prev[S], fv[S];
-#pragma unroll
-      for (int q = 0; q < S; ++q) prev[q] = PIC ? pm[q] : 0.0f;
-      ms[j] = C::template fj<false>(xs[j], prev, cf.as, cf.a, false, fv);
+      float fv[S];
+      if constexpr (PIC) {
+        ms[j] = C::template fj<false>(xs[j], pm, cf.as, cf.a, false, fv);
+      } else {
+        ms[j] = C::fj0(xs[j], cf.a, fv);  // linearised at H^(0) = 0
+      }
       acc = compose(ms[j], acc);
       if constexpr (PIC) {
         float z[S];

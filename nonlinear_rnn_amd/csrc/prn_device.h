@@ -143,6 +143,20 @@ struct CellGRU {
     const float J = fmaf(z, dc, fmaf(c - h, dz, omz));
     return {J, fmaf(-J, h, fv)};
   }
+  // fj at the zero state (the first linearisation, from H = 0, away from a
+  // segment head): the terms that vanish with h are left out.  Equal to
+  // fj(xs, {0}) for finite operands.
+  static __device__ __forceinline__ Map fj0(const float* xs, const float* a, float* fout) {
+    const float z = sig_s(xs[0]);
+    const float r = sig_s(xs[1]);
+    const float c = tanh_s(xs[2]);
+    const float fv = z * c;
+    fout[0] = fv;
+    const float omz = 1.0f - z;
+    const float dz = z * omz * a[0];
+    const float dc = fmaf(-c, c, 1.0f) * a[2] * r;
+    return {fmaf(z, dc, fmaf(c, dz, omz)), fv};
+  }
   // Backward of one step at (s, x) with cotangent lam = dL/dh': the
   // pre-activation gradients du_g (= dL/dx_g), dL/da_g = du_g * m_g (m = h,
   // h, r h) and dL/dh = J^T lam.
@@ -213,6 +227,33 @@ struct CellLSTM {
     m.a11 = j11;
     m.b0 = c1 - fmaf(fg, c, j01 * h);
     m.b1 = h1 - fmaf(j10, c, j11 * h);
+    return m;
+  }
+  // fj at the zero state (c, h) = 0 (the first linearisation, from H = 0,
+  // away from a segment head): the terms that vanish with c and h are left
+  // out.  Equal to fj(xs, {0, 0}) for finite operands.
+  static __device__ __forceinline__ Map fj0(const float* xs, const float* a, float* fout) {
+    const float ig = sig_s(xs[0]);
+    const float fg = sig_s(xs[1]);
+    const float og = sig_s(xs[2]);
+    const float gg = tanh_s(xs[3]);
+    const float c1 = ig * gg;
+    const float tc = tanh_s(c1 * kTanhScale);
+    const float h1 = og * tc;
+    fout[0] = c1;
+    fout[1] = h1;
+    const float di = ig * (1.0f - ig) * a[0];
+    const float dO = og * (1.0f - og) * a[2];
+    const float dg = fmaf(-gg, gg, 1.0f) * a[3];
+    const float j01 = fmaf(gg, di, ig * dg);
+    const float odt = og * fmaf(-tc, tc, 1.0f);
+    Map m;
+    m.a00 = fg;
+    m.a01 = j01;
+    m.a10 = odt * fg;
+    m.a11 = fmaf(tc, dO, odt * j01);
+    m.b0 = c1;
+    m.b1 = h1;
     return m;
   }
   // Backward of one step at (s, x) with cotangent lam = (dL/dc', dL/dh'):
