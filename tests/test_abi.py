@@ -265,3 +265,18 @@ def test_head_workspace_bytes():
     assert w3 > w1 > 0 and w3 % 256 == 0
     p = _params(d_h=64, dtype=1)
     assert B.lib().prn_head_workspace_bytes(ctypes.byref(p), 16, 3) == 0 and B.prn_last_error()
+
+
+def test_bench_names_the_projection_tiles_the_library_uses():
+    """bench.py reports which projection tile shape ran; its rule must be the
+    library's (256 x 256 tiles from kLargeTiles of them on)."""
+    import bench
+    from workloads import Workload
+    src = open(os.path.join(ROOT, "nonlinear_rnn_amd", "csrc", "proj.hip")).read()
+    large = int(re.search(r"constexpr int64_t kLargeTiles = (\d+);", src).group(1))
+    # rows x columns of 256 x 256 tiles: just below and at the threshold
+    # G d_h = 768: 3 column tiles; rows of 256 tokens
+    below = Workload("t", "gru", 1, 256 * (large // 3 - 1), 8, 256, "f32", 3)
+    at = Workload("t", "gru", 1, 256 * (large // 3), 8, 256, "f32", 3)
+    assert bench.proj_tiles(below) == "128x128"
+    assert bench.proj_tiles(at) == "256x256"
