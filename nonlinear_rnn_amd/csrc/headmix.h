@@ -138,7 +138,11 @@ __device__ __forceinline__ void hm_phase_a(const HmBlocks& blk, const float* xpr
   }
   if (t == 0 && h0) P = hm_ld4(h0 + b * d_h + c0);
   else if (t == 0) P = hm_f4{0.0f, 0.0f, 0.0f, 0.0f};
-  const hm_f4 uz = hm_blockmul(blk.mf[0], P), ur = hm_blockmul(blk.mf[1], P);
+  // linearising at H = 0 (the first iteration; no h0 in this block): the
+  // recurrent terms A_g P vanish, and so do their block products
+  const bool pzero = !Hprev && (!h0 || t0 + jb > 0);
+  const hm_f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const hm_f4 uz = pzero ? zero4 : hm_blockmul(blk.mf[0], P), ur = pzero ? zero4 : hm_blockmul(blk.mf[1], P);
   hm_f4 z, rr, rh;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -146,7 +150,7 @@ __device__ __forceinline__ void hm_phase_a(const HmBlocks& blk, const float* xpr
     rr[r] = sig_s(kSigScale * (xr[r] + ur[r]));
     rh[r] = rr[r] * P[r];
   }
-  const hm_f4 uc = hm_blockmul(blk.mf[2], rh);
+  const hm_f4 uc = pzero ? zero4 : hm_blockmul(blk.mf[2], rh);
   hm_f4 fv, al, be, ga, de;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -174,14 +178,17 @@ __device__ __forceinline__ float hm_matvec_lds(const float* aq, const float* x, 
 }
 
 // one step of the vector chain, vector layout (channel i = L / 4):
-// returns f + J (d - prev) for step s of the block
-__device__ __forceinline__ float hm_chain_step(const HmBlocks& blk, HmShared& sh, int s, float d, int i, int q) {
+// returns f + J (d - prev) for step s of the block.  zprev: the previous
+// iterate is 0 (the first iteration), so delta = h r (1 - r) is 0 and the
+// A_r product drops out.
+__device__ __forceinline__ float hm_chain_step(const HmBlocks& blk, HmShared& sh, int s, float d, int i, int q,
+                                               bool zprev) {
   const float dl = d - sh.cf[kCprev][s][i];
   if (q == 0) sh.dv[i] = dl;
   __syncthreads();
   const float y3 = hm_matvec_lds(blk.quad[0], sh.dv, q);
-  const float y1 = hm_matvec_lds(blk.quad[1], sh.dv, q);
-  const float w = fmaf(sh.cf[kCdelta][s][i], y1, sh.cf[kCrho][s][i] * dl);
+  const float rdl = sh.cf[kCrho][s][i] * dl;
+  const float w = zprev ? rdl : fmaf(sh.cf[kCdelta][s][i], hm_matvec_lds(blk.quad[1], sh.dv, q), rdl);
   if (q == 0) sh.wv[i] = w;
   __syncthreads();
   const float y2 = hm_matvec_lds(blk.quad[2], sh.wv, q);
@@ -213,6 +220,9 @@ k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const fl
 #pragma unroll
   for (int r = 0; r < 4; ++r) M[r] = (mk + r == mr) ? 1.0f : 0.0f;
   float d = 0.0f;  // kHmReduce: the map's offset v; kHmFix: the state
+  // linearisation at H = 0: past a sequence's first step (whose map is
+  // constant) every previous state is 0
+  const bool zprev = Hprev == nullptr;
   if (MODE == kHmFix) d = carry[((b * n_heads + head) * n_ch + chunk) * kHmD + i];
   unsigned rmax = 0;
   for (int jb = 0; jb < n; jb += kHmBlk) {
@@ -229,20 +239,27 @@ k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const fl
           d = sh.cf[kCf][s][i];
         } else {
           if constexpr (MODE == kHmReduce) {
-            // M <- J M = alpha M + beta (A_z M) + gamma A_c (rho M + delta (A_r M))
+            // M <- J M = alpha M + beta (A_z M) + gamma A_c (rho M + delta (A_r M));
+            // delta = 0 when linearising at H = 0
             const hm_f4 y3 = hm_blockmul(blk.mf[0], M);
-            const hm_f4 y1 = hm_blockmul(blk.mf[1], M);
-            const hm_f4 rho = hm_ld4(&sh.cf[kCrho][s][mk]), del = hm_ld4(&sh.cf[kCdelta][s][mk]);
+            const hm_f4 rho = hm_ld4(&sh.cf[kCrho][s][mk]);
             hm_f4 W;
+            if (zprev) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) W[r] = fmaf(del[r], y1[r], rho[r] * M[r]);
+              for (int r = 0; r < 4; ++r) W[r] = rho[r] * M[r];
+            } else {
+              const hm_f4 y1 = hm_blockmul(blk.mf[1], M);
+              const hm_f4 del = hm_ld4(&sh.cf[kCdelta][s][mk]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) W[r] = fmaf(del[r], y1[r], rho[r] * M[r]);
+            }
             const hm_f4 y2 = hm_blockmul(blk.mf[2], W);
             const hm_f4 al = hm_ld4(&sh.cf[kCalpha][s][mk]), be = hm_ld4(&sh.cf[kCbeta][s][mk]),
                         ga = hm_ld4(&sh.cf[kCgamma][s][mk]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) M[r] = fmaf(ga[r], y2[r], fmaf(be[r], y3[r], al[r] * M[r]));
           }
-          d = hm_chain_step(blk, sh, s, d, i, q);
+          d = hm_chain_step(blk, sh, s, d, i, q, zprev);
         }
         if (MODE == kHmFix && q == 0) Hout[(b * T + t0 + jb + s) * d_h + head * kHmD + i] = d;
       }
