@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "k_bw_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
     "k_newton_sp_fused": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
     "k_proj": ["proj.h", "proj.hip"],
+    "k_hm": ["prn_device.h", "headmix.h", "prn_api.hip"],
 }
 
 
