@@ -89,6 +89,7 @@ bool use_three_phase() {
   return e && (e[0] == 't' || e[0] == 'T');
 }
 constexpr int64_t kMaxGrid = 65535;
+constexpr int64_t kMaxGrid1D = (int64_t(1) << 31) - 1;  // workgroups of a one-dimensional launch
 
 struct Shape {
   int G, S;
@@ -340,6 +341,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
   constexpr int S = C::S;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   const PlanSp pl = plan_sp(p, sh, K, fx != nullptr);
+  if (pl.n_wg > kMaxGrid1D) return fail(PRN_ERR_UNSUPPORTED, "too many chunks for one launch (%lld)", (long long)pl.n_wg);
   const T* h0 = static_cast<const T*>(h0_v);
   T* slast = static_cast<T*>(p->state_last_out);
   char* ws = static_cast<char*>(p->workspace);
@@ -751,7 +753,8 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias, const
   const int kvec = p->dtype == PRN_F32 ? 4 : 8;
   if (Kd % kvec != 0)
     return fail(PRN_ERR_UNSUPPORTED, "input projection needs d_in %% %d == 0 for this storage dtype", kvec);
-  if (M > (int64_t(1) << 31) * 128 || N > (int64_t(1) << 31))
+  // one workgroup per output tile (at most 128 x 128 of them): the grid must fit
+  if (M > (int64_t(1) << 31) * 128 || N > (int64_t(1) << 31) || ((M + 127) / 128) * ((N + 127) / 128) > kMaxGrid1D)
     return fail(PRN_ERR_UNSUPPORTED, "input projection too large");
   prn::launch_proj(p->dtype == PRN_BF16, x, W, bias, xproj_out, M, N, Kd, static_cast<hipStream_t>(p->stream));
   return launched("prn_input_proj");

@@ -130,6 +130,17 @@ def test_workspace_bytes_cover_the_fused_forward():
         assert n >= need and n >= need_unfused and n == max(need, need_unfused)
 
 
+def test_grids_too_large_for_one_launch_are_rejected_on_the_host():
+    """More workgroups than one launch takes (2^31 - 1) is PRN_ERR_UNSUPPORTED,
+    checked before anything is launched."""
+    p = _params(T=1 << 36, d_in=8, d_h=1024)   # 5.4e8 row tiles x 24 column tiles
+    assert B.lib().prn_input_proj(FAKE, FAKE, None, ctypes.byref(p), FAKE) == B.PRN_ERR_UNSUPPORTED
+    assert "too large" in B.prn_last_error()
+    p = _params(B=1, T=1 << 38, d_h=64, a=FAKE, workspace=FAKE, workspace_bytes=1 << 62)   # 2^32 chunks
+    assert B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 2, None, FAKE, None) == B.PRN_ERR_UNSUPPORTED
+    assert "too many chunks" in B.prn_last_error()
+
+
 def test_input_proj_rejects_unsupported_shapes():
     p = _params(d_in=6)   # fp32 needs d_in % 4 == 0
     assert B.lib().prn_input_proj(FAKE, FAKE, None, ctypes.byref(p), FAKE) == B.PRN_ERR_UNSUPPORTED
