@@ -11,14 +11,18 @@ failure names a reproducible case.  Every case runs
   - the sequential unroll against the oracle's unroll.
 Tolerances are the parity tests' own: 1e-5 (fp32) and 2e-2 (bf16) on H and
 the final state at equal K; residuals to 1e-3 relative (fp32) or 2e-2
-(bf16) plus an absolute floor.
+(bf16) plus an absolute floor.  The backward (both schedules) and the
+head-mix GRU get sweeps of their own, drawn the same way.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (gpu_run, gpu_run_fused, gpu_sequential, oracle_newton, oracle_sequential, say, to_f64,
-                         tol)
+from gpu_helpers import (TORCH_DT, gpu_run, gpu_run_fused, gpu_sequential, oracle_newton, oracle_sequential, say,
+                         to_f64, tol)
+from oracle import headmix as ohm
+from test_gpu_backward import gpu_backward, gpu_forward_states, oracle_backward, random_grads, rel_err, tols
+from test_gpu_headmix import gpu_newton as hm_newton, gpu_sequential as hm_sequential, inputs as hm_inputs
 from workloads import Workload, make_inputs, random_state
 
 pytestmark = pytest.mark.gpu
@@ -107,3 +111,61 @@ def test_sweep_forward_paths_against_the_oracle(i):
     say(f"  unroll: max|H - oracle unroll| {err:.3e}")
     assert err <= tol(w, 1e-5)
     assert np.abs(to_f64(last_s) - seq_last).max() <= tol(w, 1e-5)
+
+
+@pytest.mark.parametrize("algo", ["sp", "tp"])
+@pytest.mark.parametrize("i", range(N_CASES // 2), ids=lambda i: case_id(N_CASES + i))
+def test_sweep_backward_against_the_oracle_adjoint(i, algo, monkeypatch):
+    """The backward on the forward's own trajectory, both schedules (the
+    library reads PRN_ALGO at every call); tolerances of the backward parity
+    tests, relative to 1 + max|reference|."""
+    monkeypatch.setenv("PRN_ALGO", algo)
+    w, cu, rows, with_h0 = draw_case(N_CASES + i)
+    say(f"[case] sweep backward {algo} {case_id(N_CASES + i)} cu={None if cu is None else cu.tolist()}")
+    inp = dict(make_inputs(w.scaled(n_seqs=0), seed=4000 + i), cu_seqlens=cu)
+    h0 = random_state(w, rows, seed=5000 + i) if with_h0 else None
+    if w.T == 0:
+        xproj = torch.empty((w.B, 0, w.G, w.d_h), dtype=TORCH_DT[w.dtype], device="cuda")
+        states = torch.empty((w.B, 0, w.S, w.d_h), dtype=TORCH_DT[w.dtype], device="cuda")
+    else:
+        xproj, _, states, _ = gpu_forward_states(w, inp, w.K, h0=h0)
+    dH, dsl = random_grads(w, rows, seed=6000 + i)
+    dx, da, dh0 = gpu_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+    rdx, rda, rdh0 = oracle_backward(w, inp, xproj, states, dH, h0=h0, dsl=dsl)
+    e_dx, e_da, e_dh0 = rel_err(to_f64(dx), rdx), rel_err(to_f64(da), rda), rel_err(to_f64(dh0), rdh0)
+    say(f"  dxproj {e_dx:.2e}  da {e_da:.2e}  dh0 {e_dh0:.2e}")
+    t_x, t_a = tols(w)
+    assert e_dx <= t_x and e_dh0 <= t_x and e_da <= t_a
+
+
+def draw_head_case(i: int):
+    rng = np.random.default_rng(7000 + i)
+    Bn = int(rng.integers(1, 4))
+    d_h = 16 * int(rng.integers(1, 9))
+    T = int(rng.integers(1, 1501)) if rng.integers(12) else 0
+    K = int(rng.integers(1, 6))
+    return Bn, T, d_h, K, bool(rng.integers(2))
+
+
+@pytest.mark.parametrize("i", range(16), ids=lambda i: "{}-B{}-T{}-dh{}-K{}-h0{}".format(i, *draw_head_case(i)))
+def test_sweep_head_mix_against_the_oracle(i):
+    """Head-mix GRU (dense 16 x 16 blocks per head): Newton at equal K and
+    the sequential kernel against the oracle, tolerances of the head-mix
+    parity tests (1e-5; residuals 2e-5 + 1e-3 r)."""
+    Bn, T, d_h, K, with_h0 = draw_head_case(i)
+    say(f"[case] sweep head-mix B={Bn} T={T} d_h={d_h} K={K} h0={with_h0}")
+    xp, A, h0 = hm_inputs(Bn, T, d_h, seed=8000 + i, with_h0=with_h0)
+    H, res, last = hm_newton(xp, A, K, h0, want_last=True)
+    if T == 0:
+        assert np.array_equal(res, np.zeros(K + 1))
+        assert np.array_equal(last, np.zeros((Bn, d_h)) if h0 is None else h0)
+        return
+    ref = ohm.newton(xp, A, K, h0=h0, dtype="f32")
+    r = np.asarray(ref["residuals"])
+    e = np.abs(H - ref["H"]).max()
+    say(f"  newton H err {e:.2e}; residuals gpu {np.round(res, 6)} oracle {np.round(r, 6)}")
+    assert e <= 1e-5 and np.array_equal(last, H[:, T - 1])
+    assert np.all(np.abs(res - r) <= 2e-5 + 1e-3 * r)
+    Hs, last_s = hm_sequential(xp, A, h0)
+    seq, seq_last = ohm.sequential(xp, A, h0=h0)
+    assert np.abs(Hs - seq).max() <= 1e-5 and np.abs(last_s - seq_last).max() <= 1e-5
