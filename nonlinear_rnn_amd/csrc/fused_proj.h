@@ -12,10 +12,14 @@
 // Newton work of another.
 //
 // The tile is an (LC x 64 G) block of x W^T: LC token rows of x and 64 G rows
-// of W.  Both are staged through LDS in K stages of 64 bytes per row, double
-// buffered, in the memory the tile itself occupies afterwards (the staging is
-// dead before the first result is written).  Each wave owns the 32-column
-// blocks cb = w, w + NW, ... and all LC / 32 row blocks.
+// of W.  Both go from global memory straight into LDS (global_load_lds_dwordx4,
+// no register round trip) in K stages of 64 bytes per row, through a ring of
+// three stage buffers, so that two stages are in flight while a third is
+// multiplied; the ring lives in the memory the tile itself occupies
+// afterwards (the staging is dead before the first result is written).  Rows
+// are unpadded and their four 16-byte chunks are XOR-swizzled by row so that
+// 16 consecutive rows read at one k fall in distinct banks.  Each wave owns
+// the 32-column blocks cb = w, w + NW, ... and all LC / 32 row blocks.
 //
 // The products use the instruction, the operand layout and the k order of
 // the stand-alone projection kernel (proj.hip): fp32 v_mfma_f32_32x32x2_f32
@@ -41,15 +45,35 @@ struct FxGeom {
   static constexpr int LC = LS * NW;               // token rows of the tile
   static constexpr int NCOL = C::G * kWave;        // gate-channel columns
   static constexpr int ROWB = 64;                  // bytes of every row per K stage
-  static constexpr int LDS_ROW = ROWB + 16;        // padded LDS row
+  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row per stage
   static constexpr int NROWS = LC + NCOL;          // x rows, then W rows
-  static constexpr int STAGE = NROWS * LDS_ROW;
-  static constexpr int BYTES = 2 * STAGE;          // double buffered
+  static constexpr int STAGE = NROWS * ROWB;
+  static constexpr int NBUF = 3;                   // stage ring
+  static constexpr int BYTES = NBUF * STAGE;
+  static constexpr int NI = STAGE / 1024;          // 1 KB wave loads per stage
+  static constexpr int IPW = (NI + NW - 1) / NW;   // wave loads of one wave per stage (at most)
+  static constexpr int IPW_MIN = NI / NW;          // (at least)
   static constexpr int NRB = LC / 32;              // 32-row blocks
   static constexpr int NCB_ALL = NCOL / 32;        // 32-column blocks (2 G)
   static constexpr int NCB = (NCB_ALL + NW - 1) / NW;  // column blocks of one wave (at most)
   static_assert(LC % 32 == 0, "the fused projection needs chunks of a multiple of 32 steps");
+  static_assert(STAGE % 1024 == 0, "a stage must be whole 1 KB wave loads");
+  static_assert(IPW_MIN < 16, "the stage wait encodes at most 15 outstanding loads");
 };
+
+// LDS position of 16-byte chunk kv of row r (rows of 64 bytes: four rows
+// span the 256 bytes of all banks, so the key changes every four rows)
+__device__ __forceinline__ int fx_pos(int r, int kv) { return kv ^ ((r >> 2) & 3); }
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (lgkm and export counts left alone)
+constexpr int fx_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16 zero bytes: the source of every chunk past T or past d_in
+static __device__ __attribute__((aligned(16))) const uint32_t kFxZeroChunk[4] = {0, 0, 0, 0};
+
+typedef __attribute__((address_space(1))) const void* fx_gptr_t;
+typedef __attribute__((address_space(3))) void* fx_lptr_t;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 fx_bf16x8;
 typedef __attribute__((ext_vector_type(16))) float fx_f32x16;
@@ -68,51 +92,48 @@ __device__ __forceinline__ void fused_tile(uint8_t* lds, const FxArgs& fx, int64
   using ST = Storage<DT>;
   constexpr int G = C::G;
   constexpr int ELT = DT == kF32 ? 4 : 2;
-  constexpr int VPR = Gm::ROWB / 16;  // 16-byte vectors per row per stage
-  constexpr int NT = kWave * NW;
-  constexpr int NV = Gm::NROWS * VPR;
-  constexpr int VPT = (NV + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t rowbytes = fx.d_in * ELT;
   const uint8_t* X = static_cast<const uint8_t*>(fx.x);
   const uint8_t* Wm = static_cast<const uint8_t*>(fx.W);
 
-  // the rows this thread stages (same rows every stage; only k moves)
-  const uint8_t* rp[VPT];
-  int lo[VPT], ko[VPT];
+  // wave load p of this wave (stage-relative index wl = w + p NW) fills LDS
+  // bytes [1024 wl, +1024) of a stage, lane l the 16 bytes at 16 l: row
+  // r = (64 wl + l) / 4, position q = l % 4, i.e. chunk kv = fx_pos(r, q) of
+  // the row (the same rows every stage; only k moves)
+  const uint8_t* src[Gm::IPW];
+  int kvb[Gm::IPW];
 #pragma unroll
-  for (int p = 0; p < VPT; ++p) {
-    const int v = tid + p * NT;
-    rp[p] = nullptr;
-    lo[p] = -1;
-    ko[p] = 0;
-    if (NV % NT == 0 || v < NV) {
-      const int r = v / VPR, kv = v % VPR;
-      if (r < Gm::LC) {
-        const int64_t t = tc0 + r;
-        if (t < T) rp[p] = X + (b * T + t) * rowbytes;
-      } else {
-        const int col = r - Gm::LC, g = col / kWave, c = col % kWave;
-        const int64_t ch = imin(tile * kWave + c, d_h - 1);
-        rp[p] = Wm + (g * d_h + ch) * rowbytes;
-      }
-      lo[p] = r * Gm::LDS_ROW + kv * 16;
-      ko[p] = kv * 16;
+  for (int p = 0; p < Gm::IPW; ++p) {
+    const int v = (w + p * NW) * kWave + lane;
+    const int r = v / Gm::CPR, q = v % Gm::CPR;
+    kvb[p] = fx_pos(r, q) * 16;
+    src[p] = nullptr;
+    if (r < Gm::LC) {
+      const int64_t t = tc0 + r;
+      if (t < T) src[p] = X + (b * T + t) * rowbytes + kvb[p];
+    } else if (r < Gm::NROWS) {
+      const int col = r - Gm::LC, g = col / kWave, c = col % kWave;
+      const int64_t ch = imin(tile * kWave + c, d_h - 1);
+      src[p] = Wm + (g * d_h + ch) * rowbytes + kvb[p];
     }
   }
-  fx_f32x4 rv[VPT];
-  auto gload = [&](int64_t kt) {
+  auto issue = [&](int64_t kt, int buf) {
 #pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const int64_t kb = kt * Gm::ROWB + ko[p];
-      rv[p] = (rp[p] && kb < rowbytes) ? *reinterpret_cast<const fx_f32x4*>(rp[p] + kb) : fx_f32x4{0, 0, 0, 0};
+    for (int p = 0; p < Gm::IPW; ++p) {
+      const int wl = w + p * NW;   // wave-uniform
+      if (Gm::NI % NW == 0 || wl < Gm::NI) {
+        const void* g = (src[p] && kt * Gm::ROWB + kvb[p] < rowbytes) ? static_cast<const void*>(src[p] + kt * Gm::ROWB)
+                                                                      : static_cast<const void*>(kFxZeroChunk);
+        // the destination goes through an opaque SGPR copy: the compiler then
+        // does not tie the later LDS reads to these writes with a full vmcnt
+        // wait of its own; the waits before the stage barrier order them
+        fx_lptr_t d = (fx_lptr_t)(lds + buf * Gm::STAGE + wl * 1024);
+        asm volatile("" : "+s"(d));
+        __builtin_amdgcn_global_load_lds((fx_gptr_t)g, d, 16, 0, 0);
+      }
     }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < VPT; ++p)
-      if (NV % NT == 0 || lo[p] >= 0) *reinterpret_cast<fx_f32x4*>(lds + buf * Gm::STAGE + lo[p]) = rv[p];
   };
 
   const int half = lane >> 5, l32 = lane & 31;
@@ -138,25 +159,35 @@ __device__ __forceinline__ void fused_tile(uint8_t* lds, const FxArgs& fx, int64
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int64_t nk = (rowbytes + Gm::ROWB - 1) / Gm::ROWB;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* L = lds + cur * Gm::STAGE;
+    // this wave's loads of stage kt have landed (those of stage kt + 1 may
+    // still be in flight); after the barrier the same holds for every wave,
+    // and every wave is done with stage kt - 1, whose buffer takes kt + 2
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(fx_vmcnt(Gm::IPW_MIN));
+    else
+      __builtin_amdgcn_s_waitcnt(fx_vmcnt(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2, static_cast<int>((kt + 2) % Gm::NBUF));
+    const uint8_t* L = lds + static_cast<int>(kt % Gm::NBUF) * Gm::STAGE;
 #pragma unroll
-    for (int kb = 0; kb < VPR / 2; ++kb) {
-      const int off = kb * 32 + half * 16;
+    for (int kb = 0; kb < Gm::CPR / 2; ++kb) {
+      const int kv = kb * 2 + half;
       fx_f32x4 av[Gm::NRB], bv[Gm::NCB];
 #pragma unroll
-      for (int i = 0; i < Gm::NRB; ++i)
-        av[i] = *reinterpret_cast<const fx_f32x4*>(L + (i * 32 + l32) * Gm::LDS_ROW + off);
+      for (int i = 0; i < Gm::NRB; ++i) {
+        const int r = i * 32 + l32;
+        av[i] = *reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv));
+      }
 #pragma unroll
       for (int j = 0; j < Gm::NCB; ++j) {
         const int cb = w + j * NW;
-        if (cb < Gm::NCB_ALL)
-          bv[j] = *reinterpret_cast<const fx_f32x4*>(L + (Gm::LC + cb * 32 + l32) * Gm::LDS_ROW + off);
+        const int r = Gm::LC + cb * 32 + l32;
+        if (cb < Gm::NCB_ALL) bv[j] = *reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv));
       }
       if constexpr (DT == kBF16) {
 #pragma unroll
@@ -178,9 +209,8 @@ __device__ __forceinline__ void fused_tile(uint8_t* lds, const FxArgs& fx, int64
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();   // every wave is done with the last stage
 
   // results: the staging is dead (every wave is past the last barrier)
   typename ST::T* xo = static_cast<typename ST::T*>(fx.xproj_out);
