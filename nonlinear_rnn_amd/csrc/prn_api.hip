@@ -68,12 +68,12 @@ int sp_ls(int cell, int dtype, int64_t n_chains) {
   return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
 }
 // With the projection fused into the Newton kernel, a chunk must be a
-// multiple of 32 steps (the projection's 32-row blocks): the GRU with many
-// chains takes 32-step chunks (8 per lane) where the unfused kernel takes
-// 48 or 40.
-constexpr int kFxLsGruMany = 8;
+// multiple of 32 steps (the projection's 32-row blocks), and longer chunks
+// stream W from L2 fewer times per token: every fused GRU takes 64-step
+// chunks (16 per lane), also with many chains where the unfused kernel takes
+// 48 or 40 (bf16 GRU at 128 chains: 32-step chunks 2.54 ms, 64-step 1.76 ms).
 int sp_ls_fused(int cell, int dtype, int64_t n_chains) {
-  if (cell == PRN_CELL_DIAG_GRU && n_chains >= kSpManyChains) return kFxLsGruMany;
+  if (cell == PRN_CELL_DIAG_GRU) return kSpLsGruFew;
   return sp_ls(cell, dtype, n_chains);
 }
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
@@ -384,10 +384,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
         else
           launch(std::integral_constant<int, kSpLsLstm>{}, T_{});
       } else {
-        if (pl.ls == kSpLsGruFew)
-          launch(std::integral_constant<int, kSpLsGruFew>{}, T_{});
-        else
-          launch(std::integral_constant<int, kFxLsGruMany>{}, T_{});
+        launch(std::integral_constant<int, kSpLsGruFew>{}, T_{});
       }
     } else if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)

@@ -31,7 +31,7 @@ CASES = [
     Workload("lstm_bf16_small", "lstm", 2, 300, 40, 130, "bf16", 3),
     Workload("gru_ragged_small", "gru", 1, 1500, 16, 40, "f32", 3, n_seqs=7),
     Workload("lstm_ragged_small", "lstm", 1, 900, 20, 64, "f32", 3, n_seqs=5, seg_lo=1, seg_hi=400),
-    Workload("gru_many_chains", "gru", 64, 100, 12, 70, "f32", 3),          # >= 64 chains: 32-step chunks
+    Workload("gru_many_chains", "gru", 64, 100, 12, 70, "f32", 3),          # >= 64 chains
     Workload("gru_many_chains_bf16", "gru", 40, 90, 48, 100, "bf16", 3),
     WORKLOADS["gru_tiny"],
 ]
