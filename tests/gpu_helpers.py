@@ -11,6 +11,7 @@ import torch
 
 import nonlinear_rnn_amd as prn
 from nonlinear_rnn_amd import binding as B
+from oracle import backward as obackward
 from oracle import newton as onewton
 from oracle import rounding as oround
 from workloads import Workload, make_inputs
@@ -125,5 +126,109 @@ def gpu_run_fused(w: Workload, inp: dict, K: int, *, h0=None, cu=None, with_xpro
     return {"xproj": xproj, "H": H, "res": res.cpu().numpy().astype(np.float64), "last": last}
 
 
+# backward: the forward's trajectory through states_out, the backward through
+# the C ABI, and the oracle's adjoint on the same stored numbers
+
+
+def rel_err(got, ref):
+    return float(np.abs(got - ref).max() / (1.0 + np.abs(ref).max())) if ref.size else 0.0
+
+
+def tols(w):
+    return (1e-5, 1e-4) if w.dtype == "f32" else (1e-2, 1e-4)
+
+
+def gpu_forward_states(w, inp, K, h0=None, cu=None, xproj=None):
+    """Newton forward with states_out; returns (xproj, H, states, last)."""
+    dt = TORCH_DT[w.dtype]
+    out = gpu_run(w, inp, K, h0=h0, cu=cu, xproj=xproj)
+    xproj = out["xproj"]
+    a = torch.from_numpy(inp["a"]).cuda()
+    cu = inp["cu_seqlens"] if cu is None else cu
+    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    n_seqs = 0 if cu is None else len(cu) - 1
+    rows = w.B if cu is None else n_seqs
+    H = torch.empty((w.B, w.T, w.d_h), dtype=dt, device="cuda")
+    states = torch.full((w.B, w.T, w.S, w.d_h), float("nan"), dtype=dt, device="cuda")
+    last = torch.empty((rows, w.S, w.d_h), dtype=dt, device="cuda")
+    ws_n = B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, K, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    h0_d = None if h0 is None else to_dev(h0, w.dtype)
+    B.prn_newton_forward(xproj, a, K, H, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, state_last_out=last,
+                         states_out=states, workspace=ws)
+    torch.cuda.synchronize()
+    return xproj, H, states, last
+
+
+def gpu_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None, want_dh0=True):
+    dt = TORCH_DT[w.dtype]
+    a = torch.from_numpy(inp["a"]).cuda()
+    cu = inp["cu_seqlens"] if cu is None else cu
+    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    n_seqs = 0 if cu is None else len(cu) - 1
+    rows = w.B if cu is None else n_seqs
+    dx = torch.full_like(xproj, float("nan"))
+    da = torch.full((w.G, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
+    dh0 = torch.full((rows, w.S, w.d_h), float("nan"), dtype=dt, device="cuda") if want_dh0 else None
+    ws_n = B.prn_backward_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, n_seqs=n_seqs)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    h0_d = None if h0 is None else to_dev(h0, w.dtype)
+    B.prn_newton_backward(xproj, a, states, dH, dx, da, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, dstate_last=dsl,
+                          dh0_out=dh0, workspace=ws)
+    torch.cuda.synchronize()
+    return dx, da, dh0
+
+
+def oracle_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None):
+    cu = inp["cu_seqlens"] if cu is None else cu
+    return obackward.adjoint(w.cell, to_f64(xproj), inp["a"].astype(np.float64), to_f64(states), to_f64(dH),
+                             h0=None if h0 is None else oround.store(h0, w.dtype), cu_seqlens=cu,
+                             dstate_last=None if dsl is None else to_f64(dsl))
+
+
+def random_grads(w, rows, seed):
+    rng = np.random.default_rng(seed)
+    dH = to_dev(rng.standard_normal((w.B, w.T, w.d_h)), w.dtype)
+    dsl = to_dev(rng.standard_normal((rows, w.S, w.d_h)), w.dtype)
+    return dH, dsl
+
+
+# head-mix GRU (dense 16 x 16 blocks per head), fp32 storage
+
+
+def hm_inputs(Bn, T, d_h, seed, scale=0.5, with_h0=True):
+    rng = np.random.default_rng(seed)
+    xp = rng.standard_normal((Bn, T, 3, d_h)).astype(np.float32).astype(np.float64)
+    A = (rng.uniform(-scale, scale, (3, d_h // 16, 16, 16)) / 4.0).astype(np.float32).astype(np.float64)
+    h0 = (0.5 * rng.standard_normal((Bn, d_h))).astype(np.float32).astype(np.float64) if with_h0 else None
+    return xp, A, h0
+
+
+def hm_dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def hm_newton(xp, A, K, h0=None, want_last=False):
+    Bn, T, _, d_h = xp.shape
+    H = torch.empty((Bn, T, d_h), device="cuda")
+    res = torch.full((K + 1,), -1.0, device="cuda")
+    last = torch.empty((Bn, d_h), device="cuda") if want_last else None
+    ws = torch.empty(max(B.prn_head_workspace_bytes(Bn, T, d_h, K), 1), dtype=torch.uint8, device="cuda")
+    B.prn_head_newton_forward(hm_dev(xp), hm_dev(A), K, H, h0=hm_dev(h0), residual_out=res, state_last_out=last,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    return to_f64(H), res.cpu().numpy().astype(np.float64), (None if last is None else to_f64(last))
+
+
+def hm_sequential(xp, A, h0=None):
+    Bn, T, _, d_h = xp.shape
+    H = torch.empty((Bn, T, d_h), device="cuda")
+    last = torch.empty((Bn, d_h), device="cuda")
+    B.prn_head_sequential_forward(hm_dev(xp), hm_dev(A), H, h0=hm_dev(h0), state_last_out=last)
+    torch.cuda.synchronize()
+    return to_f64(H), to_f64(last)
+
+
 __all__ = ["prn", "say", "to_dev", "to_f64", "gpu_run", "gpu_run_fused", "gpu_sequential", "oracle_newton", "oracle_sequential",
-           "tol", "small_inputs", "TORCH_DT"]
+           "tol", "small_inputs", "TORCH_DT", "rel_err", "tols", "gpu_forward_states", "gpu_backward", "oracle_backward",
+           "random_grads", "hm_inputs", "hm_dev", "hm_newton", "hm_sequential"]

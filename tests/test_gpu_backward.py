@@ -14,10 +14,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TORCH_DT, gpu_run, say, small_inputs, to_dev, to_f64
-from nonlinear_rnn_amd import binding as B
+from gpu_helpers import (TORCH_DT, gpu_backward, gpu_forward_states, oracle_backward, random_grads, rel_err, say,
+                         small_inputs, to_dev, to_f64, tols)
 from oracle import backward as obackward
-from oracle import rounding as oround
 from workloads import Workload, WORKLOADS, random_state
 
 pytestmark = pytest.mark.gpu
@@ -40,69 +39,6 @@ def algo(request, monkeypatch):
     three-phase kernels.  The library reads PRN_ALGO at every call."""
     monkeypatch.setenv("PRN_ALGO", request.param)
     return request.param
-
-
-def rel_err(got, ref):
-    return float(np.abs(got - ref).max() / (1.0 + np.abs(ref).max())) if ref.size else 0.0
-
-
-def tols(w):
-    return (1e-5, 1e-4) if w.dtype == "f32" else (1e-2, 1e-4)
-
-
-def gpu_forward_states(w, inp, K, h0=None, cu=None, xproj=None):
-    """Newton forward with states_out; returns (xproj, H, states, last)."""
-    dt = TORCH_DT[w.dtype]
-    out = gpu_run(w, inp, K, h0=h0, cu=cu, xproj=xproj)
-    xproj = out["xproj"]
-    a = torch.from_numpy(inp["a"]).cuda()
-    cu = inp["cu_seqlens"] if cu is None else cu
-    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
-    n_seqs = 0 if cu is None else len(cu) - 1
-    rows = w.B if cu is None else n_seqs
-    H = torch.empty((w.B, w.T, w.d_h), dtype=dt, device="cuda")
-    states = torch.full((w.B, w.T, w.S, w.d_h), float("nan"), dtype=dt, device="cuda")
-    last = torch.empty((rows, w.S, w.d_h), dtype=dt, device="cuda")
-    ws_n = B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, K, n_seqs=n_seqs)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-    h0_d = None if h0 is None else to_dev(h0, w.dtype)
-    B.prn_newton_forward(xproj, a, K, H, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, state_last_out=last,
-                         states_out=states, workspace=ws)
-    torch.cuda.synchronize()
-    return xproj, H, states, last
-
-
-def gpu_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None, want_dh0=True):
-    dt = TORCH_DT[w.dtype]
-    a = torch.from_numpy(inp["a"]).cuda()
-    cu = inp["cu_seqlens"] if cu is None else cu
-    cu_d = None if cu is None else torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
-    n_seqs = 0 if cu is None else len(cu) - 1
-    rows = w.B if cu is None else n_seqs
-    dx = torch.full_like(xproj, float("nan"))
-    da = torch.full((w.G, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
-    dh0 = torch.full((rows, w.S, w.d_h), float("nan"), dtype=dt, device="cuda") if want_dh0 else None
-    ws_n = B.prn_backward_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, n_seqs=n_seqs)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-    h0_d = None if h0 is None else to_dev(h0, w.dtype)
-    B.prn_newton_backward(xproj, a, states, dH, dx, da, cell=w.cell, h0=h0_d, cu_seqlens=cu_d, dstate_last=dsl,
-                          dh0_out=dh0, workspace=ws)
-    torch.cuda.synchronize()
-    return dx, da, dh0
-
-
-def oracle_backward(w, inp, xproj, states, dH, *, h0=None, cu=None, dsl=None):
-    cu = inp["cu_seqlens"] if cu is None else cu
-    return obackward.adjoint(w.cell, to_f64(xproj), inp["a"].astype(np.float64), to_f64(states), to_f64(dH),
-                             h0=None if h0 is None else oround.store(h0, w.dtype), cu_seqlens=cu,
-                             dstate_last=None if dsl is None else to_f64(dsl))
-
-
-def random_grads(w, rows, seed):
-    rng = np.random.default_rng(seed)
-    dH = to_dev(rng.standard_normal((w.B, w.T, w.d_h)), w.dtype)
-    dsl = to_dev(rng.standard_normal((rows, w.S, w.d_h)), w.dtype)
-    return dH, dsl
 
 
 @pytest.mark.parametrize("w", SMALL, ids=IDS)

@@ -12,44 +12,11 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import say, to_f64
+from gpu_helpers import hm_dev as dev, hm_inputs as inputs, hm_newton as gpu_newton, hm_sequential as gpu_sequential, say, to_f64
 from nonlinear_rnn_amd import binding as B
 from oracle import headmix as ohm
 
 pytestmark = pytest.mark.gpu
-
-
-def inputs(Bn, T, d_h, seed, scale=0.5, with_h0=True):
-    rng = np.random.default_rng(seed)
-    xp = rng.standard_normal((Bn, T, 3, d_h)).astype(np.float32).astype(np.float64)
-    A = (rng.uniform(-scale, scale, (3, d_h // 16, 16, 16)) / 4.0).astype(np.float32).astype(np.float64)
-    h0 = (0.5 * rng.standard_normal((Bn, d_h))).astype(np.float32).astype(np.float64) if with_h0 else None
-    return xp, A, h0
-
-
-def dev(a):
-    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
-
-
-def gpu_newton(xp, A, K, h0=None, want_last=False):
-    Bn, T, _, d_h = xp.shape
-    H = torch.empty((Bn, T, d_h), device="cuda")
-    res = torch.full((K + 1,), -1.0, device="cuda")
-    last = torch.empty((Bn, d_h), device="cuda") if want_last else None
-    ws = torch.empty(max(B.prn_head_workspace_bytes(Bn, T, d_h, K), 1), dtype=torch.uint8, device="cuda")
-    B.prn_head_newton_forward(dev(xp), dev(A), K, H, h0=dev(h0), residual_out=res, state_last_out=last,
-                              workspace=ws)
-    torch.cuda.synchronize()
-    return to_f64(H), res.cpu().numpy().astype(np.float64), (None if last is None else to_f64(last))
-
-
-def gpu_sequential(xp, A, h0=None):
-    Bn, T, _, d_h = xp.shape
-    H = torch.empty((Bn, T, d_h), device="cuda")
-    last = torch.empty((Bn, d_h), device="cuda")
-    B.prn_head_sequential_forward(dev(xp), dev(A), H, h0=dev(h0), state_last_out=last)
-    torch.cuda.synchronize()
-    return to_f64(H), to_f64(last)
 
 
 # (B, T, d_h, seed): several 32-step chunks with a ragged tail, exactly one

@@ -18,11 +18,10 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (TORCH_DT, gpu_run, gpu_run_fused, gpu_sequential, oracle_newton, oracle_sequential, say,
-                         to_f64, tol)
+from gpu_helpers import (TORCH_DT, gpu_backward, gpu_forward_states, gpu_run, gpu_run_fused, gpu_sequential, hm_inputs,
+                         hm_newton, hm_sequential, oracle_backward, oracle_newton, oracle_sequential, random_grads,
+                         rel_err, say, to_f64, tol, tols)
 from oracle import headmix as ohm
-from test_gpu_backward import gpu_backward, gpu_forward_states, oracle_backward, random_grads, rel_err, tols
-from test_gpu_headmix import gpu_newton as hm_newton, gpu_sequential as hm_sequential, inputs as hm_inputs
 from workloads import Workload, make_inputs, random_state
 
 pytestmark = pytest.mark.gpu
