@@ -229,3 +229,31 @@ def test_picard_warm_start(cell):
     guess = f(np.concatenate([h0[:, None], np.zeros((B, T - 1, S, d))], axis=1), xp, a)  # one sweep from 0
     heads = on.head_segments(B, T)
     assert g1["residuals"][0] == on.residual(cell, guess, xp, a, heads, h0)
+
+
+def test_oracle_reproduces_the_recorded_convergence_of_the_tiny_gru():
+    """The oracle, fed by the workload generator, reproduces the errors and
+    residuals an independent float64 script recorded for the 1 x 1024 GRU
+    workload (tests/golden/gru_tiny_newton_convergence.txt).  This pins the
+    input recipe (draw order, float64 draws cast to float32, W scaling) and
+    the oracle's Newton and residual together."""
+    import os
+
+    from oracle import proj as oproj
+    from oracle import rounding as oround
+    from workloads import WORKLOADS, make_inputs
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "gru_tiny_newton_convergence.txt")
+    rows = [list(map(float, ln.split())) for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    w = WORKLOADS["gru_tiny"]
+    inp = make_inputs(w, seed=0)
+    xp = oproj.input_proj(oround.load(inp["x"], "f32"), oround.load(inp["W"], "f32"),
+                          inp["bias"].astype(np.float64), w.G)
+    a = inp["a"].astype(np.float64)
+    seq, _ = newton.sequential("gru", xp, a)
+    for K, err_want, r_want in rows:
+        out = newton.newton("gru", xp, a, int(K))
+        err = np.abs(out["H"][..., 0, :] - seq[..., 0, :]).max()
+        assert abs(err - err_want) <= 5e-3 * err_want, (K, err, err_want)
+        r = out["residuals"][int(K) - 1]
+        assert abs(r - r_want) <= 5e-3 * r_want, (K, r, r_want)

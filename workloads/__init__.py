@@ -117,7 +117,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     """
     rng = np.random.default_rng(seed)
     G, d_h, d_in = w.G, w.d_h, w.d_in
-    x = rng.standard_normal((w.B, w.T, d_in), dtype=np.float32)
+    # every draw is float64 (numpy's default), then cast to the storage dtype
+    x = rng.standard_normal((w.B, w.T, d_in)).astype(np.float32)
     W = (rng.standard_normal((G * d_h, d_in)) / math.sqrt(d_in)).astype(np.float32)
     a = rng.uniform(-0.5, 0.5, (G, d_h)).astype(np.float32)
     bias = np.zeros(G * d_h, dtype=np.float32)
