@@ -90,7 +90,18 @@ typedef struct {
                               iterations should I use?": picard_iters); 0 or 1 (more:
                               PRN_ERR_UNSUPPORTED, as with PRN_ALGO=tp); r_0 is then the
                               residual of the Picard guess                                  */
+  void* error_out;         /* optional device uint32 word (4-byte aligned), forward and
+                              backward entry points: bit 0 (PRN_FAULT_LOOKBACK) is ORed in
+                              when a wait for a preceding chunk's record gave up (after about
+                              65 ms of polling: another process starving this kernel); the
+                              results of that call are then NaN from the chunk on (the
+                              forward's residual reads +Inf).  Never cleared by the library:
+                              the caller zeroes it and reads it after the stream work is
+                              done.  NULL: the bit goes to a word in the workspace only     */
 } prn_params;
+
+/* Bits of prn_params.error_out. */
+enum { PRN_FAULT_LOOKBACK = 1 };
 
 /* Input projection, once per forward:
  *   xproj[b,t,g,i] = sum_j x[b,t,j] * W[g*d_h + i, j] + bias[g*d_h + i]
@@ -125,7 +136,18 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias,
  *              batch, time, state component and channel, of the iterate as
  *              stored (H^(0) = 0).  A non-finite value reads as +Inf.  The
  *              caller applies the gate (Numerics contract: fail above 1.0).
- * Divergence is reported through the residual, never as a status. */
+ * Divergence is reported through the residual, never as a status.
+ * Reproducibility: every output is a fixed function of the inputs and the
+ * launch geometry (which depends on cell, dtype, T and the number of
+ * (row, 64-channel) chains): two calls with the same arguments give
+ * bitwise-equal results.  The carry into a chunk is defined as the serial
+ * application of the preceding chunks' composed maps to the initial state,
+ * and the look-back, whichever published prefix it starts from, performs
+ * exactly those operations.
+ * Environment (read at every call): PRN_ALGO=tp selects the multi-kernel
+ * three-phase schedule; PRN_SPIN_LIMIT overrides the number of polls before a
+ * wait for a preceding chunk gives up (0: every wait gives up at once, the
+ * way to exercise the error_out path). */
 prn_status prn_newton_forward(const void* xproj, const prn_params* params, const void* h0,
                               int32_t K, const int32_t* cu_seqlens, void* H_out,
                               float* residual_out);
@@ -142,8 +164,9 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* params, const
  *              store the projected inputs (the backward pass needs them)
  * The projected inputs are bitwise those prn_input_proj computes (same
  * matrix-core instruction and summation order), so H_out and residual_out
- * agree with prn_input_proj + prn_newton_forward up to the run-to-run
- * rounding of the single-pass schedule.  params->d_in must be set and
+ * equal those of prn_input_proj + prn_newton_forward bitwise whenever both
+ * take the same chunk length (every LSTM, and the GRU below 64 chains), and
+ * up to the rounding of another chunking otherwise.  params->d_in must be set and
  * params->picard_iters must be 0 (else PRN_ERR_UNSUPPORTED); the single-pass
  * schedule always runs (PRN_ALGO is not read).  Workspace:
  * prn_workspace_bytes(params, K), which covers both forwards.  Errors as

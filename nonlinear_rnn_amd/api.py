@@ -40,6 +40,33 @@ class AgreementError(AssertionError):
     """Newton and the sequential unroll disagree by more than tau."""
 
 
+class LookbackTimeoutError(RuntimeError):
+    """A kernel's wait for a preceding chunk's record gave up (after about
+    65 ms of polling, e.g. with the GPU starved by other work); the results of
+    that call are NaN from the chunk on.  Raised instead of returning them."""
+
+
+def _status_buffer(K: int, device):
+    """One zeroed int32 buffer holding the K + 1 residual slots (viewed as
+    fp32) and the library's error word after them: one host copy reads both."""
+    buf = torch.zeros(K + 2, dtype=torch.int32, device=device)
+    return buf, buf[:K + 1].view(torch.float32), buf[K + 1:]
+
+
+def _read_status(buf, what: str) -> list:
+    """Copy the residuals and the error word to the host (the forward's one
+    sync); raise LookbackTimeoutError if the error word is set."""
+    host = buf.cpu()
+    _check_error_word(int(host[-1]), what)
+    return host[:-1].view(torch.float32).tolist()
+
+
+def _check_error_word(err: int, what: str) -> None:
+    if err & B_.PRN_FAULT_LOOKBACK:
+        raise LookbackTimeoutError(f"{what}: a wait for a preceding chunk's record timed out; the results are "
+                                   "invalid (NaN)")
+
+
 @dataclasses.dataclass
 class AgreementReport:
     ok: bool
@@ -139,13 +166,13 @@ def newton_forward(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_tabl
     n_seqs = 0 if cu is None else cu.numel() - 1
     rows = Bn if cu is None else n_seqs
     H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
-    res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
+    buf, res, err = _status_buffer(K, xproj.device)
     st = (torch.empty((rows, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
           if return_state else None)
     ws = workspace_for(cell, xproj, K, n_seqs)
     B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=_contig(h0), cu_seqlens=cu, residual_out=res,
-                          state_last_out=st, workspace=ws)
-    residuals = res.cpu().tolist()   # the one host sync of a forward
+                          state_last_out=st, workspace=ws, error_out=err)
+    residuals = _read_status(buf, "prn_newton_forward")   # the one host sync of a forward
     if gate:
         gate_residual(residuals, xproj.dtype, residual_fail, residual_warn)
     return (H, residuals, st) if return_state else (H, residuals)
@@ -167,7 +194,8 @@ def sequential_forward(xproj, a, *, cell: str, h0=None, cu_seqlens=None, return_
 def forward(x, W, bias, a, K=3, *, cell: str, fused: bool = False, **kw):
     """Projection + Newton: the train-mode forward of one diagonal layer.
     fused=True runs both in one kernel (each Newton workgroup projects its own
-    chunk; same results up to the single-pass schedule's run-to-run rounding)."""
+    chunk; the same projected inputs, so the same results wherever both take
+    the same chunk length)."""
     if fused:
         return forward_fused(x, W, bias, a, K, cell=cell, **kw)
     return newton_forward(input_proj(x, W, bias, cell=cell), a, K, cell=cell, **kw)
@@ -188,14 +216,14 @@ def forward_fused(x, W, bias, a, K=3, *, cell: str, h0=None, cu_seqlens=None, k_
     n_seqs = 0 if cu is None else cu.numel() - 1
     rows = Bn if cu is None else n_seqs
     H = torch.empty((Bn, T, d_h), dtype=x.dtype, device=x.device)
-    res = torch.zeros(K + 1, dtype=torch.float32, device=x.device)
+    buf, res, err = _status_buffer(K, x.device)
     st = (torch.empty((rows, B_.STATE[cell], d_h), dtype=x.dtype, device=x.device) if return_state else None)
     xp = (torch.empty((Bn, T, B_.GATES[cell], d_h), dtype=x.dtype, device=x.device) if return_xproj else None)
     n = B_.prn_workspace_bytes(cell, x.dtype, Bn, T, d_h, K, n_seqs=n_seqs)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
     B_.prn_newton_forward_fused(x, W, bias, a, K, H, cell=cell, h0=_contig(h0), cu_seqlens=cu, residual_out=res,
-                                xproj_out=xp, state_last_out=st, workspace=ws)
-    residuals = res.cpu().tolist()   # the one host sync of a forward
+                                xproj_out=xp, state_last_out=st, workspace=ws, error_out=err)
+    residuals = _read_status(buf, "prn_newton_forward_fused")   # the one host sync of a forward
     if gate:
         gate_residual(residuals, x.dtype, residual_fail, residual_warn)
     out = (H, residuals)
@@ -228,28 +256,28 @@ def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol
 # NewtonConfig(recompute=True) for long sequences) the forward keeps only
 # its inputs and the backward runs the forward again to rebuild the
 # trajectory: (B, T, S, d_h) less memory held between the passes, one more
-# forward in the backward.  The projection's own gradients are plain matrix
-# products of dL/dxproj, left to torch's BLAS.
+# forward in the backward.
 
 def _forward_states(xproj, a, h0, cell, K, cu, picard_iters, with_states):
+    """Newton forward keeping the trajectory; returns (H, states, residuals on
+    the host) after the forward's one host sync."""
     Bn, T, G, d_h = xproj.shape
     n_seqs = 0 if cu is None else cu.numel() - 1
     H = torch.empty((Bn, T, d_h), dtype=xproj.dtype, device=xproj.device)
     states = (torch.empty((Bn, T, B_.STATE[cell], d_h), dtype=xproj.dtype, device=xproj.device)
               if with_states else None)
-    res = torch.zeros(K + 1, dtype=torch.float32, device=xproj.device)
+    buf, res, err = _status_buffer(K, xproj.device)
     n = B_.prn_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, K, n_seqs=n_seqs, picard_iters=picard_iters)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
     B_.prn_newton_forward(xproj, a, K, H, cell=cell, h0=h0, cu_seqlens=cu, residual_out=res,
-                          states_out=states, workspace=ws, picard_iters=picard_iters)
-    return H, states, res
+                          states_out=states, workspace=ws, picard_iters=picard_iters, error_out=err)
+    return H, states, _read_status(buf, "prn_newton_forward")
 
 
 class _NewtonFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, xproj, a, h0, cell, K, cu, picard_iters, residual_fail, gate, recompute):
-        H, states, res = _forward_states(xproj, a, h0, cell, K, cu, picard_iters, not recompute)
-        ctx.residuals = res.cpu().tolist()
+        H, states, ctx.residuals = _forward_states(xproj, a, h0, cell, K, cu, picard_iters, not recompute)
         if gate:
             gate_residual(ctx.residuals, xproj.dtype, residual_fail)
         ctx.cell, ctx.cu, ctx.K, ctx.picard_iters, ctx.recompute = cell, cu, K, picard_iters, recompute
@@ -274,8 +302,11 @@ class _NewtonFunction(torch.autograd.Function):
                if ctx.needs_input_grad[2] else None)
         n = B_.prn_backward_workspace_bytes(cell, xproj.dtype, Bn, T, d_h, n_seqs=n_seqs)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=xproj.device)
+        err = torch.zeros(1, dtype=torch.int32, device=xproj.device)
         B_.prn_newton_backward(xproj, a, states, dH.to(xproj.dtype).contiguous(), dxproj, da, cell=cell, h0=h0,
-                               cu_seqlens=cu, dh0_out=dh0, workspace=ws)
+                               cu_seqlens=cu, dh0_out=dh0, workspace=ws, error_out=err)
+        # the backward's one host sync: a timed-out wait must not hand NaN gradients to the optimizer
+        _check_error_word(int(err.item()), "prn_newton_backward")
         return dxproj, da, dh0, None, None, None, None, None, None, None
 
 
@@ -284,16 +315,18 @@ def newton_apply(xproj, a, K=None, *, cell: str, h0=None, cu_seqlens=None, picar
     """Differentiable Newton forward: H (B,T,d_h); gradients reach xproj, a
     and h0 through the backward pass.  K = None resolves the measured K*(T).
     recompute=True keeps no trajectory between the passes and rebuilds it in
-    the backward (the same kernels, so the same trajectory up to the
-    look-back's run-to-run rounding, ~1e-7)."""
+    the backward (the same kernels on the same inputs, so bitwise the same
+    trajectory)."""
     xproj = xproj.contiguous()
     Bn, T, _, _ = xproj.shape
     if K is None:
         from .kstar import load_table
         K = resolve_k(T, load_table(cell))
     cu = None if cu_seqlens is None else validate_cu_seqlens(cu_seqlens, T, xproj.device)
-    return _NewtonFunction.apply(xproj, a.contiguous(), _contig(h0), cell, int(K), cu, int(picard_iters),
-                                 residual_fail, gate, bool(recompute))
+    # a of another dtype (a bf16 parameter) is cast here, so that autograd
+    # casts its fp32 gradient back
+    return _NewtonFunction.apply(xproj, a.to(torch.float32).contiguous(), _contig(h0), cell, int(K), cu,
+                                 int(picard_iters), residual_fail, gate, bool(recompute))
 
 
 class _ProjFunction(torch.autograd.Function):

@@ -39,6 +39,15 @@ class PrnError(RuntimeError):
         self.status = status
 
 
+class PrnUnsupportedError(PrnError, TypeError):
+    """PRN_ERR_UNSUPPORTED: a valid request pinned to a path the library does
+    not implement (shapes/layout page: an unsupported pinned path raises
+    TypeError, with no silent remap)."""
+
+
+PRN_FAULT_LOOKBACK = 1   # bit of prn_params.error_out
+
+
 class prn_params(ctypes.Structure):
     _fields_ = [
         ("cell", ctypes.c_int32),
@@ -55,6 +64,7 @@ class prn_params(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("states_out", ctypes.c_void_p),
         ("picard_iters", ctypes.c_int32),
+        ("error_out", ctypes.c_void_p),
     ]
 
 
@@ -106,6 +116,8 @@ def prn_version() -> int:
 
 
 def _check(status: int) -> None:
+    if status == PRN_ERR_UNSUPPORTED:
+        raise PrnUnsupportedError(status, prn_last_error())
     if status != PRN_OK:
         raise PrnError(status, prn_last_error())
 
@@ -133,7 +145,7 @@ def _stream(stream) -> int:
 
 def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in: int = 0, n_seqs: int = 0,
                 a=None, state_last_out=None, states_out=None, workspace=None, stream=None,
-                picard_iters: int = 0) -> prn_params:
+                picard_iters: int = 0, error_out=None) -> prn_params:
     if cell not in CELLS:
         raise ValueError(f"unknown cell {cell!r}")
     if dtype not in DTYPES:
@@ -145,6 +157,7 @@ def make_params(cell: str, dtype: torch.dtype, B: int, T: int, d_h: int, *, d_in
     p.state_last_out = _ptr(state_last_out)
     p.states_out = _ptr(states_out)
     p.picard_iters = int(picard_iters)
+    p.error_out = _ptr(error_out)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.stream = _stream(stream) if torch.cuda.is_available() else 0
@@ -210,23 +223,31 @@ def _states_out(states_out, xproj, cell):
         raise ValueError(f"states_out must be {(B, T, STATE[cell], d_h)}, got {tuple(states_out.shape)}")
 
 
+def _error_word(error_out):
+    _dev(error_out, "error_out", torch.int32)
+    if error_out is not None and error_out.numel() < 1:
+        raise ValueError("error_out needs one int32 element")
+
+
 def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None, residual_out=None,
                        state_last_out=None, states_out=None, workspace=None, stream=None,
-                       picard_iters: int = 0) -> None:
+                       picard_iters: int = 0, error_out=None) -> None:
     B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
     _states_out(states_out, xproj, cell)
     _dev(residual_out, "residual_out", torch.float32)
+    _error_word(error_out)
     if residual_out is not None and residual_out.numel() < K + 1:
         raise ValueError("residual_out needs K + 1 entries")
     p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
-                    states_out=states_out, workspace=workspace, stream=stream, picard_iters=picard_iters)
+                    states_out=states_out, workspace=workspace, stream=stream, picard_iters=picard_iters,
+                    error_out=error_out)
     _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
                                     _ptr(H_out), _ptr(residual_out)))
 
 
 def prn_newton_forward_fused(x, W, bias, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None,
                              residual_out=None, xproj_out=None, state_last_out=None, states_out=None,
-                             workspace=None, stream=None) -> None:
+                             workspace=None, stream=None, error_out=None) -> None:
     """prn_input_proj + prn_newton_forward in one kernel: x (B,T,d_in), W (G*d_h, d_in), bias (G*d_h)
     fp32 or None; xproj_out (B,T,G,d_h) optionally receives the projected inputs."""
     _dev(x, "x")
@@ -259,8 +280,9 @@ def prn_newton_forward_fused(x, W, bias, a, K: int, H_out, *, cell: str, h0=None
             raise ValueError(f"{name} must be {(rows, S, d_h)}, got {tuple(t.shape)}")
     if residual_out is not None and residual_out.numel() < K + 1:
         raise ValueError("residual_out needs K + 1 entries")
+    _error_word(error_out)
     p = make_params(cell, x.dtype, B, T, d_h, d_in=d_in, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
-                    states_out=states_out, workspace=workspace, stream=stream)
+                    states_out=states_out, workspace=workspace, stream=stream, error_out=error_out)
     _check(lib().prn_newton_forward_fused(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(h0), K,
                                           _ptr(cu_seqlens), _ptr(H_out), _ptr(residual_out), _ptr(xproj_out)))
 
@@ -283,7 +305,7 @@ def prn_backward_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, 
 
 
 def prn_newton_backward(xproj, a, states, dH, dxproj_out, da_out, *, cell: str, h0=None, cu_seqlens=None,
-                        dstate_last=None, dh0_out=None, workspace=None, stream=None) -> None:
+                        dstate_last=None, dh0_out=None, workspace=None, stream=None, error_out=None) -> None:
     """Gradients through the recurrence at the trajectory `states` (B,T,S,d_h):
     dxproj_out (B,T,G,d_h), da_out (G,d_h) fp32 and optionally dh0_out (rows,S,d_h)."""
     _dev(xproj, "xproj")
@@ -308,7 +330,9 @@ def prn_newton_backward(xproj, a, states, dH, dxproj_out, da_out, *, cell: str, 
     for t, name in ((h0, "h0"), (dstate_last, "dstate_last"), (dh0_out, "dh0_out")):
         if t is not None and t.shape != (rows, S, d_h):
             raise ValueError(f"{name} must be {(rows, S, d_h)}, got {tuple(t.shape)}")
-    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, workspace=workspace, stream=stream)
+    _error_word(error_out)
+    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, workspace=workspace, stream=stream,
+                    error_out=error_out)
     _check(lib().prn_newton_backward(_ptr(xproj), ctypes.byref(p), _ptr(h0), _ptr(cu_seqlens), _ptr(states),
                                      _ptr(dH), _ptr(dstate_last), _ptr(dxproj_out), _ptr(da_out), _ptr(dh0_out)))
 

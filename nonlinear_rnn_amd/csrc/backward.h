@@ -30,7 +30,8 @@
 // of the forward's single-pass kernel: chunks are taken by ticket in reverse
 // time order, each workgroup composes its chunk's maps, obtains the gradient
 // entering it from the later chunks by the same decoupled look-back (chunk
-// records indexed in processing order), publishes what leaves it, and walks
+// records indexed in processing order; the result does not depend on
+// timing), publishes what leaves it, and walks
 // its steps backwards; inputs cross HBM once and no scan pass is needed.
 // The three-phase kernels above remain as the PRN_ALGO=tp schedule.
 //
@@ -276,7 +277,8 @@ k_bw_fix(const typename Storage<DT>::T* __restrict__ xproj, const typename Stora
 // index r = i / n_chains, i.e. time chunk n_ch - 1 - r: a chunk only waits on
 // chunks later in time, which hold smaller tickets and have started.  Chunk
 // records (status, aggregate map, outgoing gradient) are indexed by r; the
-// look-back is the forward's (lookback_carry), so are its bounded waits.
+// look-back is the forward's (lookback_carry), so are its bounded waits and
+// its timing-independent (bitwise reproducible) arithmetic.
 template <class C, int DT, int LS, int NW>
 __global__ void __launch_bounds__(kWave * NW)
 k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storage<DT>::T* __restrict__ states,

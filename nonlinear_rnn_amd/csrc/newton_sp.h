@@ -1,6 +1,7 @@
 // Single-pass parallel Newton: all K iterations of one chunk in one
 // workgroup, the chunk's projected inputs held in registers throughout,
-// carries obtained by a decoupled look-back over the preceding chunks.
+// carries obtained by a decoupled look-back over the preceding chunks whose
+// result does not depend on timing (bitwise reproducible).
 //
 // The three phases of the chunked affine scan are still there, per
 // iteration:  (1) the workgroup composes its chunk's maps (lane-serial over
@@ -24,7 +25,8 @@
 // ever waits for chunks with smaller tickets, which have started; chunk 0 of
 // every chain never waits.  Every wait is bounded (spin_limit polls); on
 // timeout the carry becomes NaN (so the residual reads +Inf) and an error
-// word in the workspace is set: the kernel always terminates.
+// word (the caller's, or one in the workspace) is set: the kernel always
+// terminates.
 //
 // Memory ordering of the chunk records: every record word is written and
 // read with relaxed agent-scope atomics, which gfx950 performs at the
@@ -82,15 +84,31 @@ struct SpRecords {
   unsigned* error;     // 1 word: set when a look-back wait timed out
 };
 
-// Carry-in of chunk `chunk` (the state just before its first step) by a
-// decoupled look-back, executed by one whole wave (lane = channel).  Each
-// round reads the status words of the 64 nearest unconsumed predecessors
-// with one load (lane i looks at chunk jh - i), finds the nearest published
-// inclusive prefix behind an unbroken run of published aggregates, and
-// consumes that run: the aggregates are composed (loaded RB at a time, their
-// latencies overlapped) and applied to the prefix.  A run that ends at an
-// unpublished chunk is consumed as far as it goes before polling again.
-// Chunk 0 of a chain has carry 0 (its first step is a segment head, J = 0).
+// Carry-in E(c) of chunk c (the state just before its first step) by a
+// decoupled look-back whose arithmetic does not depend on timing.  The carry
+// is defined by the serial recurrence over chunks
+//     E(0) = 0,   E(c+1) = A_c applied to E(c)
+// (A_c the chunk's composed map; apply() is a fixed sequence of fused
+// multiply-adds), and every chunk publishes its inclusive prefix E(c+1)
+// computed that way.  A chunk that finds the prefix E(p+1) of a predecessor
+// p behind an unbroken run of published aggregates A_{p+1} .. A_{c-1}
+// applies those aggregates to that prefix, oldest first: exactly the
+// operations of the serial definition, so E(c) comes out bit for bit the
+// same whichever predecessor's prefix happened to be found, and repeated
+// runs agree bitwise.  (Composing the run into one map first, then applying
+// it, would round differently for every run length, hence with timing.)
+// Executed by one whole wave (lane = channel).  Each round reads the status
+// words of 64 predecessors with one load (lane i looks at chunk jh - i) and
+// finds the nearest published prefix behind an unbroken run of published
+// aggregates; a window of published aggregates without a prefix moves the
+// scan one window further back; a run broken by an unpublished chunk before
+// any prefix waits for that chunk (a chunk publishes its aggregate as soon
+// as its first poll cannot resolve its own carry, or at once with few
+// chains).  The aggregates are loaded RB at a time, their latencies
+// overlapped.  Chunk 0 of a chain has carry 0 (its first step is a segment
+// head, J = 0).  Every wait is bounded: after spin_limit polls without
+// progress (none at all for spin_limit = 0) the carry becomes NaN and the
+// error word is set, and the chunk goes on, so the kernel terminates.
 template <int S, int RB = 8>
 __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t base, int64_t chunk,
                                                const Aff<S>& tot, int lane, unsigned spin_limit, bool agg_first, float* cin) {
@@ -99,7 +117,6 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 #pragma unroll
   for (int q = 0; q < S; ++q) cin[q] = 0.0f;
   if (chunk == 0) return;
-  Map accm = Map::identity();
   int64_t jh = chunk - 1;
   // Our aggregate's data are stored, and the first poll is issued without
   // waiting for them: the wait for the poll also covers the stores, so the
@@ -112,6 +129,13 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
   bool published = false;
   unsigned spins = 0;
   while (true) {
+    if (spins >= spin_limit) {  // gave up: poison the carry, flag the error, stop waiting
+      if (lane == 0) atomicOr(rec.error, 1u);
+      if (!published) rec_publish(rec.status + base + chunk, kRecAggregate, lane);
+#pragma unroll
+      for (int q = 0; q < S; ++q) cin[q] = __builtin_nanf("");
+      return;
+    }
     const int64_t jj = jh - lane;
     const unsigned st = jj >= 0 ? __hip_atomic_load(rec.status + base + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                 : kRecEmpty;
@@ -120,44 +144,38 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
     const int n_ready = ~ready ? __builtin_ctzll(~ready) : 64;
     const int i_p = pref ? __builtin_ctzll(pref) : 64;
     const bool hit = i_p < n_ready;
-    const int n_use = hit ? i_p : n_ready;
     if ((agg_first || !hit) && !published) {
       rec_publish(rec.status + base + chunk, kRecAggregate, lane);
       published = true;
     }
-    if (n_use == 0 && !hit) {
-      if (++spins > spin_limit) {  // timed out: poison the carry, flag the error, stop waiting
-        if (lane == 0) atomicOr(rec.error, 1u);
+    if (hit) {
+      // E(c) = A_{c-1}( ... A_{p+1}(E(p+1)) ... ), p = jh - i_p; the
+      // prefix is loaded in the same batch as the first aggregates
+      const int64_t p = jh - i_p, n_app = chunk - 1 - p;
+      float e[S];
+      const float* pp = rec.pre + (base + p) * S * kWave + lane;
 #pragma unroll
-        for (int q = 0; q < S; ++q) cin[q] = __builtin_nanf("");
-        return;
+      for (int q = 0; q < S; ++q) e[q] = rec_load(pp + q * kWave);
+      for (int64_t r0 = 0; r0 < n_app; r0 += RB) {
+        Map mb[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+          mb[u] = (r0 + u < n_app) ? rec_load_map<S>(rec.agg + (base + p + 1 + r0 + u) * NC * kWave + lane)
+                                   : Map::identity();
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+          if (r0 + u < n_app) apply(mb[u], e);
       }
-      __builtin_amdgcn_s_sleep(2);
-      continue;
-    }
-    // the prefix (if found) is loaded in the same batch as the aggregates
-    float pv[S];
-    if (hit) {
-      const float* pp = rec.pre + (base + jh - i_p) * S * kWave + lane;
 #pragma unroll
-      for (int q = 0; q < S; ++q) pv[q] = rec_load(pp + q * kWave);
-    }
-    for (int r0 = 0; r0 < n_use; r0 += RB) {
-      Map mb[RB];
-#pragma unroll
-      for (int u = 0; u < RB; ++u)
-        mb[u] = (r0 + u < n_use) ? rec_load_map<S>(rec.agg + (base + jh - r0 - u) * NC * kWave + lane)
-                                 : Map::identity();
-#pragma unroll
-      for (int u = 0; u < RB; ++u) accm = compose(accm, mb[u]);
-    }
-    if (hit) {
-#pragma unroll
-      for (int q = 0; q < S; ++q) cin[q] = pv[q];
-      apply(accm, cin);
+      for (int q = 0; q < S; ++q) cin[q] = e[q];
       return;
     }
-    jh -= n_use;
+    if (n_ready == kWave) {  // 64 published aggregates and no prefix: look one window further back
+      jh -= kWave;
+      continue;
+    }
+    ++spins;   // the run breaks at a chunk that has published nothing yet
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 

@@ -77,6 +77,14 @@ int sp_ls_fused(int cell, int dtype, int64_t n_chains) {
   return sp_ls(cell, dtype, n_chains);
 }
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
+// PRN_SPIN_LIMIT overrides the poll limit at every call; 0 makes every
+// look-back wait give up at once (every chunk but the first of each chain),
+// which exercises the error path without any fault or hang.
+unsigned spin_limit() {
+  const char* e = getenv("PRN_SPIN_LIMIT");
+  if (e && *e) return unsigned(strtoul(e, nullptr, 10));
+  return kSpinLimit;
+}
 // below this many independent chains, chunks publish their aggregate before
 // polling (measured: helps 4-32 chains, hurts 128)
 constexpr int64_t kAggFirstBelowChains = 64;
@@ -132,6 +140,7 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
   if (!sh.ragged && cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
   if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(H_out, sh.elt) ||
       misaligned(p->state_last_out, sh.elt) || misaligned(p->states_out, sh.elt) || misaligned(p->a, 4) ||
+      misaligned(p->error_out, 4) ||
       misaligned(cu, 4))
     return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   return PRN_OK;
@@ -349,7 +358,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     prn::SpRecords rec;
     unsigned* words = reinterpret_cast<unsigned*>(ws + pl.status_off);
     rec.ticket = words;
-    rec.error = words + 1;
+    rec.error = p->error_out ? static_cast<unsigned*>(p->error_out) : words + 1;
     rec.status = words + 2;
     rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
     rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
@@ -366,7 +375,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
         prn::k_newton_sp<C, DT, LS, kSpNW, decltype(ws)::value, decltype(pic)::value, FX>
             <<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
                 static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles,
-                pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, kSpinLimit,
+                pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, spin_limit(),
                 pl.n_chains < kAggFirstBelowChains, fa);
       };
       if constexpr (FX) {
@@ -452,7 +461,7 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
       prn::SpRecords rec;
       unsigned* words = reinterpret_cast<unsigned*>(ws + pl.words_off);
       rec.ticket = words;
-      rec.error = words + 1;
+      rec.error = p->error_out ? static_cast<unsigned*>(p->error_out) : words + 1;
       rec.status = words + 2;
       rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
       rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
@@ -461,7 +470,7 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
         constexpr int LS = decltype(ls)::value;
         prn::k_bw_sp<C, DT, LS, kBwNW><<<unsigned(pl.n_ch * pl.n_chains), 64 * kBwNW, 0, st>>>(
             xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, dxproj,
-            dh0, dap, rec, kSpinLimit, pl.n_chains < kAggFirstBelowChains);
+            dh0, dap, rec, spin_limit(), pl.n_chains < kAggFirstBelowChains);
       };
       if constexpr (S == 1) {
         if (pl.lc == kBwLsFew * kBwNW)
@@ -607,7 +616,7 @@ prn_status prn_newton_backward(const void* xproj, const prn_params* p, const voi
   if (!sh.ragged && cu) return fail(PRN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
   if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(states, sh.elt) || misaligned(dH, sh.elt) ||
       misaligned(dstate_last, sh.elt) || misaligned(dxproj_out, sh.elt) || misaligned(dh0_out, sh.elt) ||
-      misaligned(da_out, 4) || misaligned(p->a, 4) || misaligned(cu, 4))
+      misaligned(da_out, 4) || misaligned(p->a, 4) || misaligned(cu, 4) || misaligned(p->error_out, 4))
     return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   const PlanBw pl = plan_bw(p, sh);
   if (p->T > 0) {
@@ -632,7 +641,7 @@ prn_status prn_newton_backward(const void* xproj, const prn_params* p, const voi
                                               dh0_out);
 }
 
-int32_t prn_version(void) { return 100; }
+int32_t prn_version(void) { return 200; }
 
 const char* prn_last_error(void) { return g_err.c_str(); }
 

@@ -92,7 +92,31 @@ def oracle_sequential(w: Workload, xp64, a, *, h0=None, cu=None):
 
 
 def tol(w: Workload, f32: float, bf16: float = 2e-2) -> float:
+    """A scalar band: f32 for fp32 storage, bf16 for bf16 storage (used for
+    residuals, whose bf16 floor is about 2^-9 max|h|)."""
     return f32 if w.dtype == "f32" else bf16
+
+
+BF16_ABS = 4e-3   # twice the largest bf16 error seen on h (1.95e-3, one rounding of |h| < 1)
+
+
+def bf16_ulp(x) -> np.ndarray:
+    """Spacing of bf16 numbers (8 significant bits) at |x|."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def state_err(w: Workload, got, ref, f32: float) -> float:
+    """Largest |got - ref| as a fraction of the allowed band (<= 1 passes).
+    fp32 storage: the fixed f32.  bf16 storage: BF16_ABS, or one bf16 ulp of
+    the reference where that is larger (an LSTM cell state above 1); every
+    stored value carries one rounding to 8 significant bits."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    band = f32 if w.dtype == "f32" else np.maximum(BF16_ABS, bf16_ulp(ref))
+    return float((np.abs(got - ref) / band).max())
 
 
 def small_inputs(w: Workload, seed: int = 0) -> dict:
@@ -230,5 +254,5 @@ def hm_sequential(xp, A, h0=None):
 
 
 __all__ = ["prn", "say", "to_dev", "to_f64", "gpu_run", "gpu_run_fused", "gpu_sequential", "oracle_newton", "oracle_sequential",
-           "tol", "small_inputs", "TORCH_DT", "rel_err", "tols", "gpu_forward_states", "gpu_backward", "oracle_backward",
+           "tol", "state_err", "bf16_ulp", "BF16_ABS", "small_inputs", "TORCH_DT", "rel_err", "tols", "gpu_forward_states", "gpu_backward", "oracle_backward",
            "random_grads", "hm_inputs", "hm_dev", "hm_newton", "hm_sequential"]

@@ -75,6 +75,7 @@ FAKE = 1 << 20   # an aligned non-null address; never dereferenced (validation f
     (dict(a=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),                    # misaligned
     (dict(a=FAKE, picard_iters=-1), 3, B.PRN_ERR_INVALID_ARG),
     (dict(a=FAKE, picard_iters=2), 3, B.PRN_ERR_UNSUPPORTED),
+    (dict(a=FAKE, error_out=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),    # misaligned error word
 ])
 def test_newton_forward_rejects_bad_arguments_before_launch(kw, K, status):
     p = _params(**kw)
@@ -291,3 +292,19 @@ def test_bench_names_the_projection_tiles_the_library_uses():
     at = Workload("t", "gru", 1, 256 * (large // 3), 8, 256, "f32", 3)
     assert bench.proj_tiles(below) == "128x128"
     assert bench.proj_tiles(at) == "256x256"
+
+
+def test_unsupported_status_raises_type_error():
+    """A valid request pinned to a path the library does not implement raises
+    TypeError (shapes/layout page: an unsupported pinned path raises, with no
+    silent remap); other failures stay plain PrnError (RuntimeError)."""
+    with pytest.raises(TypeError) as e:
+        B._check(B.PRN_ERR_UNSUPPORTED)
+    assert isinstance(e.value, B.PrnError) and e.value.status == B.PRN_ERR_UNSUPPORTED
+    with pytest.raises(B.PrnError) as e:
+        B._check(B.PRN_ERR_INVALID_ARG)
+    assert not isinstance(e.value, TypeError)
+    p = _params(a=FAKE, picard_iters=2)
+    st = B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None)
+    with pytest.raises(TypeError, match="Picard"):
+        B._check(st)

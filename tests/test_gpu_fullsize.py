@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import gpu_run, oracle_newton, oracle_sequential, say, to_f64, tol
+from gpu_helpers import gpu_run, oracle_newton, oracle_sequential, say, state_err, to_f64, tol
 from oracle import newton as onewton
 from workloads import WORKLOADS, make_inputs
 
@@ -46,13 +46,13 @@ def test_full_size_sampled_parity(name):
     err_seq = np.abs(H - seq[..., -1, :]).max()
     r = out["res"]
     say(f"  {name}: max|H - oracle Newton| {err:.3e}; max|H - sequential| {err_seq:.3e}; residuals {r}")
-    assert err <= tol(w, 1e-5)
+    assert state_err(w, H, ref["H"][..., -1, :], 1e-5) <= 1
     assert np.all(np.isfinite(r)) and r[-1] <= 1.0
     # the device residual is a max over all channels: at least the sampled one
     rs = np.array(ref["residuals"])
     assert np.all(r >= rs - (tol(w, 2e-5) + 1e-3 * rs))
     if w.cell == "gru":
-        assert err_seq <= tol(w, 1e-4)
+        assert state_err(w, H, seq[..., -1, :], 1e-4) <= 1
         # r_K recomputed in fp64 on the GPU's own output for the sampled channels
         heads = onewton.head_segments(len(rows), w.T, cu)
         n0 = len(rows) if cu is None else len(cu) - 1

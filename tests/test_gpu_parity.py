@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (gpu_run, gpu_sequential, oracle_newton, oracle_sequential, say, small_inputs, to_dev,
+from gpu_helpers import (gpu_run, gpu_sequential, oracle_newton, oracle_sequential, say, small_inputs, state_err, to_dev,
                          to_f64, tol, TORCH_DT)
 import nonlinear_rnn_amd as prn
 from oracle import proj as oproj
@@ -77,9 +77,9 @@ def test_newton_matches_oracle_at_equal_K(w, algo):
     H = to_f64(out["H"])
     err = np.abs(H - ref["H"][..., -1, :]).max()
     say(f"  max|H_gpu - H_oracle| = {err:.3e}; residuals gpu {out['res']} oracle {ref['residuals']}")
-    assert err <= tol(w, 1e-5)
+    assert state_err(w, H, ref["H"][..., -1, :], 1e-5) <= 1
     last = to_f64(out["last"])
-    assert np.abs(last - ref["last"]).max() <= tol(w, 1e-5)
+    assert state_err(w, last, ref["last"], 1e-5) <= 1
     r_g, r_o = out["res"], np.array(ref["residuals"])
     bound = (2e-5 + 1e-3 * r_o) if w.dtype == "f32" else (2e-2 + 2e-2 * r_o)
     assert np.all(np.abs(r_g - r_o) <= bound), (r_g, r_o)
@@ -95,7 +95,7 @@ def test_newton_agrees_with_sequential_within_tau(w, algo):
     seq, _ = oracle_sequential(w, xp, inp["a"], cu=inp["cu_seqlens"])
     err = np.abs(to_f64(out["H"]) - seq[..., -1, :]).max()
     say(f"  max|H_newton - h_sequential| = {err:.3e}")
-    assert err <= tol(w, 1e-4)
+    assert state_err(w, to_f64(out["H"]), seq[..., -1, :], 1e-4) <= 1
 
 
 @pytest.mark.parametrize("w", SMALL, ids=IDS)
@@ -106,8 +106,8 @@ def test_sequential_kernel_matches_oracle(w):
     H, last = gpu_sequential(w, inp, out["xproj"])
     xp = xp64_of(w, out["xproj"])
     seq, slast = oracle_sequential(w, xp, inp["a"], cu=inp["cu_seqlens"])
-    assert np.abs(to_f64(H) - seq[..., -1, :]).max() <= tol(w, 1e-5)
-    assert np.abs(to_f64(last) - slast).max() <= tol(w, 1e-5)
+    assert state_err(w, to_f64(H), seq[..., -1, :], 1e-5) <= 1
+    assert state_err(w, to_f64(last), slast, 1e-5) <= 1
 
 
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[4]], ids=["gru_small", "gru_ragged_small"])
@@ -125,27 +125,24 @@ def test_final_residual_equals_recomputation_on_output(w, algo):
 
 @pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[4]], ids=lambda w: w.name)
 def test_run_to_run_reproducibility(w, algo):
-    """Three-phase: bitwise identical runs (fixed combination order).
-    Single-pass: the look-back folds a timing-dependent number of chunk
-    aggregates into a carry, so runs may differ by a few ulps; they must
-    agree to 1e-6 (fp32 storage) or one bf16 rounding step."""
+    """Both schedules combine the chunk carries in an order fixed by the
+    chunk index (the single-pass look-back by a binary decomposition of the
+    chunk index, never by which chunks happened to finish first): repeated
+    runs are bitwise identical."""
     say(f"[case] reproducibility {w}")
     inp = small_inputs(w)
     o1 = gpu_run(w, inp, w.K)
     for _ in range(3):
         o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
-        if algo == "tp":
-            assert torch.equal(o1["H"], o2["H"])
-            assert torch.equal(o1["last"], o2["last"])
-            assert np.array_equal(o1["res"], o2["res"])
-        else:
-            lim = 1e-6 if w.dtype == "f32" else 1e-2
-            assert (o1["H"].float() - o2["H"].float()).abs().max().item() <= lim
-            assert (o1["last"].float() - o2["last"].float()).abs().max().item() <= lim
-            assert np.all(np.abs(o1["res"] - o2["res"]) <= lim + 1e-5 * o1["res"])
+        assert torch.equal(o1["H"], o2["H"])
+        assert torch.equal(o1["last"], o2["last"])
+        assert np.array_equal(o1["res"], o2["res"])
 
 
 def test_batch_rows_are_independent(algo):
+    """A row computed alone equals the same row inside a batch, bit for bit
+    (same chunk boundaries, same arithmetic; the LSTM's chunk length does not
+    depend on the number of chains)."""
     w = SMALL[1]
     say(f"[case] batch independence {w}")
     inp = small_inputs(w)
@@ -153,12 +150,8 @@ def test_batch_rows_are_independent(algo):
     for b in range(w.B):
         wb = w.scaled(B=1)
         ob = gpu_run(wb, inp, w.K, xproj=full["xproj"][b:b + 1].contiguous())
-        if algo == "tp":   # same chunk boundaries, same arithmetic
-            assert torch.equal(ob["H"][0], full["H"][b])
-            assert torch.equal(ob["last"][0], full["last"][b])
-        else:
-            assert (ob["H"][0] - full["H"][b]).abs().max().item() <= 1e-6
-            assert (ob["last"][0] - full["last"][b]).abs().max().item() <= 1e-6
+        assert torch.equal(ob["H"][0], full["H"][b])
+        assert torch.equal(ob["last"][0], full["last"][b])
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
@@ -283,7 +276,7 @@ def test_single_pass_and_three_phase_agree(w, monkeypatch):
     o1 = gpu_run(w, inp, w.K)
     monkeypatch.setenv("PRN_ALGO", "tp")
     o2 = gpu_run(w, inp, w.K, xproj=o1["xproj"])
-    assert (o1["H"].float() - o2["H"].float()).abs().max().item() <= tol(w, 1e-5)
+    assert state_err(w, to_f64(o1["H"]), to_f64(o2["H"]), 1e-5) <= 1
     assert np.all(np.abs(o1["res"] - o2["res"]) <= tol(w, 2e-5) + 1e-3 * o2["res"])
 
 
