@@ -176,6 +176,25 @@ prn_status prn_newton_forward_fused(const void* x, const void* W, const float* b
                                     const int32_t* cu_seqlens, void* H_out, float* residual_out,
                                     void* xproj_out);
 
+/* prn_newton_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as prn_newton_forward (the
+ * single-pass schedule; PRN_ALGO is not read), but params->workspace and
+ * workspace_bytes are ignored: the scratch (chunk records, status words,
+ * residual partials) is a file-scope device array of
+ * PRN_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call);
+ * the first call on a device looks up that device's copy of the array.
+ * A call needing more scratch than the array holds (prn_workspace_bytes
+ * tells how much) returns PRN_ERR_WORKSPACE before anything is launched.
+ * Every call on a GPU shares its array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.
+ * The current device must be the stream's device. */
+#define PRN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+prn_status prn_newton_forward_noalloc(const void* xproj, const prn_params* params, const void* h0,
+                                      int32_t K, const int32_t* cu_seqlens, void* H_out,
+                                      float* residual_out);
+
 /* Sequential unroll s_t = f(s_{t-1}, x_t) (the eval-mode path and the truth
  * the Newton result must match within tau).  Arguments as for
  * prn_newton_forward.  Uses no workspace. */

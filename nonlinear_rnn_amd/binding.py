@@ -30,7 +30,8 @@ EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "
            "prn_workspace_bytes",
            "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_head_newton_forward",
            "prn_head_sequential_forward", "prn_head_workspace_bytes", "prn_validate_cu_seqlens",
-           "prn_last_error", "prn_version")
+           "prn_last_error", "prn_version", "prn_newton_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PRN_NOALLOC_SCRATCH_BYTES
 
 
 class PrnError(RuntimeError):
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.prn_input_proj.argtypes = [vp, vp, vp, P, vp]
         L.prn_newton_forward.argtypes = [vp, P, vp, i32, vp, vp, vp]
         L.prn_newton_forward_fused.argtypes = [vp, vp, vp, P, vp, i32, vp, vp, vp, vp]
+        L.prn_newton_forward_noalloc.argtypes = [vp, P, vp, i32, vp, vp, vp]
         L.prn_sequential_forward.argtypes = [vp, P, vp, vp, vp]
         L.prn_workspace_bytes.argtypes = [P, i32]
         L.prn_workspace_bytes.restype = ctypes.c_size_t
@@ -98,7 +100,8 @@ def lib() -> ctypes.CDLL:
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
-        for name in ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "prn_sequential_forward",
+        for name in ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "prn_newton_forward_noalloc",
+                     "prn_sequential_forward",
                      "prn_newton_backward",
                      "prn_decode_step", "prn_head_newton_forward", "prn_head_sequential_forward",
                      "prn_validate_cu_seqlens"):
@@ -243,6 +246,24 @@ def prn_newton_forward(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlen
                     error_out=error_out)
     _check(lib().prn_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
                                     _ptr(H_out), _ptr(residual_out)))
+
+
+def prn_newton_forward_noalloc(xproj, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None,
+                               residual_out=None, state_last_out=None, states_out=None, stream=None,
+                               picard_iters: int = 0, error_out=None) -> None:
+    """prn_newton_forward with the library's own static scratch instead of a
+    caller workspace (for callers that cannot allocate); calls on one GPU must
+    not overlap."""
+    B, T, d_h, n_seqs = _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell)
+    _states_out(states_out, xproj, cell)
+    _dev(residual_out, "residual_out", torch.float32)
+    _error_word(error_out)
+    if residual_out is not None and residual_out.numel() < K + 1:
+        raise ValueError("residual_out needs K + 1 entries")
+    p = make_params(cell, xproj.dtype, B, T, d_h, n_seqs=n_seqs, a=a, state_last_out=state_last_out,
+                    states_out=states_out, stream=stream, picard_iters=picard_iters, error_out=error_out)
+    _check(lib().prn_newton_forward_noalloc(_ptr(xproj), ctypes.byref(p), _ptr(h0), K, _ptr(cu_seqlens),
+                                            _ptr(H_out), _ptr(residual_out)))
 
 
 def prn_newton_forward_fused(x, W, bias, a, K: int, H_out, *, cell: str, h0=None, cu_seqlens=None,

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -556,9 +557,69 @@ prn_status check_head(const prn_params* p, Shape* sh, int32_t d_head) {
   return PRN_OK;
 }
 
+// ---- scratch of the allocation-free forward ----
+// One file-scope device array per GPU, alive until the process ends.  Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = PRN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+prn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PRN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PRN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PRN_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PRN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+prn_status prn_newton_forward_noalloc(const void* xproj, const prn_params* p, const void* h0, int32_t K,
+                                      const int32_t* cu, void* H_out, float* residual_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
+  if (p->picard_iters < 0) return fail(PRN_ERR_INVALID_ARG, "picard_iters must be >= 0");
+  if (p->picard_iters > 1)
+    return fail(PRN_ERR_UNSUPPORTED, "picard_iters = %d: one Picard sweep is supported", p->picard_iters);
+  if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
+  if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
+  const PlanSp pl = plan_sp(p, sh, K);
+  if (pl.total > kScratchBytes)
+    return fail(PRN_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the allocation-free forward holds %zu "
+                "(use prn_newton_forward with a caller workspace)", pl.total, kScratchBytes);
+  prn_params q = *p;
+  q.workspace = nullptr;
+  q.workspace_bytes = kScratchBytes;
+  if (p->T > 0 && (s = scratch_of_current_device(&q.workspace)) != PRN_OK) return s;
+  if (p->cell == PRN_CELL_DIAG_GRU) {
+    if (p->dtype == PRN_F32) return newton_sp<prn::CellGRU, prn::kF32>(&q, sh, xproj, h0, K, cu, H_out, residual_out);
+    return newton_sp<prn::CellGRU, prn::kBF16>(&q, sh, xproj, h0, K, cu, H_out, residual_out);
+  }
+  if (p->dtype == PRN_F32) return newton_sp<prn::CellLSTM, prn::kF32>(&q, sh, xproj, h0, K, cu, H_out, residual_out);
+  return newton_sp<prn::CellLSTM, prn::kBF16>(&q, sh, xproj, h0, K, cu, H_out, residual_out);
+}
 
 prn_status prn_decode_step(const void* x, const void* W, const float* bias, const prn_params* p,
                            const void* state_in, void* state_out, void* h_out) {

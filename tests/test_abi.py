@@ -308,3 +308,20 @@ def test_unsupported_status_raises_type_error():
     st = B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None)
     with pytest.raises(TypeError, match="Picard"):
         B._check(st)
+
+
+def test_noalloc_forward_rejects_calls_beyond_its_scratch_before_any_device_call():
+    """The allocation-free forward checks its scratch need on the host: a
+    call larger than the static array is PRN_ERR_WORKSPACE with a message that
+    names both sizes, before any HIP call (this runs without a GPU)."""
+    p = _params(cell=B.CELLS["lstm"], B=2, T=131072, d_h=256, a=FAKE)   # the long LSTM: ~67 MB of records
+    st = B.lib().prn_newton_forward_noalloc(FAKE, ctypes.byref(p), None, 2, None, FAKE, None)
+    assert st == B.PRN_ERR_WORKSPACE
+    msg = B.prn_last_error()
+    assert str(B.NOALLOC_SCRATCH_BYTES) in msg and "needs" in msg
+    need = int(re.search(r"needs (\d+) bytes", msg).group(1))
+    assert need == B.lib().prn_workspace_bytes(ctypes.byref(p), 2)
+    # argument checks come first, as for prn_newton_forward
+    p = _params(a=None)
+    assert B.lib().prn_newton_forward_noalloc(FAKE, ctypes.byref(p), None, 3, None, FAKE, None) == \
+        B.PRN_ERR_INVALID_ARG
