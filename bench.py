@@ -11,8 +11,12 @@ The other workloads (--workload) are parity cases; they can be timed too.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation; HIP events around every library call on the stream the
-kernels run on give per-call durations.  The CPU baseline times the oracle
-(NumPy, float64) on a bounded sample of the same workload.
+kernels run on give per-call durations.  Beside the step: the agreement of
+the result with the GPU unroll at the bench's K, the same forward at the
+measured K*(T), the backward, the fused forward, the decode step and the
+head-mix GRU.  CPU baselines: the oracle (NumPy, float64, one thread) on a
+bounded sample, and the unroll in plain C (float64, OpenMP, all host
+threads) on the whole workload.
 """
 from __future__ import annotations
 
@@ -77,13 +81,12 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this kernel and workload (FETCH_SIZE + WRITE_SIZE, each scaled by what a
-    512 MiB copy reads), or None if there is none or the kernels changed since."""
+def profile_fields(kernel: str, workload: str) -> dict:
+    """Fields of the committed rocprofv3 summary of this kernel and workload,
+    or {} if there is none or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     with open(path) as f:
         for line in f:
@@ -91,11 +94,22 @@ def profiled_traffic(kernel: str, workload: str):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
     if fields.get("source_hash") != kernel_source_hash(kernel):
-        return None
+        return {}
+    return fields
+
+
+def _field(fields: dict, key: str):
     try:
-        return float(fields["traffic_bytes_per_launch"].split()[0])
-    except (KeyError, ValueError):
+        return float(fields[key].split()[0])
+    except (KeyError, ValueError, IndexError):
         return None
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload (FETCH_SIZE + WRITE_SIZE, each scaled by what a
+    512 MiB copy reads), or None if there is none or the kernels changed since."""
+    return _field(profile_fields(kernel, workload), "traffic_bytes_per_launch")
 
 
 VALU_F32_PEAK_TFLOPS = 157.3
@@ -199,6 +213,31 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
                                             f"(numpy float64), 1 thread, {el_seq:.1f} s"}}
 
 
+def cpu_openmp_unroll(w, xproj_host, inp, cu) -> dict:
+    """The multi-core CPU baseline: the sequential unroll in plain C (float64,
+    OpenMP over blocks of channels; oracle/c/unroll.c) on the whole workload,
+    all host threads, from the same stored projected inputs the GPU reads.
+    Cross-checked against the NumPy oracle's unroll on a sample (row 0, 8
+    channels, the first 4096 steps)."""
+    from oracle import newton as onewton
+    from oracle import unroll_c
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    a64 = inp["a"].astype(np.float64)
+    unroll_c.unroll(w.cell, xproj_host[:1, :64], a64, cu_seqlens=None)   # load the library, start the threads
+    t0 = time.perf_counter()
+    h = unroll_c.unroll(w.cell, xproj_host, a64, cu_seqlens=cu)
+    el = time.perf_counter() - t0
+    Ts = min(w.T, 4096)
+    cu_s = None if cu is None else np.concatenate([cu[cu < Ts], [Ts]]).astype(np.int64)
+    ref, _ = onewton.sequential(w.cell, xproj_host[:1, :Ts, :, :8].astype(np.float64), a64[:, :8], cu_seqlens=cu_s)
+    err = float(np.abs(h[:1, :Ts, :8] - ref[..., -1, :]).max())
+    return {"value": w.tokens / el, "unit": "tokens/s", "cores": threads, "kind": "plain C unroll",
+            "sample": f"the whole workload ({w.tokens} tokens x {w.d_h} channels), sequential unroll in C, "
+                      f"float64, OpenMP over channel blocks, {threads} threads, {el:.2f} s",
+            "max_abs_vs_numpy_oracle_sample": err}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +252,7 @@ def main() -> int:
                     help="skip timing the fused forward (projection inside the Newton kernel)")
     ap.add_argument("--no-headmix", action="store_true", help="skip timing the head-mix GRU")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-kstar", action="store_true", help="skip the leg at the measured K*(T)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size reference for byte counters)")
     args = ap.parse_args()
@@ -436,6 +476,59 @@ def main() -> int:
         headmix = {"batch": bench_headmix(torch, B, dev, n, 2), "long": bench_headmix(torch, B, dev, n, 2, 1, 32768)}
         print("[bench] head-mix timed", file=sys.stderr, flush=True)
 
+    # agreement with the unroll at the bench's own K (FAQs, "Does parallel Newton match sequential
+    # unroll?"; Numerics contract, "Invariant": within tau at the measured K*(T)): the GPU unroll
+    # (prn_sequential_forward) on the same projected inputs, every h compared on the host
+    B.prn_newton_forward(xproj, a, w.K, H, cell=w.cell, cu_seqlens=cu, residual_out=res, workspace=ws,
+                         stream=stream)
+    H_seq = torch.empty_like(H)
+    B.prn_sequential_forward(xproj, a, H_seq, cell=w.cell, cu_seqlens=cu, stream=stream)
+    torch.cuda.synchronize()
+    H_seq_host = H_seq.float().cpu().numpy()
+    agreement = {"K": w.K, "max_abs_vs_unroll": float(np.abs(H.float().cpu().numpy() - H_seq_host).max()),
+                 "tau_f32": 1e-4, "compared": "every h of the workload, Newton at this K vs the GPU unroll"}
+    print(f"[bench] agreement at K={w.K}: {agreement['max_abs_vs_unroll']:.3e}", file=sys.stderr, flush=True)
+
+    kstar = None
+    if not args.no_kstar:
+        # the same forward at the measured K*(T) of this cell (nonlinear_rnn_amd/kstar_table.json):
+        # the depth at which it meets tau against the unroll
+        from nonlinear_rnn_amd.kstar import load_table
+        k_s = prn.resolve_k(w.T if not w.n_seqs else int(np.diff(inp["cu_seqlens"]).max()), load_table(w.cell))
+        ws_k = torch.empty(max(B.prn_workspace_bytes(w.cell, dt, w.B, w.T, w.d_h, k_s, n_seqs=n_seqs), 1),
+                           dtype=torch.uint8, device=dev)
+        res_k = torch.zeros(k_s + 1, dtype=torch.float32, device=dev)
+        Hk = torch.empty_like(H)
+
+        def kstep():
+            B.prn_newton_forward(xproj, a, k_s, Hk, cell=w.cell, cu_seqlens=cu, residual_out=res_k, workspace=ws_k,
+                                 stream=stream)
+        for _ in range(args.warmup):
+            kstep()
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            kev[i][0].record(stream)
+            kstep()
+            kev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_k = np.array([e[0].elapsed_time(e[1]) for e in kev])
+        k_ms = float(t_k.mean())
+        wk = w.scaled(K=k_s)
+        kb = algorithmic_newton_bytes(wk)
+        kstar = {"K": k_s, "kernel": "k_newton_sp (prn_newton_forward)", "newton_ms_mean": k_ms,
+                 "newton_ms_min": float(t_k.min()), "newton_tokens_per_s": w.tokens / (k_ms * 1e-3),
+                 "step_tokens_per_s": w.tokens / ((k_ms + float(t_proj.mean())) * 1e-3),
+                 "residuals": res_k.cpu().tolist(),
+                 "max_abs_vs_unroll": float(np.abs(Hk.float().cpu().numpy() - H_seq_host).max()),
+                 "roofline": {"bound": "hbm", "achieved": kb / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "algorithmic_bytes": kb}}
+        del Hk, ws_k
+        print(f"[bench] K*={k_s} leg timed: {k_ms:.3f} ms, max|H - unroll| {kstar['max_abs_vs_unroll']:.3e}",
+              file=sys.stderr, flush=True)
+    del H_seq
+
     residuals = res.cpu().tolist()
     ms_step = wall * 1e3 / args.steps
     value = w.tokens / (wall / args.steps)
@@ -443,11 +536,21 @@ def main() -> int:
     newton_ms = float(t_newt.mean())
     proj_ms = float(t_proj.mean())
     alg_bytes = algorithmic_newton_bytes(w)
+    prof = profile_fields("k_newton_sp", w.name)
     roof_newton = {"kernel": "k_newton_sp (prn_newton_forward)", "bound": "hbm",
                    "achieved": alg_bytes / (newton_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                   "traffic": profiled_traffic("k_newton_sp", w.name),
+                   "traffic": _field(prof, "traffic_bytes_per_launch"),
                    "algorithmic_bytes": alg_bytes}
     roof_newton["frac"] = roof_newton["achieved"] / roof_newton["peak"]
+    if roof_newton["traffic"]:
+        # what the kernel really moves: the single-pass schedule reads the projected inputs once and
+        # writes no iterate, so its counted bytes are well below the K-pass method's algorithmic count
+        roof_newton["achieved_counted"] = roof_newton["traffic"] / (newton_ms * 1e-3) / 1e9
+        roof_newton["frac_counted"] = roof_newton["achieved_counted"] / HBM_PEAK_GBPS
+    if _field(prof, "valu_busy") is not None:
+        roof_newton["valu_busy"] = _field(prof, "valu_busy")
+        roof_newton["valu_lane_slots_per_channel_step"] = next(
+            (_field(prof, k) for k in prof if k.startswith("valu_lane_slots_per_channel_step")), None)
     fl = proj_flops(w)
     roof_proj = {"kernel": f"k_proj, {proj_tiles(w)} tiles (prn_input_proj)", "bound": "mfma",
                  "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
@@ -482,6 +585,8 @@ def main() -> int:
                                       "newton_hbm_frac": alg_bytes / (float(t_newt_fl.mean()) * 1e-3) / 1e9
                                       / HBM_PEAK_GBPS},
         "residuals": residuals,
+        "agreement": agreement,
+        "k_star": kstar,
         "backward": backward,
         "fused": fused,
         "decode": decode,
@@ -492,6 +597,9 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        print("[bench] cpu baseline (OpenMP unroll) ...", file=sys.stderr, flush=True)
+        xp_host = xproj.float().cpu().numpy()
+        out["cpu_baseline"]["openmp"] = cpu_openmp_unroll(w, xp_host, inp, inp["cu_seqlens"])
     print(json.dumps(out), flush=True)
     return 0
 

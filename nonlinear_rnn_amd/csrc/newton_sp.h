@@ -471,10 +471,10 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           xs_get(j, xj);
           C::f(xj, pr, cf.as, cf.a, fv);
           if (ch_ok) {
-            hq[j * dq] = ST::pack(s[S - 1]);
+            gstore(hq + j * dq, ST::pack(s[S - 1]));
             if constexpr (WS) {
 #pragma unroll
-              for (int q = 0; q < S; ++q) sq[(j * S + q) * dq] = ST::pack(s[q]);
+              for (int q = 0; q < S; ++q) gstore(sq + (j * S + q) * dq, ST::pack(s[q]));
             }
           }
 #pragma unroll
@@ -486,7 +486,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         }
         if (slast && ch_ok && (t0 + LS == T || sg.next == t0 + LS)) {
 #pragma unroll
-          for (int q = 0; q < S; ++q) lq[(sg.seg * S + q) * dq + ch] = ST::pack(s[q]);
+          for (int q = 0; q < S; ++q) gstore(lq + (sg.seg * S + q) * dq + ch, ST::pack(s[q]));
         }
       }
     } else if (wact) {
@@ -513,14 +513,14 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           } else {
             C::f(xj, p, cf.as, cf.a, fv);
             if (ch_ok) {
-              hq[j * dq] = ST::pack(s[S - 1]);
+              gstore(hq + j * dq, ST::pack(s[S - 1]));
               if constexpr (WS) {
 #pragma unroll
-                for (int q = 0; q < S; ++q) sq[(j * S + q) * dq] = ST::pack(s[q]);
+                for (int q = 0; q < S; ++q) gstore(sq + (j * S + q) * dq, ST::pack(s[q]));
               }
               if (slast && st.last(t, T)) {
 #pragma unroll
-                for (int q = 0; q < S; ++q) lq[(st.seg * S + q) * dq + ch] = ST::pack(s[q]);
+                for (int q = 0; q < S; ++q) gstore(lq + (st.seg * S + q) * dq + ch, ST::pack(s[q]));
               }
             }
           }

@@ -39,6 +39,16 @@ template <> struct Storage<kBF16> {
   static __device__ __forceinline__ float round(float v) { return static_cast<float>(static_cast<__bf16>(v)); }
 };
 
+// A store through the global address space.  A pointer that went through an
+// empty asm statement (to keep the compiler from hoisting addresses) is only
+// known as a generic pointer, and a plain store to it becomes a flat store,
+// which the LDS counter tracks as well: every later wait for an LDS read then
+// also waits for the store to complete.
+template <class T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+  *(__attribute__((address_space(1))) T*)p = v;
+}
+
 // ------------------------------------------------- transcendentals -------
 // v_exp_f32 computes 2^x and v_rcp_f32 1/x, each to about 1 ulp.  Gate
 // pre-activations are carried pre-multiplied by the factor that turns them
