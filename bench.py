@@ -377,6 +377,36 @@ def main() -> int:
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": bw_bytes / (bw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                  "traffic": profiled_traffic("k_bw_sp", w.name), "algorithmic_bytes": bw_bytes}}
+        # the projection's gradients at the same dL/dxproj: dx = g W, dW = g^T x, dbias (the rest of the
+        # training step's backward, prn_input_proj_backward)
+        dxi = torch.empty_like(x)
+        dWi = torch.empty_like(W)
+        dbi = torch.empty(w.G * w.d_h, dtype=torch.float32, device=dev)
+        pws = torch.empty(max(B.prn_input_proj_backward_workspace_bytes(w.cell, dt, w.B, w.T, w.d_in, w.d_h), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def pstep():
+            B.prn_input_proj_backward(dxp, x, W, cell=w.cell, dx_out=dxi, dW_out=dWi, dbias_out=dbi, workspace=pws,
+                                      stream=stream)
+        for _ in range(args.warmup):
+            pstep()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            pev[i][0].record(stream)
+            pstep()
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_pb = np.array([e[0].elapsed_time(e[1]) for e in pev])
+        pb_ms = float(t_pb.mean())
+        pfl = 2.0 * proj_flops(w)   # dx and dW: one projection's worth of products each
+        backward["input_proj_backward"] = {
+            "kernels": "transposes + k_proj (dx) + split-K k_proj (dW) + ordered sums (prn_input_proj_backward)",
+            "ms_mean": pb_ms, "ms_min": float(t_pb.min()), "workspace_bytes": int(pws.numel()),
+            "roofline": {"bound": "mfma", "achieved": pfl / (pb_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                         "unit": "TFLOP/s", "frac": pfl / (pb_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+                         "algorithmic_flops": pfl}}
+        del dxi, dWi, pws
         print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
     fused = None

@@ -116,6 +116,33 @@ enum { PRN_FAULT_LOOKBACK = 1 };
 prn_status prn_input_proj(const void* x, const void* W, const float* bias,
                           const prn_params* params, void* xproj_out);
 
+/* Gradients of the input projection (its train-mode backward: FAQs "train()
+ * vs eval()"; shapes/layout page, the train forward+backward surface and
+ * W_x), given dL/dxproj:
+ *   dx[b,t,j]  = sum_n dxproj[b,t,n] W[n,j]        (n = g*d_h + i)
+ *   dW[n,j]    = sum_{b,t} dxproj[b,t,n] x[b,t,j]
+ *   dbias[n]   = sum_{b,t} dxproj[b,t,n]
+ *   dxproj     (B, T, G, d_h) storage dtype (prn_newton_backward's dxproj_out)
+ *   x, W       the forward's operands: (B, T, d_in), (G*d_h, d_in) storage dtype
+ *   dx_out     (B, T, d_in) storage dtype, or NULL (not computed)
+ *   dW_out     (G*d_h, d_in) storage dtype, or NULL
+ *   dbias_out  (G*d_h) fp32, or NULL
+ * params: cell, dtype, B, T, d_in, d_h, workspace (at least
+ * prn_input_proj_backward_workspace_bytes(params); it covers all three
+ * outputs), stream; n_seqs must be 0 (a ragged pack is B = 1, T = N).
+ * dxproj must be 16-byte aligned (it is read by the matrix-core tiles);
+ * the other pointers need only their element alignment.
+ * Products on the matrix cores as in prn_input_proj (fp32, or bf16 with fp32
+ * accumulation); every sum is taken in a fixed order (the result is bitwise
+ * reproducible) and rounded once to the storage dtype; dbias sums in fp32.
+ * The weight gradient is split over token slices whose fp32 partial sums are
+ * added in slice order; both of its operands are first transposed into the
+ * workspace (the workspace holds dxproj and x once more). */
+prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void* W,
+                                   const prn_params* params, void* dx_out, void* dW_out,
+                                   float* dbias_out);
+size_t prn_input_proj_backward_workspace_bytes(const prn_params* params);
+
 /* Parallel Newton forward (the train-mode path of the FAQs' "train() vs
  * eval()"): K iterations from the guess H = 0, then the final trajectory.
  *   xproj      (B, T, G, d_h) storage dtype, biases included

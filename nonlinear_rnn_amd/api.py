@@ -256,7 +256,8 @@ def verify_agreement(xproj, a, K=3, *, cell: str, h0=None, cu_seqlens=None, atol
 # NewtonConfig(recompute=True) for long sequences) the forward keeps only
 # its inputs and the backward runs the forward again to rebuild the
 # trajectory: (B, T, S, d_h) less memory held between the passes, one more
-# forward in the backward.
+# forward in the backward.  The projection's gradients (input_proj_apply)
+# come from prn_input_proj_backward.
 
 def _forward_states(xproj, a, h0, cell, K, cu, picard_iters, with_states):
     """Newton forward keeping the trajectory; returns (H, states, residuals on
@@ -334,21 +335,27 @@ class _ProjFunction(torch.autograd.Function):
     def forward(ctx, x, W, bias, cell):
         ctx.save_for_backward(x, W)
         ctx.has_bias = bias is not None
+        ctx.cell = cell
         return input_proj(x, W, bias, cell=cell)
 
     @staticmethod
     def backward(ctx, dxp):
         x, W = ctx.saved_tensors
         Bn, T, G, d_h = dxp.shape
-        g = dxp.reshape(Bn * T, G * d_h).float()
-        dx = (g @ W.float()).reshape(x.shape).to(x.dtype)
-        dW = (g.t() @ x.reshape(Bn * T, -1).float()).to(W.dtype)
-        dbias = g.sum(0) if ctx.has_bias else None
+        dxp = dxp.to(x.dtype).contiguous()
+        want_x, want_W, want_b = ctx.needs_input_grad[:3]
+        dx = torch.empty_like(x) if want_x else None
+        dW = torch.empty_like(W) if want_W else None
+        dbias = torch.empty(G * d_h, dtype=torch.float32, device=x.device) if (want_b and ctx.has_bias) else None
+        n = B_.prn_input_proj_backward_workspace_bytes(ctx.cell, x.dtype, Bn, T, x.shape[-1], d_h)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+        B_.prn_input_proj_backward(dxp, x, W, cell=ctx.cell, dx_out=dx, dW_out=dW, dbias_out=dbias, workspace=ws)
         return dx, dW, dbias, None
 
 
 def input_proj_apply(x, W, bias=None, *, cell: str):
-    """Differentiable projection: xproj = x W^T + bias on the matrix cores,
-    gradients by plain matrix products."""
+    """Differentiable projection: xproj = x W^T + bias on the matrix cores;
+    its backward (dx, dW, dbias) is prn_input_proj_backward, also on the
+    matrix cores, with fixed summation orders."""
     return _ProjFunction.apply(x.contiguous(), W.contiguous(),
                                None if bias is None else bias.to(torch.float32).contiguous(), cell)

@@ -30,7 +30,8 @@ EXPORTS = ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "
            "prn_workspace_bytes",
            "prn_newton_backward", "prn_backward_workspace_bytes", "prn_decode_step", "prn_head_newton_forward",
            "prn_head_sequential_forward", "prn_head_workspace_bytes", "prn_validate_cu_seqlens",
-           "prn_last_error", "prn_version", "prn_newton_forward_noalloc")
+           "prn_last_error", "prn_version", "prn_newton_forward_noalloc", "prn_input_proj_backward",
+           "prn_input_proj_backward_workspace_bytes")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PRN_NOALLOC_SCRATCH_BYTES
 
 
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.prn_newton_forward.argtypes = [vp, P, vp, i32, vp, vp, vp]
         L.prn_newton_forward_fused.argtypes = [vp, vp, vp, P, vp, i32, vp, vp, vp, vp]
         L.prn_newton_forward_noalloc.argtypes = [vp, P, vp, i32, vp, vp, vp]
+        L.prn_input_proj_backward.argtypes = [vp, vp, vp, P, vp, vp, vp]
+        L.prn_input_proj_backward_workspace_bytes.argtypes = [P]
+        L.prn_input_proj_backward_workspace_bytes.restype = ctypes.c_size_t
         L.prn_sequential_forward.argtypes = [vp, P, vp, vp, vp]
         L.prn_workspace_bytes.argtypes = [P, i32]
         L.prn_workspace_bytes.restype = ctypes.c_size_t
@@ -100,7 +104,8 @@ def lib() -> ctypes.CDLL:
         L.prn_validate_cu_seqlens.argtypes = [vp, i64, i64]
         L.prn_last_error.restype = ctypes.c_char_p
         L.prn_version.restype = i32
-        for name in ("prn_input_proj", "prn_newton_forward", "prn_newton_forward_fused", "prn_newton_forward_noalloc",
+        for name in ("prn_input_proj", "prn_input_proj_backward", "prn_newton_forward", "prn_newton_forward_fused",
+                     "prn_newton_forward_noalloc",
                      "prn_sequential_forward",
                      "prn_newton_backward",
                      "prn_decode_step", "prn_head_newton_forward", "prn_head_sequential_forward",
@@ -198,6 +203,40 @@ def prn_input_proj(x, W, bias, xproj_out, *, cell: str, stream=None) -> None:
         raise ValueError("bias must have G*d_h entries")
     p = make_params(cell, x.dtype, B, T, d_h, d_in=d_in, stream=stream)
     _check(lib().prn_input_proj(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(p), _ptr(xproj_out)))
+
+
+def prn_input_proj_backward_workspace_bytes(cell: str, dtype: torch.dtype, B: int, T: int, d_in: int,
+                                            d_h: int) -> int:
+    p = make_params(cell, dtype, B, T, d_h, d_in=d_in)
+    n = int(lib().prn_input_proj_backward_workspace_bytes(ctypes.byref(p)))
+    if n == 0 and prn_last_error():
+        raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
+    return n
+
+
+def prn_input_proj_backward(dxproj, x, W, *, cell: str, dx_out=None, dW_out=None, dbias_out=None, workspace=None,
+                            stream=None) -> None:
+    """dx_out (B,T,d_in) = dxproj W, dW_out (G*d_h, d_in) = dxproj^T x, dbias_out (G*d_h) fp32 = column sums
+    of dxproj (B,T,G,d_h); each output optional."""
+    _dev(dxproj, "dxproj")
+    _dev(x, "x", dxproj.dtype)
+    _dev(W, "W", dxproj.dtype)
+    _dev(dx_out, "dx_out", dxproj.dtype)
+    _dev(dW_out, "dW_out", dxproj.dtype)
+    _dev(dbias_out, "dbias_out", torch.float32)
+    B, T, G, d_h = dxproj.shape
+    d_in = x.shape[-1]
+    if G != GATES[cell] or x.shape != (B, T, d_in) or W.shape != (G * d_h, d_in):
+        raise ValueError(f"shape mismatch: dxproj {tuple(dxproj.shape)} x {tuple(x.shape)} W {tuple(W.shape)}")
+    if dx_out is not None and dx_out.shape != x.shape:
+        raise ValueError("dx_out must have the shape of x")
+    if dW_out is not None and dW_out.shape != W.shape:
+        raise ValueError("dW_out must have the shape of W")
+    if dbias_out is not None and dbias_out.shape != (G * d_h,):
+        raise ValueError("dbias_out must have G*d_h entries")
+    p = make_params(cell, dxproj.dtype, B, T, d_h, d_in=d_in, workspace=workspace, stream=stream)
+    _check(lib().prn_input_proj_backward(_ptr(dxproj), _ptr(x), _ptr(W), ctypes.byref(p), _ptr(dx_out),
+                                         _ptr(dW_out), _ptr(dbias_out)))
 
 
 def _newton_common(xproj, a, H_out, h0, cu_seqlens, state_last_out, cell):

@@ -6,6 +6,7 @@
 // loop with no residual host sync).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -557,6 +558,73 @@ prn_status check_head(const prn_params* p, Shape* sh, int32_t d_head) {
   return PRN_OK;
 }
 
+// ---- the projection's backward ----
+// dW = dxproj^T x reduces over tokens, the row index of both operands; the
+// matrix-core tile multiplies operands whose reduction index runs along
+// their rows, so both are transposed into the workspace first (token-padded
+// with zeros to splits x ks), and the product runs split-K: slice z
+// multiplies tokens [z ks, (z+1) ks) into its own fp32 block, and the blocks
+// are summed in slice order.  dx = dxproj W only needs W transposed; dxproj
+// is read in place when its rows are whole 16-byte chunks, else from a
+// zero-padded copy.  dbias comes from the column sums the dxproj transpose
+// takes on the way (per 64 tokens, then in token order, in two fixed-order
+// levels).
+struct PlanPb {
+  int64_t M, N, Kd;      // tokens, G d_h, d_in
+  bool do_dx, do_dw, do_db;
+  bool pad_g;            // dxproj rows are not whole 16-byte chunks: use a padded copy for dx
+  int64_t Np;            // row length (elements) of W^T and of the padded dxproj
+  int splits;
+  int64_t ks, Mp, n_rt;  // tokens per slice, padded tokens, 64-token tiles of the dxproj transpose
+  int64_t n_slices, per;  // the tile column sums: n_rt rows reduced in n_slices slices of per rows
+  size_t wt_off, gp_off, gt_off, xt_off, part_off, csum_off, cslice_off, total;
+};
+constexpr int64_t kPbWgTarget = 1024;   // workgroups the split-K product aims for
+constexpr int64_t kPbTok = 256;         // slices are multiples of 256 tokens
+
+PlanPb plan_pb(const prn_params* p, const Shape& sh, bool dx, bool dw, bool db) {
+  PlanPb pl{};
+  pl.M = p->B * p->T;
+  pl.N = sh.G * p->d_h;
+  pl.Kd = p->d_in;
+  pl.do_dx = dx && pl.M > 0;
+  pl.do_dw = dw && pl.M > 0;
+  pl.do_db = db && pl.M > 0;
+  const int64_t vec = 16 / int64_t(sh.elt);
+  pl.pad_g = pl.N % vec != 0;
+  pl.Np = pl.pad_g ? (pl.N + vec - 1) / vec * vec : pl.N;
+  const int64_t tiles = ((pl.N + 127) / 128) * ((pl.Kd + 127) / 128);
+  int64_t splits = (kPbWgTarget + tiles - 1) / tiles;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, (pl.M + kPbTok - 1) / kPbTok));
+  pl.ks = ((pl.M + splits - 1) / splits + kPbTok - 1) / kPbTok * kPbTok;
+  pl.splits = int(splits);
+  pl.Mp = pl.ks * splits;
+  pl.n_rt = (pl.Mp + 63) / 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  if (pl.do_dx) {
+    pl.wt_off = take(size_t(pl.Kd) * pl.Np * sh.elt);
+    if (pl.pad_g) pl.gp_off = take(size_t(pl.M) * pl.Np * sh.elt);
+  }
+  if (pl.do_dw) {
+    pl.gt_off = take(size_t(pl.N) * pl.Mp * sh.elt);
+    pl.xt_off = take(size_t(pl.Kd) * pl.Mp * sh.elt);
+    pl.part_off = take(size_t(pl.splits) * pl.N * pl.Kd * 4);
+  }
+  if (pl.do_db) {
+    pl.per = (pl.n_rt + kDaSlices - 1) / kDaSlices;
+    pl.n_slices = (pl.n_rt + pl.per - 1) / pl.per;
+    pl.csum_off = take(size_t(pl.n_rt) * pl.N * 4);
+    pl.cslice_off = take(size_t(pl.n_slices) * pl.N * 4);
+  }
+  pl.total = off;
+  return pl;
+}
+
 // ---- scratch of the allocation-free forward ----
 // One file-scope device array per GPU, alive until the process ends.  Host
 // code never uses the array's name as an address (on the host it names a
@@ -825,6 +893,91 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias, const
     return fail(PRN_ERR_UNSUPPORTED, "input projection too large");
   prn::launch_proj(p->dtype == PRN_BF16, x, W, bias, xproj_out, M, N, Kd, static_cast<hipStream_t>(p->stream));
   return launched("prn_input_proj");
+}
+
+size_t prn_input_proj_backward_workspace_bytes(const prn_params* p) {
+  g_err.clear();  // a 0 result with no message means no workspace is needed
+  Shape sh;
+  if (check_common(p, &sh) != PRN_OK) return 0;
+  if (p->d_in < 1) {
+    fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
+    return 0;
+  }
+  return plan_pb(p, sh, true, true, true).total;
+}
+
+prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void* W, const prn_params* p,
+                                   void* dx_out, void* dW_out, float* dbias_out) {
+  Shape sh;
+  prn_status s = check_common(p, &sh);
+  if (s != PRN_OK) return s;
+  if (sh.ragged) return fail(PRN_ERR_INVALID_ARG, "the projection's backward takes (B, T) rows, n_seqs must be 0");
+  if (p->d_in < 1) return fail(PRN_ERR_INVALID_ARG, "d_in must be >= 1");
+  const int64_t M = p->B * p->T, N = sh.G * p->d_h, Kd = p->d_in;
+  if (M > 0 && !dxproj) return fail(PRN_ERR_INVALID_ARG, "dxproj is NULL");
+  if (dW_out && M > 0 && !x) return fail(PRN_ERR_INVALID_ARG, "x is NULL");
+  if (dx_out && M > 0 && !W) return fail(PRN_ERR_INVALID_ARG, "W is NULL");
+  if (misaligned(dxproj, 16) || misaligned(x, sh.elt) || misaligned(W, sh.elt) || misaligned(dx_out, sh.elt) ||
+      misaligned(dW_out, sh.elt) || misaligned(dbias_out, 4))
+    return fail(PRN_ERR_INVALID_ARG, "dxproj must be 16-byte aligned, the other tensors aligned to their element size");
+  const PlanPb pl = plan_pb(p, sh, dx_out != nullptr, dW_out != nullptr, dbias_out != nullptr);
+  if (pl.total > 0) {
+    if (!p->workspace || p->workspace_bytes < pl.total)
+      return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
+                  p->workspace, pl.total);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+      return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  }
+  // grids: transposes take (rows / 64) x (columns / 64) workgroups, the products one per 128 x 128 tile
+  if (pl.Mp / 64 > kMaxGrid1D || (pl.N + 63) / 64 > kMaxGrid || (Kd + 63) / 64 > kMaxGrid ||
+      ((M + 127) / 128) * ((Kd + 127) / 128) > kMaxGrid1D || pl.splits > kMaxGrid)
+    return fail(PRN_ERR_UNSUPPORTED, "projection backward too large");
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  const bool bf = p->dtype == PRN_BF16;
+  const size_t elt = sh.elt;
+  char* ws = static_cast<char*>(p->workspace);
+  if (M == 0) {
+    if (dW_out) {
+      if (bf)
+        prn::k_copy_or_zero<uint16_t><<<unsigned((N * Kd + 255) / 256), 256, 0, st>>>(
+            nullptr, static_cast<uint16_t*>(dW_out), N * Kd);
+      else
+        prn::k_zero_f32<<<unsigned((N * Kd + 255) / 256), 256, 0, st>>>(static_cast<float*>(dW_out), N * Kd);
+    }
+    if (dbias_out) prn::k_zero_f32<<<unsigned((N + 255) / 256), 256, 0, st>>>(dbias_out, N);
+    return launched("prn_input_proj_backward");
+  }
+  if (pl.do_dx) {
+    // dx (M x Kd) = dxproj (M x N) W (N x Kd): W^T rows of Np elements, zero past N
+    void* wt = ws + pl.wt_off;
+    prn::launch_transpose(bf, W, N, Kd, Kd, wt, pl.Np, nullptr, st);
+    const void* g = dxproj;
+    if (pl.pad_g) {
+      prn::launch_pad_rows(bf, dxproj, M, N, ws + pl.gp_off, pl.Np, st);
+      g = ws + pl.gp_off;
+    }
+    prn::launch_proj_ld(bf, g, pl.Np * elt, wt, pl.Np * elt, dx_out, M, Kd, pl.Np, st);
+  }
+  float* csum = pl.do_db ? reinterpret_cast<float*>(ws + pl.csum_off) : nullptr;
+  if (pl.do_dw) {
+    // dW (N x Kd) = dxproj^T x, split-K over tokens
+    void* gt = ws + pl.gt_off;
+    void* xt = ws + pl.xt_off;
+    float* part = reinterpret_cast<float*>(ws + pl.part_off);
+    prn::launch_transpose(bf, dxproj, M, N, N, gt, pl.Mp, csum, st);
+    prn::launch_transpose(bf, x, M, Kd, Kd, xt, pl.Mp, nullptr, st);
+    prn::launch_proj_splitk(bf, gt, pl.Mp * elt, xt, pl.Mp * elt, part, N, Kd, pl.ks, pl.splits, st);
+    prn::launch_splitk_sum(bf, part, pl.splits, N * Kd, dW_out, st);
+  } else if (pl.do_db) {
+    prn::launch_transpose(bf, dxproj, M, N, N, nullptr, pl.Mp, csum, st);
+  }
+  if (pl.do_db) {
+    float* cslice = reinterpret_cast<float*>(ws + pl.cslice_off);
+    prn::k_bw_da_partial<1><<<dim3(unsigned((N + 63) / 64), 1u, unsigned(pl.n_slices)), 256, 0, st>>>(
+        csum, pl.n_rt, pl.per, N, cslice);
+    prn::k_bw_da_reduce<1><<<dim3(unsigned((N + 63) / 64), 1u), 256, 0, st>>>(cslice, pl.n_slices, N, dbias_out);
+  }
+  return launched("prn_input_proj_backward");
 }
 
 size_t prn_head_workspace_bytes(const prn_params* p, int32_t d_head, int32_t K) {

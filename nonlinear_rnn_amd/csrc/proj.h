@@ -14,4 +14,26 @@ namespace prn {
 void launch_proj(bool bf16, const void* A, const void* B, const float* bias, void* C, int64_t M, int64_t N,
                  int64_t K, hipStream_t stream);
 
+// The same product without bias, with operand rows lda / ldb bytes apart
+// (16-byte multiples, at least K elements).
+void launch_proj_ld(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t M,
+                    int64_t N, int64_t K, hipStream_t stream);
+
+// Split-K: slice z (0 <= z < splits) multiplies elements [z K, (z+1) K) of
+// every operand row and writes its fp32 sums, unrounded, to P + z M N
+// (M x N row-major).  128 x 128 tiles.
+void launch_proj_splitk(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M,
+                        int64_t N, int64_t K, int splits, hipStream_t stream);
+
+// Helpers of the projection's backward (elements of the storage dtype):
+// out (C x Rp) = the transpose of in (R x C, rows ld_in apart), zero for
+// R <= r < Rp; csum (optional, ceil(Rp/64) x C fp32): column sums of every
+// 64 input rows, in row order; out may be null.
+void launch_transpose(bool bf16, const void* in, int64_t R, int64_t C, int64_t ld_in, void* out, int64_t Rp,
+                      float* csum, hipStream_t stream);
+// out (R x Cp) = in (R x C) with zero columns appended
+void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out, int64_t Cp, hipStream_t stream);
+// out[i] = sum_z P[z n + i] in z order, rounded once to the storage dtype
+void launch_splitk_sum(bool bf16, const float* P, int S, int64_t n, void* out, hipStream_t stream);
+
 }  // namespace prn

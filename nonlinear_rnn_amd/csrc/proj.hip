@@ -87,14 +87,25 @@ struct Tile {
   static_assert(STAGE % (1024 * NW) == 0, "a stage must split evenly over the waves");
 };
 
-template <bool BF16, bool EDGE, int WR, int WC>
+// OUTF32: store the fp32 sums as they are (no bias, no rounding), for the
+// split-K partial products of the weight gradient.  Operand rows are lda /
+// ldb bytes apart (16-byte multiples); slice z = blockIdx.y of a split-K
+// launch starts K elements into every operand row and writes its own M x N
+// block of C.
+template <bool BF16, bool EDGE, int WR, int WC, bool OUTF32>
 __global__ void __launch_bounds__(64 * WR * WC)
 k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float* __restrict__ bias,
-       uint8_t* __restrict__ C, int64_t M, int64_t N, int64_t K, int n_tiles_n, int remap) {
+       uint8_t* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int n_tiles_n, int remap) {
   using Tl = Tile<WR, WC>;
   constexpr int BM = Tl::BM, BN = Tl::BN, IPW = Tl::IPW, STAGE = Tl::STAGE;
   constexpr int ELT = BF16 ? 2 : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  {
+    const int64_t z = blockIdx.y;
+    A += z * K * ELT;
+    B += z * K * ELT;
+    C += z * M * N * (OUTF32 ? 4 : ELT);
+  }
   // block -> tile, keeping the column tiles of a row tile on one XCD
   int64_t bid = blockIdx.x;
   if (remap) {
@@ -119,7 +130,7 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
     kvb[p] = lds_pos(r, q) * 16;
     int64_t g = r < BM ? m0 + r : n0 + r - BM;
     if (EDGE) g = r < BM ? (g < M ? g : M - 1) : (g < N ? g : N - 1);
-    src[p] = (r < BM ? A : B) + g * rowbytes + kvb[p];
+    src[p] = (r < BM ? A + g * lda : B + g * ldb) + kvb[p];
   }
   auto issue = [&](int64_t kt, int buf) {
     uint8_t* base = lds + buf * STAGE + wave * IPW * 1024;
@@ -205,7 +216,9 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
         const int64_t gm = m0 + wr * WM * 32 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         const float v = acc[i][j][r] + bcol[j];
         if (full || (gm < M && gn < N)) {
-          if constexpr (BF16)
+          if constexpr (OUTF32)
+            reinterpret_cast<float*>(C)[gm * N + gn] = v;
+          else if constexpr (BF16)
             __builtin_nontemporal_store(bf16_rne(v), reinterpret_cast<uint16_t*>(C) + gm * N + gn);
           else
             __builtin_nontemporal_store(v, reinterpret_cast<float*>(C) + gm * N + gn);
@@ -215,18 +228,18 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
   }
 }
 
-template <int WR, int WC>
+template <int WR, int WC, bool OUTF32>
 void launch_tiles(bool bf16, const void* A, const void* B, const float* bias, void* C, int64_t M, int64_t N,
-                  int64_t K, hipStream_t stream) {
+                  int64_t K, int64_t lda, int64_t ldb, int splits, hipStream_t stream) {
   using Tl = Tile<WR, WC>;
   const int64_t tn = (N + Tl::BN - 1) / Tl::BN, nb = ((M + Tl::BM - 1) / Tl::BM) * tn;
   const int remap = (nb % NXCD == 0) ? 1 : 0;
   const bool edge = M % Tl::BM != 0 || N % Tl::BN != 0 || (K * (bf16 ? 2 : 4)) % ROWB != 0;
-  const dim3 grid(static_cast<unsigned>(nb));
+  const dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>(splits));
   auto go = [&](auto bf, auto ed) {
-    k_proj<decltype(bf)::value, decltype(ed)::value, WR, WC><<<grid, Tl::NTHR, 0, stream>>>(
+    k_proj<decltype(bf)::value, decltype(ed)::value, WR, WC, OUTF32><<<grid, Tl::NTHR, 0, stream>>>(
         static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), bias, static_cast<uint8_t*>(C), M, N, K,
-        int(tn), remap);
+        lda, ldb, int(tn), remap);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -243,10 +256,126 @@ void launch_proj(bool bf16, const void* A, const void* B, const float* bias, voi
                  int64_t K, hipStream_t stream) {
   using Large = Tile<4, 4>;
   const int64_t large = ((M + Large::BM - 1) / Large::BM) * ((N + Large::BN - 1) / Large::BN);
+  const int64_t ld = K * (bf16 ? 2 : 4);
   if (large >= kLargeTiles)
-    launch_tiles<4, 4>(bf16, A, B, bias, C, M, N, K, stream);
+    launch_tiles<4, 4, false>(bf16, A, B, bias, C, M, N, K, ld, ld, 1, stream);
   else
-    launch_tiles<2, 2>(bf16, A, B, bias, C, M, N, K, stream);
+    launch_tiles<2, 2, false>(bf16, A, B, bias, C, M, N, K, ld, ld, 1, stream);
+}
+
+void launch_proj_ld(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t M,
+                    int64_t N, int64_t K, hipStream_t stream) {
+  using Large = Tile<4, 4>;
+  const int64_t large = ((M + Large::BM - 1) / Large::BM) * ((N + Large::BN - 1) / Large::BN);
+  if (large >= kLargeTiles)
+    launch_tiles<4, 4, false>(bf16, A, B, nullptr, C, M, N, K, lda, ldb, 1, stream);
+  else
+    launch_tiles<2, 2, false>(bf16, A, B, nullptr, C, M, N, K, lda, ldb, 1, stream);
+}
+
+void launch_proj_splitk(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M,
+                        int64_t N, int64_t K, int splits, hipStream_t stream) {
+  launch_tiles<2, 2, true>(bf16, A, B, nullptr, P, M, N, K, lda, ldb, splits, stream);
+}
+
+// ---------------------------------------------- backward helpers ---------
+
+namespace {
+
+template <bool BF16> struct Elt;
+template <> struct Elt<false> {
+  using T = float;
+  static __device__ __forceinline__ float ld(T v) { return v; }
+  static __device__ __forceinline__ T st(float v) { return v; }
+};
+template <> struct Elt<true> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float ld(T v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  static __device__ __forceinline__ T st(float v) { return bf16_rne(v); }
+};
+
+// out[c, r] = in[r, c] (in: R x C, rows ld_in elements apart; out: C x Rp,
+// zero for R <= r < Rp), through a 64 x 64 LDS tile: reads coalesced along
+// the input rows, writes along the output rows.  bf16 values pass through
+// fp32 exactly.  csum (optional): the column sums of the tile's 64 input
+// rows, taken in row order, at csum[blockIdx.x * C + c].  out may be null
+// (column sums only).
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_transpose(const typename Elt<BF16>::T* __restrict__ in, int64_t R, int64_t C,
+                                                   int64_t ld_in, typename Elt<BF16>::T* __restrict__ out, int64_t Rp,
+                                                   float* __restrict__ csum) {
+  using E = Elt<BF16>;
+  __shared__ float tile[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64, c0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+    tile[ty + 4 * i][tx] = (r < R && c < C) ? E::ld(in[r * ld_in + c]) : 0.0f;
+  }
+  __syncthreads();
+  if (csum && ty == 0 && c0 + tx < C) {
+    float sum = 0.0f;
+    for (int i = 0; i < 64; ++i) sum += tile[i][tx];
+    csum[static_cast<int64_t>(blockIdx.x) * C + c0 + tx] = sum;
+  }
+  if (!out) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t c = c0 + ty + 4 * i, r = r0 + tx;
+    if (c < C && r < Rp) out[c * Rp + r] = E::st(tile[tx][ty + 4 * i]);
+  }
+}
+
+// out[r, c] = in[r, c] for c < C, 0 for C <= c < Cp (rows of Cp elements)
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_pad_rows(const typename Elt<BF16>::T* __restrict__ in, int64_t R, int64_t C,
+                                                  typename Elt<BF16>::T* __restrict__ out, int64_t Cp) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= R * Cp) return;
+  const int64_t r = i / Cp, c = i - r * Cp;
+  out[i] = c < C ? in[r * C + c] : Elt<BF16>::st(0.0f);
+}
+
+// out[i] = the sum over z = 0 .. S-1, in that order, of P[z * n + i],
+// rounded once to the storage dtype
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_splitk_sum(const float* __restrict__ P, int S, int64_t n,
+                                                    typename Elt<BF16>::T* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float sum = 0.0f;
+  for (int z = 0; z < S; ++z) sum += P[z * n + i];
+  out[i] = Elt<BF16>::st(sum);
+}
+
+}  // namespace
+
+void launch_transpose(bool bf16, const void* in, int64_t R, int64_t C, int64_t ld_in, void* out, int64_t Rp,
+                      float* csum, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((Rp + 63) / 64), static_cast<unsigned>((C + 63) / 64));
+  if (bf16)
+    k_transpose<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(in), R, C, ld_in,
+                                                static_cast<uint16_t*>(out), Rp, csum);
+  else
+    k_transpose<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(in), R, C, ld_in,
+                                                 static_cast<float*>(out), Rp, csum);
+}
+
+void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out, int64_t Cp, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((R * Cp + 255) / 256));
+  if (bf16)
+    k_pad_rows<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(in), R, C, static_cast<uint16_t*>(out), Cp);
+  else
+    k_pad_rows<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(in), R, C, static_cast<float*>(out), Cp);
+}
+
+void launch_splitk_sum(bool bf16, const float* P, int S, int64_t n, void* out, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (bf16)
+    k_splitk_sum<true><<<grid, 256, 0, stream>>>(P, S, n, static_cast<uint16_t*>(out));
+  else
+    k_splitk_sum<false><<<grid, 256, 0, stream>>>(P, S, n, static_cast<float*>(out));
 }
 
 }  // namespace prn

@@ -18,3 +18,16 @@ def input_proj(x64: np.ndarray, W64: np.ndarray, bias64, G: int) -> np.ndarray:
     if bias64 is not None:
         y = y + bias64
     return y.reshape(B, T, G, -1)
+
+
+def input_proj_backward(g64: np.ndarray, x64: np.ndarray, W64: np.ndarray):
+    """Gradients of a loss L through xproj = x W^T + bias, given
+    g64 = dL/dxproj (B,T,G,d_h): the chain rule through a linear map,
+    written as library matmuls:
+        dx    = g W        (B,T,d_in)
+        dW    = g^T x      (G*d_h, d_in), summed over every token
+        dbias = sum of g   (G*d_h,)"""
+    B, T = g64.shape[:2]
+    g = g64.reshape(B * T, -1)
+    x = x64.reshape(B * T, -1)
+    return (g @ W64).reshape(B, T, -1), g.T @ x, g.sum(axis=0)

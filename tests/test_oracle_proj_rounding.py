@@ -46,3 +46,30 @@ def test_generator_bf16_bits_roundtrip():
     bits = f32_to_bf16_bits(v)
     np.testing.assert_array_equal(bf16_bits_to_f32(bits).astype(np.float64), rounding.bf16_round(v))
     np.testing.assert_array_equal(rounding.bf16_from_bits(bits), rounding.bf16_round(v))
+
+
+def test_projection_backward_against_finite_differences():
+    """dx, dW and dbias of the oracle's projection backward are the central
+    finite differences of L = sum(w * input_proj(x, W, bias)) (exact up to
+    rounding: L is linear in each operand), element by element."""
+    rng = np.random.default_rng(11)
+    B, T, d_in, d_h, G = 2, 3, 5, 4, 3
+    x = rng.standard_normal((B, T, d_in))
+    W = rng.standard_normal((G * d_h, d_in))
+    bias = rng.standard_normal(G * d_h)
+    w = rng.standard_normal((B, T, G, d_h))   # dL/dxproj
+
+    def L(x_, W_, b_):
+        return float((w * proj.input_proj(x_, W_, b_, G)).sum())
+
+    dx, dW, db = proj.input_proj_backward(w, x, W)
+    eps = 1e-6
+    for arr, grad, args in ((x, dx, lambda a: (a, W, bias)), (W, dW, lambda a: (x, a, bias)),
+                            (bias, db, lambda a: (x, W, a))):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            fd[idx] = (L(*args(ap)) - L(*args(am))) / (2 * eps)
+        assert np.abs(fd - grad).max() <= 1e-7
