@@ -68,6 +68,22 @@ struct RevSegTracker {
     start = cu[seg];
     end = cu[seg + 1];
   }
+  // init by a whole wave (every lane active, t wave-uniform): the forward's
+  // wave-wide segment search
+  __device__ __forceinline__ void init_wave(const int32_t* cu_, int64_t n_seqs, int64_t row, int64_t t, int64_t T) {
+    cu = cu_;
+    if (!cu) {
+      seg = row;
+      start = 0;
+      end = T;
+      return;
+    }
+    SegTracker f;
+    f.init_wave(cu_, n_seqs, 0, t);
+    seg = f.seg;
+    start = f.start;
+    end = cu[seg + 1];
+  }
   __device__ __forceinline__ void at(int64_t t) {
     if (cu) {
       while (seg > 0 && start > t) {
@@ -319,7 +335,7 @@ k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storag
   Map acc = Map::identity();
   RevSegTracker rs;
   if (wact) {
-    rs.init(cu, n_seqs, b, t0 + n - 1, T);
+    rs.init_wave(cu, n_seqs, b, t0 + n - 1, T);
 #pragma unroll
     for (int j = LS - 1; j >= 0; --j) {
       if (j < n) {
@@ -370,7 +386,7 @@ k_bw_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename Storag
 #pragma unroll
     for (int q = 0; q < S; ++q) mu[q] = carry_sh[q][lane];
     for (int v = NW - 1; v > w; --v) apply(part[v][lane], mu);
-    rs.init(cu, n_seqs, b, t0 + n - 1, T);
+    rs.init_wave(cu, n_seqs, b, t0 + n - 1, T);
 #pragma unroll
     for (int j = LS - 1; j >= 0; --j) {
       if (j < n) {

@@ -247,7 +247,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   const bool wact = ticket < n_wg && t0 < T;
   const int n = wact ? static_cast<int>(imin(LS, T - t0)) : 0;
   SegTracker sg;
-  sg.init(cu, n_seqs, b, t0);
+  sg.init_wave(cu, n_seqs, b, t0);
   // a full sub-chunk without a segment head needs no per-step guards
   const bool fast = n == LS && t0 != 0 && sg.start != t0 && sg.next >= t0 + LS;
   if constexpr (FX) fused_tile<C, DT, LS, NW>(reinterpret_cast<uint8_t*>(xraw), fx, b, T, chunk * LC, tile, d_h, xsh);

@@ -346,6 +346,41 @@ struct SegTracker {
     start = cu[seg];
     next = (seg + 1 < n_seqs) ? static_cast<int64_t>(cu[seg + 1]) : INT64_MAX;
   }
+  // The same as init, searched by a whole wave at once (every lane active,
+  // t0 wave-uniform): each load probes 64 offsets, a ballot narrows the
+  // range, so a pack of up to 64 segments costs two dependent loads instead
+  // of a binary search's six or more.  Stays in bounds for any cu contents.
+  __device__ __forceinline__ void init_wave(const int32_t* cu_, int64_t n_seqs_, int64_t row, int64_t t0) {
+    cu = cu_;
+    n_seqs = n_seqs_;
+    if (!cu) {
+      seg = row;
+      start = 0;
+      next = INT64_MAX;
+      return;
+    }
+    const int lane = threadIdx.x & 63;
+    int64_t lo = 0, hi = n_seqs;   // the answer lies in [lo, hi); cu[lo] <= t0 once lo has been probed
+    while (hi - lo > 63) {
+      const int64_t step = (hi - lo + 63) / 64;
+      const int64_t j = lo + lane * step;
+      const bool ok = j < hi && static_cast<int64_t>(cu[j < hi ? j : lo]) <= t0;
+      const unsigned long long m = __ballot(ok);
+      const int k = m ? 63 - __builtin_clzll(m) : 0;
+      lo += k * step;
+      hi = imin(hi, lo + step);
+    }
+    // the last range has at most 63 candidates: lane i probes lo + i, and the
+    // next lane holds the following offset (lo + i + 1 <= n_seqs)
+    const int64_t j = lo + lane;
+    const int64_t v = j <= n_seqs ? static_cast<int64_t>(cu[j <= n_seqs ? j : n_seqs]) : 0;
+    const unsigned long long m = __ballot(j < hi && v <= t0);
+    const int k = m ? 63 - __builtin_clzll(m) : 0;
+    seg = lo + k;
+    start = __shfl(v, k, 64);
+    const int64_t nx = __shfl(v, k + 1, 64);
+    next = (seg + 1 < n_seqs) ? nx : INT64_MAX;
+  }
   // advance to step t (t non-decreasing); returns true if t is a head
   __device__ __forceinline__ bool at(int64_t t) {
     if (cu) {

@@ -58,7 +58,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int WM = 2, WN = 2;                  // 32 x 32 blocks per wave (rows, columns)
 constexpr int ROWB = 128;                      // bytes of every row per K stage
 constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
 constexpr int RPG = 16 / CPR;                  // rows per 256 bytes (64 banks)
@@ -76,8 +75,10 @@ __device__ __forceinline__ int lds_pos(int r, int kv) { return kv ^ ((r / RPG) &
 // round to nearest even (v_cvt_pk_bf16_f32); NaN stays a quiet NaN
 __device__ __forceinline__ uint16_t bf16_rne(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 
-template <int WR, int WC>
+// WR x WC waves, each owning WM x WN blocks of 32 x 32
+template <int WR, int WC, int WM_ = 2, int WN_ = 2>
 struct Tile {
+  static constexpr int WM = WM_, WN = WN_;
   static constexpr int NW = WR * WC;
   static constexpr int BM = WR * WM * 32, BN = WC * WN * 32;
   static constexpr int NTHR = 64 * NW;
@@ -92,11 +93,11 @@ struct Tile {
 // ldb bytes apart (16-byte multiples); slice z = blockIdx.y of a split-K
 // launch starts K elements into every operand row and writes its own M x N
 // block of C.
-template <bool BF16, bool EDGE, int WR, int WC, bool OUTF32>
+template <bool BF16, bool EDGE, int WR, int WC, bool OUTF32, int WM, int WN>
 __global__ void __launch_bounds__(64 * WR * WC)
 k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float* __restrict__ bias,
        uint8_t* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int n_tiles_n, int remap) {
-  using Tl = Tile<WR, WC>;
+  using Tl = Tile<WR, WC, WM, WN>;
   constexpr int BM = Tl::BM, BN = Tl::BN, IPW = Tl::IPW, STAGE = Tl::STAGE;
   constexpr int ELT = BF16 ? 2 : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
@@ -228,16 +229,16 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
   }
 }
 
-template <int WR, int WC, bool OUTF32>
+template <int WR, int WC, bool OUTF32, int WM = 2, int WN = 2>
 void launch_tiles(bool bf16, const void* A, const void* B, const float* bias, void* C, int64_t M, int64_t N,
                   int64_t K, int64_t lda, int64_t ldb, int splits, hipStream_t stream) {
-  using Tl = Tile<WR, WC>;
+  using Tl = Tile<WR, WC, WM, WN>;
   const int64_t tn = (N + Tl::BN - 1) / Tl::BN, nb = ((M + Tl::BM - 1) / Tl::BM) * tn;
   const int remap = (nb % NXCD == 0) ? 1 : 0;
   const bool edge = M % Tl::BM != 0 || N % Tl::BN != 0 || (K * (bf16 ? 2 : 4)) % ROWB != 0;
   const dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>(splits));
   auto go = [&](auto bf, auto ed) {
-    k_proj<decltype(bf)::value, decltype(ed)::value, WR, WC, OUTF32><<<grid, Tl::NTHR, 0, stream>>>(
+    k_proj<decltype(bf)::value, decltype(ed)::value, WR, WC, OUTF32, WM, WN><<<grid, Tl::NTHR, 0, stream>>>(
         static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), bias, static_cast<uint8_t*>(C), M, N, K,
         lda, ldb, int(tn), remap);
   };
