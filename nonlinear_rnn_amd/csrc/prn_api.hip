@@ -52,31 +52,43 @@ constexpr int kScanSeg = 16;
 // 0.97, 0.86, 0.78 ms; once the output addresses stopped being hoisted out
 // of the iteration loop (236 -> 213 registers at LS = 12), LS = 14 and 16
 // fit too: 0.756 and 0.713 ms (LS = 16 under a two-waves-per-SIMD register
-// cap, no spills).  A Picard sweep takes the same LS = 16 (0.78 ms at K = 2,
-// against 0.92 ms at LS = 10).  The GRU takes LS = 16 below 64 chains
-// (4 chains: 0.25 -> 0.18 ms against LS = 8) and LS = 12 above (128 chains:
-// 0.96 -> 0.91 ms; LS = 16 took 1.05 ms there).
+// cap, no spills).  Shorter chunks under a three-waves-per-SIMD cap do not
+// pay for their extra look-backs: LS = 8 (168 registers, 45 KB of LDS, three
+// workgroups per CU) took 0.84 ms and LS = 10 (spills) 0.95 ms, against
+// 0.69 ms for LS = 16 at two.  A Picard sweep takes the same LS = 16 (0.78 ms
+// at K = 2, against 0.92 ms at LS = 10).  The GRU takes LS = 16 below 64
+// chains (4 chains: 0.25 -> 0.18 ms against LS = 8) and LS = 12 above (128
+// chains: 0.96 -> 0.91 ms; LS = 16 took 1.05 ms there).  With few chains the
+// four-wave 64-step chunk also beat the other shapes tried on the 4-chain
+// ragged pack (LS x NW = 16 x 4: 0.24 ms; 12 x 4: 0.27; 16 x 3: 0.27;
+// 8 x 4: 0.32; 24 x 2: 0.31; 16 x 2: 0.34).
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
 // keeps LS = 8 (LS = 12 already needs 256 registers, LS = 16 spills); the
 // bf16 GRU with many chains takes LS = 10, the longest chunk that keeps four
 // waves per SIMD (122 registers, 35 KB of LDS) -- measured at 16 x 16384 x
 // 512: LS = 8 / 10 took 1.06 / 0.97 ms.
 constexpr int kSpNW = 4;
-constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruFew = 16, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
+constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
+constexpr int kSpLsGruFew = 16, kSpNwGruFew = 4;   // GRU below kSpManyChains chains
+constexpr int kSpLsFusedGru = 16, kSpLsFusedLstm = 16;
 constexpr int64_t kSpManyChains = 64;
-int sp_ls(int cell, int dtype, int64_t n_chains) {
-  if (cell != PRN_CELL_DIAG_GRU) return dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm;
-  if (n_chains < kSpManyChains) return kSpLsGruFew;
-  return dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany;
+struct SpGeo {
+  int ls, nw;   // steps per wave, waves per workgroup
+};
+SpGeo sp_geo(int cell, int dtype, int64_t n_chains) {
+  if (cell != PRN_CELL_DIAG_GRU) return {dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm, kSpNW};
+  if (n_chains < kSpManyChains) return {kSpLsGruFew, kSpNwGruFew};
+  return {dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany, kSpNW};
 }
 // With the projection fused into the Newton kernel, a chunk must be a
 // multiple of 32 steps (the projection's 32-row blocks), and longer chunks
 // stream W from L2 fewer times per token: every fused GRU takes 64-step
 // chunks (16 per lane), also with many chains where the unfused kernel takes
 // 48 or 40 (bf16 GRU at 128 chains: 32-step chunks 2.54 ms, 64-step 1.76 ms).
-int sp_ls_fused(int cell, int dtype, int64_t n_chains) {
-  if (cell == PRN_CELL_DIAG_GRU) return kSpLsGruFew;
-  return sp_ls(cell, dtype, n_chains);
+SpGeo sp_geo_fused(int cell, int dtype, int64_t n_chains) {
+  if (cell == PRN_CELL_DIAG_GRU) return {kSpLsFusedGru, kSpNW};
+  if (dtype == PRN_F32) return {kSpLsFusedLstm, kSpNW};
+  return sp_geo(cell, dtype, n_chains);
 }
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
 // PRN_SPIN_LIMIT overrides the poll limit at every call; 0 makes every
@@ -232,6 +244,7 @@ Plan plan_tp(const prn_params* p, const Shape& sh, int K) {
 
 struct PlanSp {
   int ls;  // steps per lane
+  int nw;  // waves per workgroup
   int64_t n_ch, n_tiles, n_chains, n_wg;
   size_t status_off, n_status;  // words zeroed per launch: ticket, error, K*n_chains*n_ch statuses
   size_t agg_off, pre_off, rpart_off, total;
@@ -241,8 +254,10 @@ PlanSp plan_sp(const prn_params* p, const Shape& sh, int K, bool fused = false) 
   PlanSp pl{};
   pl.n_tiles = (p->d_h + 63) / 64;
   pl.n_chains = p->B * pl.n_tiles;
-  pl.ls = fused ? sp_ls_fused(p->cell, p->dtype, pl.n_chains) : sp_ls(p->cell, p->dtype, pl.n_chains);
-  const int lc = pl.ls * kSpNW;
+  const SpGeo geo = fused ? sp_geo_fused(p->cell, p->dtype, pl.n_chains) : sp_geo(p->cell, p->dtype, pl.n_chains);
+  pl.ls = geo.ls;
+  pl.nw = geo.nw;
+  const int lc = pl.ls * pl.nw;
   pl.n_ch = (p->T + lc - 1) / lc;
   pl.n_wg = pl.n_ch * pl.n_chains;
   const size_t nrec = size_t(K) * pl.n_chains * pl.n_ch;
@@ -369,13 +384,13 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     using T_ = std::true_type;
     using F_ = std::false_type;
     const prn::FxArgs fa = fx ? *fx : prn::FxArgs{nullptr, nullptr, nullptr, 0, nullptr};
-    auto launch = [&](auto ls, auto fxc) {
-      constexpr int LS = decltype(ls)::value;
+    auto launch = [&](auto ls, auto nw, auto fxc) {
+      constexpr int LS = decltype(ls)::value, NW = decltype(nw)::value;
       constexpr bool FX = decltype(fxc)::value;
       T* sout = static_cast<T*>(p->states_out);
       auto go = [&](auto ws, auto pic) {
-        prn::k_newton_sp<C, DT, LS, kSpNW, decltype(ws)::value, decltype(pic)::value, FX>
-            <<<unsigned(pl.n_wg), 64 * kSpNW, 0, st>>>(
+        prn::k_newton_sp<C, DT, LS, NW, decltype(ws)::value, decltype(pic)::value, FX>
+            <<<unsigned(pl.n_wg), 64 * NW, 0, st>>>(
                 static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles,
                 pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, spin_limit(),
                 pl.n_chains < kAggFirstBelowChains, fa);
@@ -388,27 +403,28 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
         if (sout) go(T_{}, F_{}); else go(F_{}, F_{});
       }
     };
+    using NW4 = std::integral_constant<int, kSpNW>;
     if (fx) {
       if constexpr (S == 2) {
         if constexpr (DT == prn::kBF16)
-          launch(std::integral_constant<int, kSpLsLstmBf16>{}, T_{});
+          launch(std::integral_constant<int, kSpLsLstmBf16>{}, NW4{}, T_{});
         else
-          launch(std::integral_constant<int, kSpLsLstm>{}, T_{});
+          launch(std::integral_constant<int, kSpLsFusedLstm>{}, NW4{}, T_{});
       } else {
-        launch(std::integral_constant<int, kSpLsGruFew>{}, T_{});
+        launch(std::integral_constant<int, kSpLsFusedGru>{}, NW4{}, T_{});
       }
     } else if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsLstmBf16>{}, F_{});
+        launch(std::integral_constant<int, kSpLsLstmBf16>{}, NW4{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsLstm>{}, F_{});
+        launch(std::integral_constant<int, kSpLsLstm>{}, NW4{}, F_{});
     } else {
-      if (pl.ls == kSpLsGruFew)
-        launch(std::integral_constant<int, kSpLsGruFew>{}, F_{});
+      if (pl.n_chains < kSpManyChains)
+        launch(std::integral_constant<int, kSpLsGruFew>{}, std::integral_constant<int, kSpNwGruFew>{}, F_{});
       else if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsGruManyBf16>{}, F_{});
+        launch(std::integral_constant<int, kSpLsGruManyBf16>{}, NW4{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsGruMany>{}, F_{});
+        launch(std::integral_constant<int, kSpLsGruMany>{}, NW4{}, F_{});
     }
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {
