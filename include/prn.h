@@ -85,11 +85,16 @@ typedef struct {
                               every state s_t of the returned trajectory (LSTM (c, h);
                               for the GRU it equals H_out).  The backward pass takes it as
                               its trajectory                                                */
-  int32_t picard_iters;    /* prn_newton_forward: Picard (Jacobi) sweeps H <- f(shift(H), x)
-                              from 0 before the K Newton iterations (FAQs "How many Newton
-                              iterations should I use?": picard_iters); 0 or 1 (more:
-                              PRN_ERR_UNSUPPORTED, as with PRN_ALGO=tp); r_0 is then the
-                              residual of the Picard guess                                  */
+  int32_t picard_iters;    /* prn_newton_forward: P >= 0 Picard (Jacobi) sweeps
+                              H <- f(shift(H), x) from 0 before the K Newton iterations
+                              (FAQs "How many Newton iterations should I use?":
+                              picard_iters), each sweep rounded to the storage dtype;
+                              r_0 is then the residual of the guess H^(P).  Every sub-chunk
+                              builds its own guess (H^(P)_t depends on the P steps up to t
+                              only): about P * (L + P / 2) cell evaluations per sub-chunk
+                              of L = 8 to 16 steps, so it is meant for a few sweeps.
+                              P >= T gives the unroll itself and runs as P = T.
+                              Single-pass schedule only (PRN_ALGO=tp: PRN_ERR_UNSUPPORTED) */
   void* error_out;         /* optional device uint32 word (4-byte aligned), forward and
                               backward entry points: bit 0 (PRN_FAULT_LOOKBACK) is ORed in
                               when a wait for a preceding chunk's record gave up (after about

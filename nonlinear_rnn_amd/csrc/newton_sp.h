@@ -181,10 +181,15 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 
 // WS: also write every state of the final trajectory to sout (the training
 // forward); a separate instance, so that the plain forward's registers are
-// not spent on it.  PIC: one Picard sweep before the Newton iterations, so
-// iteration 1 linearises at H^(1)_{t-1} = f(0 (h0 at a head), x_{t-1})
-// rather than at 0; it needs the projected inputs of one step before each
-// wave's sub-chunk, and r_0 is the residual of H^(1).
+// not spent on it.  PIC: P = picard >= 1 Picard (Jacobi) sweeps
+// H <- f(shift(H), x) from H = 0 before the Newton iterations, so iteration
+// 1 linearises at the guess H^(P) rather than at 0, and r_0 is the residual
+// of H^(P).  H^(P)_t depends on the P steps up to t only (it is the unroll
+// started from 0 P steps back, or from h0 at a head inside that window), so
+// every wave builds the guess of its own sub-chunk: P sweeps over its steps
+// in registers, each starting from H^(p-1) of the step before the sub-chunk,
+// which a short unroll over the p - 1 steps before it (from xproj, or from
+// h0 at the segment's head) supplies.
 // Waves per SIMD the compiler must leave room for: two for the longest
 // chunk (LS = 16, fp32 LSTM), whose register need otherwise lands a few
 // registers above 256 (the states_out instance: 264, 20 bytes of spills under
@@ -218,7 +223,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
             int64_t n_seqs, int64_t n_ch, int64_t n_tiles, int64_t n_chains, int K,
             typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast,
             typename Storage<DT>::T* __restrict__ sout, float* __restrict__ rpart, SpRecords rec,
-            unsigned spin_limit, bool agg_first, FxArgs fx) {
+            unsigned spin_limit, bool agg_first, FxArgs fx, int picard) {
   using ST = Storage<DT>;
   using Map = typename C::Map;
   constexpr int G = C::G, S = C::S, LC = LS * NW;
@@ -273,21 +278,72 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   typename ST::T* hp = Hout + (b * T + t0) * d_h + ch;
   typename ST::T* sp = WS ? sout + (b * T + t0) * S * d_h + ch : nullptr;
 
-  // the Picard guess H^(1) of the step before t0 (PIC; t0 not a head): a
-  // sweep from 0, or from h0 where that step is its segment's head
-  auto picard_before = [&](float* pm) {
-    float xm[G], p0[S];
-    load_xs<C, DT>(xp - G * d_h, d_h, xm);
+  // H^(p)_{t0-1}, the Picard iterate p of the step before the sub-chunk
+  // (PIC; t0 not a head, so that step lies in the segment of t0): the
+  // unroll over the p steps before t0, started from 0, or from h0 at the
+  // segment's head where that falls inside them; every value is rounded to
+  // the storage type like a stored sweep
+  auto picard_before = [&](int p, float* pm) {
 #pragma unroll
-    for (int q = 0; q < S; ++q) p0[q] = 0.0f;
-    if (h0 && sg.start == t0 - 1) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, p0);
-    C::f(xm, p0, cf.as, cf.a, pm);
+    for (int q = 0; q < S; ++q) pm[q] = 0.0f;
+    int64_t s0 = t0 - p;
+    if (s0 <= sg.start) {
+      s0 = sg.start;
+      if (h0) load_state<DT, S>(h0 + sg.seg * S * d_h + ch, d_h, pm);
+    }
+    for (int64_t t = s0; t < t0; ++t) {
+      float xm[G], nx[S];
+      load_xs<C, DT>(xp - (t0 - t) * G * d_h, d_h, xm);
+      C::f(xm, pm, cf.as, cf.a, nx);
 #pragma unroll
-    for (int q = 0; q < S; ++q) pm[q] = ST::round(pm[q]);
+      for (int q = 0; q < S; ++q) pm[q] = ST::round(nx[q]);
+    }
+  };
+  // the Picard guess H^(picard) at the sub-chunk's n steps, in place in hv;
+  // HD: the sub-chunk may hold segment heads (h0 there instead of the step
+  // before); t0 at a head needs no step before
+  auto picard_guess = [&](const float(*xs)[G], float(*hv)[S], int n, auto hd) {
+    constexpr bool HD = decltype(hd)::value;
+    const bool before = t0 != 0 && sg.start != t0;
+#pragma unroll
+    for (int j = 0; j < LS; ++j) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) hv[j][q] = 0.0f;   // H^(0)
+    }
+    for (int p = 1; p <= picard; ++p) {
+      float c[S];   // H^(p-1) of the step before the one being swept
+      if (p > 1 && before) {
+        picard_before(p - 1, c);
+      } else {
+#pragma unroll
+        for (int q = 0; q < S; ++q) c[q] = 0.0f;
+      }
+      SegTracker st = sg;
+#pragma unroll
+      for (int j = 0; j < LS; ++j) {
+        if (!HD || j < n) {
+          float prev[S];
+#pragma unroll
+          for (int q = 0; q < S; ++q) prev[q] = c[q];
+          if (HD && st.at(t0 + j)) {
+#pragma unroll
+            for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+            if (h0) load_state<DT, S>(h0 + st.seg * S * d_h + ch, d_h, prev);
+          }
+          float nx[S];
+          C::f(xs[j], prev, cf.as, cf.a, nx);
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            c[q] = hv[j][q];
+            hv[j][q] = ST::round(nx[q]);
+          }
+        }
+      }
+    }
   };
 
   // ---- load the tile; linearise iteration 1 at H^(0) = 0 (h0 at heads), or
-  // at the Picard guess H^(1) ----
+  // at the Picard guess H^(P) ----
   if (fast) {
     float xs[LS][G];
 #pragma unroll
@@ -297,32 +353,26 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       else
         load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
     }
+    float hv[PIC ? LS : 1][S];
     float pm[S];
-    if constexpr (PIC) picard_before(pm);
+    if constexpr (PIC) {
+      picard_guess(xs, hv, LS, std::false_type{});
+      picard_before(picard, pm);
+    }
 #pragma unroll
     for (int j = 0; j < LS; ++j) {
       if constexpr (!FX) xs_put(j, xs[j]);
       float fv[S];
       if constexpr (PIC) {
-        ms[j] = C::template fj<false>(xs[j], pm, cf.as, cf.a, false, fv);
+        ms[j] = C::template fj<false>(xs[j], j ? hv[j - 1] : pm, cf.as, cf.a, false, fv);
+#pragma unroll
+        for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, hv[j][q] - fv[q]);
       } else {
         ms[j] = C::fj0(xs[j], cf.a, fv);  // linearised at H^(0) = 0
-      }
-      acc = compose(ms[j], acc);
-      if constexpr (PIC) {
-        float z[S];
-#pragma unroll
-        for (int q = 0; q < S; ++q) z[q] = 0.0f;
-        C::f(xs[j], z, cf.as, cf.a, pm);
-#pragma unroll
-        for (int q = 0; q < S; ++q) {
-          pm[q] = ST::round(pm[q]);
-          rmax = rmax_bits(rmax, pm[q] - fv[q]);
-        }
-      } else {
 #pragma unroll
         for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);
       }
+      acc = compose(ms[j], acc);
     }
   } else if (wact) {
     float xs[LS][G];
@@ -335,11 +385,13 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           load_xs<C, DT>(xp + j * G * d_h, d_h, xs[j]);
       }
     }
+    float hv[PIC ? LS : 1][S];
     float pm[S];
     if constexpr (PIC) {
+      picard_guess(xs, hv, n, std::true_type{});
 #pragma unroll
       for (int q = 0; q < S; ++q) pm[q] = 0.0f;
-      if (t0 != 0 && sg.start != t0) picard_before(pm);
+      if (t0 != 0 && sg.start != t0) picard_before(picard, pm);
     }
     SegTracker st = sg;
 #pragma unroll
@@ -348,8 +400,13 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         if constexpr (!FX) xs_put(j, xs[j]);
         const bool head = st.at(t0 + j);
         float prev[S], fv[S];
+        if constexpr (PIC) {
 #pragma unroll
-        for (int q = 0; q < S; ++q) prev[q] = PIC ? pm[q] : 0.0f;
+          for (int q = 0; q < S; ++q) prev[q] = j ? hv[j - 1][q] : pm[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < S; ++q) prev[q] = 0.0f;
+        }
         if (head) {
 #pragma unroll
           for (int q = 0; q < S; ++q) prev[q] = 0.0f;
@@ -358,21 +415,8 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
         ms[j] = C::fj(xs[j], prev, cf.as, cf.a, head, fv);
         acc = compose(ms[j], acc);
         if constexpr (PIC) {
-          // H^(1)_t: f(h0, x_t) = fv at a head, f(0, x_t) elsewhere
-          if (head) {
 #pragma unroll
-            for (int q = 0; q < S; ++q) pm[q] = fv[q];
-          } else {
-            float z[S];
-#pragma unroll
-            for (int q = 0; q < S; ++q) z[q] = 0.0f;
-            C::f(xs[j], z, cf.as, cf.a, pm);
-          }
-#pragma unroll
-          for (int q = 0; q < S; ++q) {
-            pm[q] = ST::round(pm[q]);
-            rmax = rmax_bits(rmax, pm[q] - fv[q]);
-          }
+          for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, hv[j][q] - fv[q]);
         } else {
 #pragma unroll
           for (int q = 0; q < S; ++q) rmax = rmax_bits(rmax, fv[q]);

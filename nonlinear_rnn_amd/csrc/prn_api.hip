@@ -384,6 +384,9 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
     using T_ = std::true_type;
     using F_ = std::false_type;
     const prn::FxArgs fa = fx ? *fx : prn::FxArgs{nullptr, nullptr, nullptr, 0, nullptr};
+    // sweeps beyond T change nothing (every step's window already reaches
+    // its segment's head), so the kernel never runs more than T of them
+    const int picard = static_cast<int>(std::min<int64_t>(p->picard_iters, p->T));
     auto launch = [&](auto ls, auto nw, auto fxc) {
       constexpr int LS = decltype(ls)::value, NW = decltype(nw)::value;
       constexpr bool FX = decltype(fxc)::value;
@@ -393,7 +396,7 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
             <<<unsigned(pl.n_wg), 64 * NW, 0, st>>>(
                 static_cast<const T*>(xproj_v), h0, cu, p->a, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles,
                 pl.n_chains, K, static_cast<T*>(Hout_v), slast, sout, rpart, rec, spin_limit(),
-                pl.n_chains < kAggFirstBelowChains, fa);
+                pl.n_chains < kAggFirstBelowChains, fa, picard);
       };
       if constexpr (FX) {
         if (sout) go(T_{}, F_{}); else go(F_{}, F_{});
@@ -685,8 +688,6 @@ prn_status prn_newton_forward_noalloc(const void* xproj, const prn_params* p, co
   if (s != PRN_OK) return s;
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
   if (p->picard_iters < 0) return fail(PRN_ERR_INVALID_ARG, "picard_iters must be >= 0");
-  if (p->picard_iters > 1)
-    return fail(PRN_ERR_UNSUPPORTED, "picard_iters = %d: one Picard sweep is supported", p->picard_iters);
   if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;
   if (misaligned(residual_out, 4)) return fail(PRN_ERR_INVALID_ARG, "residual_out is not 4-byte aligned");
   const PlanSp pl = plan_sp(p, sh, K);
@@ -821,8 +822,6 @@ prn_status prn_newton_forward(const void* xproj, const prn_params* p, const void
   if (s != PRN_OK) return s;
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
   if (p->picard_iters < 0) return fail(PRN_ERR_INVALID_ARG, "picard_iters must be >= 0");
-  if (p->picard_iters > 1)
-    return fail(PRN_ERR_UNSUPPORTED, "picard_iters = %d: one Picard sweep is supported", p->picard_iters);
   if (p->picard_iters > 0 && use_three_phase())
     return fail(PRN_ERR_UNSUPPORTED, "Picard warm-start runs in the single-pass schedule only (PRN_ALGO=tp)");
   if ((s = check_newton_args(p, sh, xproj, h0, cu, H_out)) != PRN_OK) return s;

@@ -74,7 +74,7 @@ FAKE = 1 << 20   # an aligned non-null address; never dereferenced (validation f
     (dict(a=FAKE, workspace=FAKE, workspace_bytes=16), 3, B.PRN_ERR_WORKSPACE),
     (dict(a=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),                    # misaligned
     (dict(a=FAKE, picard_iters=-1), 3, B.PRN_ERR_INVALID_ARG),
-    (dict(a=FAKE, picard_iters=2), 3, B.PRN_ERR_UNSUPPORTED),
+    (dict(a=FAKE, picard_iters=2), 3, B.PRN_ERR_WORKSPACE),          # any P >= 0 passes validation
     (dict(a=FAKE, error_out=FAKE + 2), 3, B.PRN_ERR_INVALID_ARG),    # misaligned error word
 ])
 def test_newton_forward_rejects_bad_arguments_before_launch(kw, K, status):
@@ -304,8 +304,8 @@ def test_unsupported_status_raises_type_error():
     with pytest.raises(B.PrnError) as e:
         B._check(B.PRN_ERR_INVALID_ARG)
     assert not isinstance(e.value, TypeError)
-    p = _params(a=FAKE, picard_iters=2)
-    st = B.lib().prn_newton_forward(FAKE, ctypes.byref(p), None, 3, None, FAKE, None)
+    p = _params(a=FAKE, picard_iters=1, d_in=16)
+    st = B.lib().prn_newton_forward_fused(FAKE, FAKE, None, ctypes.byref(p), None, 3, None, FAKE, None, None)
     with pytest.raises(TypeError, match="Picard"):
         B._check(st)
 

@@ -224,6 +224,20 @@ def test_picard_warm_start(cell):
             assert np.abs(Hk[:, :P + k] - seq[:, :P + k]).max() <= 1e-13
     full = on.newton(cell, xp, a, 1, h0=h0, picard=T)
     assert np.abs(full["H"] - seq).max() <= 1e-13 and full["residuals"][0] <= 1e-13
+    # in a ragged pack the guess restarts at every head: after P sweeps and
+    # k iterations the first P + k steps of every segment are exact, also in
+    # segments shorter than P
+    cu = np.array([0, 1, 4, 12, 13, 24], dtype=np.int32)
+    xq = xp[:1].reshape(1, T, G, d).repeat(2, axis=1)
+    hq = rng.standard_normal((len(cu) - 1, S, d)) * 0.3
+    sq, _ = on.sequential(cell, xq, a, h0=hq, cu_seqlens=cu)
+    for P in (2, 5):
+        out = on.newton(cell, xq, a, 1, h0=hq, cu_seqlens=cu, picard=P, keep_iterates=True)
+        for lo, hi in zip(cu[:-1], cu[1:]):
+            m = min(hi, lo + P + 1)
+            assert np.abs(out["H"][:, lo:m] - sq[:, lo:m]).max() <= 1e-13
+        if P == 2:   # and not beyond: the segment of 11 steps is not solved at step 3
+            assert np.abs(out["H"][:, 4:12] - sq[:, 4:12]).max() > 1e-8
     g1 = on.newton(cell, xp, a, 1, h0=h0, picard=1)
     _, _, f, _ = cells.cell_fns(cell)
     guess = f(np.concatenate([h0[:, None], np.zeros((B, T - 1, S, d))], axis=1), xp, a)  # one sweep from 0
