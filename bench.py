@@ -34,6 +34,27 @@ sys.path.insert(0, ROOT)
 METRIC = "Newton-forward tokens/sec at K=3 (B*T/s) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+# fp32 products run on the bf16 matrix cores as six products of exact bf16
+# splits (csrc/bf16split.h): the executed matrix-core work per fp32 flop
+F32_SPLIT_PRODUCTS = 6
+
+
+def mfma_roofline(dtype: str, flops: float, ms: float, **extra) -> dict:
+    """Roofline of a matrix-core contraction: algorithmic flops over time
+    against the peak of the storage dtype's own matrix instruction; an fp32
+    contraction also states the bf16 matrix-core work it executes (six term
+    products per fp32 product) against the bf16 peak, the unit that bounds it."""
+    ach = flops / (ms * 1e-3) / 1e12
+    r = {"bound": "mfma", "achieved": ach, "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+         "frac": ach / MFMA_PEAK_TFLOPS[dtype], "algorithmic_flops": flops}
+    if dtype == "f32":
+        ex = F32_SPLIT_PRODUCTS * flops
+        r["matrix_core"] = {"instruction": "v_mfma_f32_32x32x16_bf16 on exact bf16 splits",
+                            "executed_flops": ex, "achieved": ex / (ms * 1e-3) / 1e12,
+                            "peak": MFMA_PEAK_TFLOPS["bf16"],
+                            "frac": ex / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"]}
+    r.update(extra)
+    return r
 
 
 def algorithmic_newton_bytes(w) -> float:
@@ -403,9 +424,7 @@ def main() -> int:
         backward["input_proj_backward"] = {
             "kernels": "transposes + k_proj (dx) + split-K k_proj (dW) + ordered sums (prn_input_proj_backward)",
             "ms_mean": pb_ms, "ms_min": float(t_pb.min()), "workspace_bytes": int(pws.numel()),
-            "roofline": {"bound": "mfma", "achieved": pfl / (pb_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
-                         "unit": "TFLOP/s", "frac": pfl / (pb_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-                         "algorithmic_flops": pfl}}
+            "roofline": mfma_roofline(w.dtype, pfl, pb_ms)}
         del dxi, dWi, pws
         print(f"[bench] backward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
@@ -435,10 +454,8 @@ def main() -> int:
                  "speedup_vs_two_calls": float(t_step.mean()) / fx_ms,
                  "max_abs_vs_two_calls": float((Hf.float() - H.float()).abs().max().item()),
                  "residuals": resf.cpu().tolist(),
-                 "roofline": {"bound": "mfma", "achieved": ffl / (fx_ms * 1e-3) / 1e12,
-                              "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                              "frac": ffl / (fx_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-                              "traffic": profiled_traffic("k_newton_sp_fused", w.name), "algorithmic_flops": ffl}}
+                 "roofline": mfma_roofline(w.dtype, ffl, fx_ms,
+                                           traffic=profiled_traffic("k_newton_sp_fused", w.name))}
         del Hf
         print(f"[bench] fused forward timed ({args.steps} calls)", file=sys.stderr, flush=True)
 
@@ -582,10 +599,8 @@ def main() -> int:
         roof_newton["valu_lane_slots_per_channel_step"] = next(
             (_field(prof, k) for k in prof if k.startswith("valu_lane_slots_per_channel_step")), None)
     fl = proj_flops(w)
-    roof_proj = {"kernel": f"k_proj, {proj_tiles(w)} tiles (prn_input_proj)", "bound": "mfma",
-                 "achieved": fl / (proj_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                 "traffic": profiled_traffic("k_proj", w.name), "algorithmic_flops": fl}
-    roof_proj["frac"] = roof_proj["achieved"] / roof_proj["peak"]
+    roof_proj = {"kernel": f"k_proj, {proj_tiles(w)} tiles (prn_input_proj)",
+                 **mfma_roofline(w.dtype, fl, proj_ms, traffic=profiled_traffic("k_proj", w.name))}
     dominant = roof_newton if newton_ms >= proj_ms else roof_proj
 
     out = {

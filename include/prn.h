@@ -116,8 +116,12 @@ enum { PRN_FAULT_LOOKBACK = 1 };
  *   bias   (G*d_h) fp32, or NULL for none (LSTM callers fold the +1 forget
  *          bias in here)
  *   xproj_out (B, T, G, d_h) storage dtype
- * fp32 storage multiplies in fp32 on the matrix cores; bf16 multiplies bf16
- * with fp32 accumulation and rounds the result to bf16.  Uses no workspace. */
+ * fp32 storage: fp32-accurate products on the bf16 matrix cores (each
+ * operand split exactly into three bf16 terms; the six term products of
+ * weight 2^-16 or more, so the dropped part is below 3 * 2^-24 |a b|),
+ * accumulated in fp32; non-finite inputs give non-finite outputs.  bf16
+ * multiplies bf16 with fp32 accumulation and rounds the result to bf16.
+ * Uses no workspace. */
 prn_status prn_input_proj(const void* x, const void* W, const float* bias,
                           const prn_params* params, void* xproj_out);
 

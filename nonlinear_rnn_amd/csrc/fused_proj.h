@@ -22,12 +22,14 @@
 // the 32-column blocks cb = w, w + NW, ... and all LC / 32 row blocks.
 //
 // The products use the instruction, the operand layout and the k order of
-// the stand-alone projection kernel (proj.hip): fp32 v_mfma_f32_32x32x2_f32
-// with k = 8 kb + 4 h + s, bf16 v_mfma_f32_32x32x16_bf16 with
-// k = 16 kb + 8 h + e, accumulators from 0 and the bias added last, so the
-// tile is bitwise the stand-alone projection's output.
+// the stand-alone projection kernel (proj.hip): bf16 v_mfma_f32_32x32x16_bf16
+// with k = 16 kb + 8 h + e; fp32 the same instruction on the exact bf16
+// splits of the operands (bf16split.h), six term products per 16 k in the
+// same order, k = 16 ks + 8 h + e; accumulators from 0 and the bias added
+// last, so the tile is bitwise the stand-alone projection's output.
 #pragma once
 
+#include "bf16split.h"
 #include "prn_device.h"
 
 namespace prn {
@@ -174,6 +176,36 @@ __device__ __forceinline__ void fused_tile(uint8_t* lds, const FxArgs& fx, int64
     asm volatile("" ::: "memory");
     if (kt + 2 < nk) issue(kt + 2, static_cast<int>((kt + 2) % Gm::NBUF));
     const uint8_t* L = lds + static_cast<int>(kt % Gm::NBUF) * Gm::STAGE;
+    if constexpr (DT == kF32) {
+      // 16 k per stage: half h takes chunks 2 h and 2 h + 1 (k = 16 kt + 8 h + e)
+      static_assert(Gm::CPR == 4, "the fp32 split path takes 16 k per stage");
+      const int kv = 2 * half;
+      sp_bf16x8 bp[Gm::NCB][3];
+#pragma unroll
+      for (int j = 0; j < Gm::NCB; ++j) {
+        const int cb = w + j * NW;
+        const int r = Gm::LC + cb * 32 + l32;
+        if (cb < Gm::NCB_ALL)
+          split3(*reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv)),
+                 *reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv + 1)), bp[j][0], bp[j][1],
+                 bp[j][2]);
+      }
+#pragma unroll
+      for (int i = 0; i < Gm::NRB; ++i) {
+        const int r = i * 32 + l32;
+        sp_bf16x8 ap[3];
+        split3(*reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv)),
+               *reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv + 1)), ap[0], ap[1], ap[2]);
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+#pragma unroll
+          for (int j = 0; j < Gm::NCB; ++j)
+            if (w + j * NW < Gm::NCB_ALL)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
+      }
+      continue;
+    }
 #pragma unroll
     for (int kb = 0; kb < Gm::CPR / 2; ++kb) {
       const int kv = kb * 2 + half;
@@ -189,25 +221,14 @@ __device__ __forceinline__ void fused_tile(uint8_t* lds, const FxArgs& fx, int64
         const int r = Gm::LC + cb * 32 + l32;
         if (cb < Gm::NCB_ALL) bv[j] = *reinterpret_cast<const fx_f32x4*>(L + r * Gm::ROWB + 16 * fx_pos(r, kv));
       }
-      if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int i = 0; i < Gm::NRB; ++i)
+      for (int i = 0; i < Gm::NRB; ++i)
 #pragma unroll
-          for (int j = 0; j < Gm::NCB; ++j)
-            if (w + j * NW < Gm::NCB_ALL)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(fx_bf16x8, av[i]),
-                                                                  __builtin_bit_cast(fx_bf16x8, bv[j]), acc[i][j], 0,
-                                                                  0, 0);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int i = 0; i < Gm::NRB; ++i)
-#pragma unroll
-            for (int j = 0; j < Gm::NCB; ++j)
-              if (w + j * NW < Gm::NCB_ALL)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < Gm::NCB; ++j)
+          if (w + j * NW < Gm::NCB_ALL)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(fx_bf16x8, av[i]),
+                                                                __builtin_bit_cast(fx_bf16x8, bv[j]), acc[i][j], 0, 0,
+                                                                0);
     }
   }
   __syncthreads();   // every wave is done with the last stage

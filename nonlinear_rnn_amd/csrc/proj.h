@@ -7,7 +7,9 @@
 namespace prn {
 
 // C[M, N] = A[M, K] * B[N, K]^T + bias[N]; A, B, C row-major, K contiguous.
-// bf16 = false: fp32 storage, fp32 matrix-core products.
+// bf16 = false: fp32 storage; fp32-accurate products on the bf16 matrix
+//               cores (six products of exact three-term bf16 splits,
+//               bf16split.h), fp32 accumulation.
 // bf16 = true : bf16 storage, bf16 products with fp32 accumulation, result
 //               rounded to bf16 (nearest even).
 // Requires K % 4 == 0 (fp32) or K % 8 == 0 (bf16) and 16-byte aligned A, B, C.

@@ -22,11 +22,16 @@
 // Operand layout of the 32 x 32 matrix instructions (wave64): lane l feeds
 // row (l % 32) of A and column (l % 32) of B; lane half h = l / 32 feeds the
 // k values of that half.  Only the pairing of A's and B's k values matters to
-// a dot product, so each lane reads 16 contiguous bytes of its LDS row
-// (4 fp32 or 8 bf16 k values) and A and B use the same k order.
-//   fp32: v_mfma_f32_32x32x2_f32 takes one k per half; the 4 values of a
-//         16-byte read feed 4 instructions (k = 8 kb + 4 h + s, s = 0..3).
-//   bf16: v_mfma_f32_32x32x16_bf16 takes 8 k per half (k = 16 kb + 8 h + e).
+// a dot product, so each lane reads contiguous bytes of its LDS row and A
+// and B use the same k order.
+//   bf16: v_mfma_f32_32x32x16_bf16 takes 8 k per half (k = 16 kb + 8 h + e),
+//         one 16-byte read.
+//   fp32: the same bf16 instruction on the exact three-term bf16 splits of
+//         the operands (bf16split.h), six term products per 16 k: a lane
+//         reads two 16-byte chunks (k = 16 ks + 8 h + e, e = 0..7) and
+//         splits them in registers.  The sums agree with fp32 products to
+//         fp32 rounding, in 3/8 of the matrix-core time of
+//         v_mfma_f32_32x32x2_f32.
 // Result layout: lane l, accumulator r holds row 8 (r / 4) + 4 (l / 32) +
 // (r % 4), column l % 32.
 //
@@ -42,11 +47,13 @@
 //
 // Measured (262144 x 1024 x 256 fp32; 262144 x 1536 x 512 bf16): 1.12 ms and
 // 0.57 ms with 256 x 256 tiles, against 1.31 and 0.88 ms for 128 x 128 tiles
-// staged through registers into padded LDS rows.
+// staged through registers into padded LDS rows; the fp32 case takes
+// 0.79 ms on the split bf16 products (1.13 ms on v_mfma_f32_32x32x2_f32).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 
+#include "bf16split.h"
 #include "proj.h"
 
 namespace prn {
@@ -72,8 +79,30 @@ __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0, 0, 0,
 // LDS position of chunk kv of row r
 __device__ __forceinline__ int lds_pos(int r, int kv) { return kv ^ ((r / RPG) & (CPR - 1)); }
 
+// LDS address (byte offset) of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)const_cast<void*>(p)));
+}
+
+// One direct-to-LDS load of 16 bytes per lane (lane l lands at LDS byte
+// lds + 16 l; lds is wave-uniform, the instruction takes it from M0).
+// Issued from asm so that the compiler does not track it: it would make
+// every later LDS read wait for all such loads in flight, the next stage's
+// included, although the reads touch only the stage buffer that the stage
+// barrier has already made complete.  The kernel waits for these loads
+// itself (vmcnt(0) before every stage barrier).  M0 written by a scalar
+// instruction needs one wait state before the load reads it; nothing else
+// in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is a reserved register
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // round to nearest even (v_cvt_pk_bf16_f32); NaN stays a quiet NaN
 __device__ __forceinline__ uint16_t bf16_rne(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
 
 // WR x WC waves, each owning WM x WN blocks of 32 x 32
 template <int WR, int WC, int WM_ = 2, int WN_ = 2>
@@ -122,35 +151,46 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
   // the chunk each of this lane's loads fetches: wave load p fills LDS bytes
   // [1024 (wave IPW + p), +1024) of a stage, lane l the 16 bytes at 16 l,
   // i.e. position q of row r with 16 (r CPR + q) = 1024 (wave IPW + p) + 16 l
-  const uint8_t* src[IPW];
-  int kvb[IPW];
+  //
+  // Without edges (EDGE = false) the 64 lanes of a wave load cover 64 / CPR
+  // whole rows, which lie all in the x rows or all in the W rows: the first
+  // row's address is wave-uniform (scalar registers) and each lane adds a
+  // 32-bit offset (fewer vector registers than a 64-bit address per load).
+  static_assert(BM % (64 / CPR) == 0, "a wave load must not straddle the x and W rows");
+  const uint8_t* src[EDGE ? IPW : 1];
+  int kvb[EDGE ? IPW : 1];
+  const uint8_t* gbase[EDGE ? 1 : IPW];
+  uint32_t voff[EDGE ? 1 : IPW];
 #pragma unroll
   for (int p = 0; p < IPW; ++p) {
     const int v = (wave * IPW + p) * 64 + lane;
     const int r = v / CPR, q = v % CPR;
-    kvb[p] = lds_pos(r, q) * 16;
-    int64_t g = r < BM ? m0 + r : n0 + r - BM;
-    if (EDGE) g = r < BM ? (g < M ? g : M - 1) : (g < N ? g : N - 1);
-    src[p] = (r < BM ? A + g * lda : B + g * ldb) + kvb[p];
+    if constexpr (EDGE) {
+      kvb[p] = lds_pos(r, q) * 16;
+      int64_t g = r < BM ? m0 + r : n0 + r - BM;
+      g = r < BM ? (g < M ? g : M - 1) : (g < N ? g : N - 1);
+      src[p] = (r < BM ? A + g * lda : B + g * ldb) + kvb[p];
+    } else {
+      const int r0 = (wave * IPW + p) * (64 / CPR);
+      gbase[p] = r0 < BM ? A + (m0 + r0) * lda : B + (n0 + r0 - BM) * ldb;
+      voff[p] = static_cast<uint32_t>((r - r0) * (r0 < BM ? lda : ldb) + lds_pos(r, q) * 16);
+    }
   }
   auto issue = [&](int64_t kt, int buf) {
     uint8_t* base = lds + buf * STAGE + wave * IPW * 1024;
 #pragma unroll
     for (int p = 0; p < IPW; ++p) {
-      const void* g = src[p] + kt * ROWB;
-      if (EDGE && kt * ROWB + kvb[p] >= rowbytes) g = kZeroChunk;
-      __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)(base + p * 1024), 16, 0, 0);
+      const void* g;
+      if constexpr (EDGE) {
+        g = src[p] + kt * ROWB;
+        if (kt * ROWB + kvb[p] >= rowbytes) g = kZeroChunk;
+      } else {
+        g = gbase[p] + kt * ROWB + voff[p];
+      }
+      dma16(g, lds_addr(base + p * 1024));
     }
   };
 
-  // bias of this lane's output columns, loaded up front (the epilogue must
-  // not wait on a load between its stores)
-  float bcol[WN];
-#pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    const int64_t gn = n0 + wc * WN * 32 + j * 32 + (lane & 31);
-    bcol[j] = (bias && (!EDGE || gn < N)) ? bias[gn] : 0.0f;
-  }
   f32x16 acc[WM][WN];
 #pragma unroll
   for (int i = 0; i < WM; ++i)
@@ -172,40 +212,71 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
     asm volatile("" ::: "memory");
     if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
     const uint8_t* L = lds + cur * STAGE;
+    if constexpr (BF16) {
 #pragma unroll
-    for (int kb = 0; kb < CPR / 2; ++kb) {  // 32 bytes of k per step: two 16-byte halves
-      const int kv = kb * 2 + half;
-      f32x4 av[WM], bv[WN];
+      for (int kb = 0; kb < CPR / 2; ++kb) {  // 32 bytes of k per step: two 16-byte halves
+        const int kv = kb * 2 + half;
+        f32x4 av[WM], bv[WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const int r = wr * WM * 32 + i * 32 + l32;
-        av[i] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
-      }
+        for (int i = 0; i < WM; ++i) {
+          const int r = wr * WM * 32 + i * 32 + l32;
+          av[i] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
+        }
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int r = BM + wc * WN * 32 + j * 32 + l32;
-        bv[j] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
-      }
-      if constexpr (BF16) {
+        for (int j = 0; j < WN; ++j) {
+          const int r = BM + wc * WN * 32 + j * 32 + l32;
+          bv[j] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
+        }
 #pragma unroll
         for (int i = 0; i < WM; ++i)
 #pragma unroll
           for (int j = 0; j < WN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                                 __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
-      } else {
+      }
+    } else {
+      // fp32: 16 k per step, half h takes chunks 4 ks + 2 h and 4 ks + 2 h + 1
+      // (k = 16 ks + 8 h + e); six bf16 products per block and step
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+      for (int ks = 0; ks < CPR / 4; ++ks) {
+        const int kv = ks * 4 + half * 2;
+        bf16x8 bp[WN][3];
 #pragma unroll
-          for (int i = 0; i < WM; ++i)
+        for (int j = 0; j < WN; ++j) {
+          const int r = BM + wc * WN * 32 + j * 32 + l32;
+          split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
+                 *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), bp[j][0], bp[j][1],
+                 bp[j][2]);
+        }
+        // the x blocks are split one at a time (registers)
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const int r = wr * WM * 32 + i * 32 + l32;
+          bf16x8 ap[3];
+          split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
+                 *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), ap[0], ap[1], ap[2]);
+#pragma unroll
+          for (int t = 0; t < 6; ++t)
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
+        }
+        // keep the scheduler from hoisting the next step's reads and splits
+        // above these products (their registers would not fit)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // epilogue: bias, round to the storage dtype, store
+  // epilogue: bias, round to the storage dtype, store.  The bias of this
+  // lane's columns is loaded here, before the first store (not held in
+  // registers through the main loop, nor awaited between stores)
+  float bcol[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int64_t gn = n0 + wc * WN * 32 + j * 32 + (lane & 31);
+    bcol[j] = (bias && (!EDGE || gn < N)) ? bias[gn] : 0.0f;
+  }
   const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
