@@ -27,11 +27,14 @@
 //   bf16: v_mfma_f32_32x32x16_bf16 takes 8 k per half (k = 16 kb + 8 h + e),
 //         one 16-byte read.
 //   fp32: the same bf16 instruction on the exact three-term bf16 splits of
-//         the operands (bf16split.h), six term products per 16 k: a lane
-//         reads two 16-byte chunks (k = 16 ks + 8 h + e, e = 0..7) and
-//         splits them in registers.  The sums agree with fp32 products to
-//         fp32 rounding, in 3/8 of the matrix-core time of
-//         v_mfma_f32_32x32x2_f32.
+//         the operands (bf16split.h), six term products per 16 k
+//         (k = 16 ks + 8 h + e, e = 0..7).  The sums agree with fp32
+//         products to fp32 rounding, in 3/8 of the matrix-core time of
+//         v_mfma_f32_32x32x2_f32.  The 16-wave tiles split every stage once,
+//         cooperatively, into three bf16 term planes in LDS (each value by
+//         one thread) and multiply from the planes while the next stage is
+//         split; the 4-wave tiles, which have room for the registers but not
+//         the LDS of that, split the two 16-byte chunks each lane reads.
 // Result layout: lane l, accumulator r holds row 8 (r / 4) + 4 (l / 32) +
 // (r % 4), column l % 32.
 //
@@ -48,7 +51,8 @@
 // Measured (262144 x 1024 x 256 fp32; 262144 x 1536 x 512 bf16): 1.12 ms and
 // 0.57 ms with 256 x 256 tiles, against 1.31 and 0.88 ms for 128 x 128 tiles
 // staged through registers into padded LDS rows; the fp32 case takes
-// 0.79 ms on the split bf16 products (1.13 ms on v_mfma_f32_32x32x2_f32).
+// 0.75 ms on the split bf16 products from term planes (0.79 ms splitting in
+// registers, 1.13 ms on v_mfma_f32_32x32x2_f32).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -129,7 +133,11 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
   using Tl = Tile<WR, WC, WM, WN>;
   constexpr int BM = Tl::BM, BN = Tl::BN, IPW = Tl::IPW, STAGE = Tl::STAGE;
   constexpr int ELT = BF16 ? 2 : 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  // fp32 with 16 waves (PLANES): two K stages of 64 bytes per row, then two
+  // sets of the three bf16 term planes of a stage (32 bytes per row each):
+  // 320 bytes per row.  Otherwise two K stages of 128 bytes per row.
+  constexpr bool PLANES = !BF16 && Tl::NW == 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[PLANES ? Tl::NROWS * 320 : 2 * STAGE];
   {
     const int64_t z = blockIdx.y;
     A += z * K * ELT;
@@ -199,71 +207,176 @@ k_proj(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const float
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t nk = (rowbytes + ROWB - 1) / ROWB;
   const int half = lane >> 5, l32 = lane & 31;
-  issue(0, 0);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // this wave's loads of stage kt have landed and its reads of the other
-    // buffer are done; after the barrier the same holds for every wave
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-    const uint8_t* L = lds + cur * STAGE;
-    if constexpr (BF16) {
+  if constexpr (!PLANES) {
+    const int64_t nk = (rowbytes + ROWB - 1) / ROWB;
+    issue(0, 0);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      // this wave's loads of stage kt have landed and its reads of the other
+      // buffer are done; after the barrier the same holds for every wave
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+      const uint8_t* L = lds + cur * STAGE;
+      if constexpr (BF16) {
 #pragma unroll
-      for (int kb = 0; kb < CPR / 2; ++kb) {  // 32 bytes of k per step: two 16-byte halves
-        const int kv = kb * 2 + half;
-        f32x4 av[WM], bv[WN];
+        for (int kb = 0; kb < CPR / 2; ++kb) {  // 32 bytes of k per step: two 16-byte halves
+          const int kv = kb * 2 + half;
+          f32x4 av[WM], bv[WN];
 #pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const int r = wr * WM * 32 + i * 32 + l32;
-          av[i] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
-        }
+          for (int i = 0; i < WM; ++i) {
+            const int r = wr * WM * 32 + i * 32 + l32;
+            av[i] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
+          }
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const int r = BM + wc * WN * 32 + j * 32 + l32;
-          bv[j] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
-        }
+          for (int j = 0; j < WN; ++j) {
+            const int r = BM + wc * WN * 32 + j * 32 + l32;
+            bv[j] = *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv));
+          }
 #pragma unroll
-        for (int i = 0; i < WM; ++i)
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
-                                                                __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // fp32: 16 k per step, half h takes chunks 4 ks + 2 h and 4 ks + 2 h + 1
-      // (k = 16 ks + 8 h + e); six bf16 products per block and step
-#pragma unroll
-      for (int ks = 0; ks < CPR / 4; ++ks) {
-        const int kv = ks * 4 + half * 2;
-        bf16x8 bp[WN][3];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const int r = BM + wc * WN * 32 + j * 32 + l32;
-          split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
-                 *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), bp[j][0], bp[j][1],
-                 bp[j][2]);
-        }
-        // the x blocks are split one at a time (registers)
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const int r = wr * WM * 32 + i * 32 + l32;
-          bf16x8 ap[3];
-          split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
-                 *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), ap[0], ap[1], ap[2]);
-#pragma unroll
-          for (int t = 0; t < 6; ++t)
+          for (int i = 0; i < WM; ++i)
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, av[i]), __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
         }
-        // keep the scheduler from hoisting the next step's reads and splits
-        // above these products (their registers would not fit)
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // fp32: 16 k per step, half h takes chunks 4 ks + 2 h and 4 ks + 2 h + 1
+        // (k = 16 ks + 8 h + e); six bf16 products per block and step
+#pragma unroll
+        for (int ks = 0; ks < CPR / 4; ++ks) {
+          const int kv = ks * 4 + half * 2;
+          bf16x8 bp[WN][3];
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int r = BM + wc * WN * 32 + j * 32 + l32;
+            split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
+                   *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), bp[j][0], bp[j][1],
+                   bp[j][2]);
+          }
+          // the x blocks are split one at a time (registers)
+#pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            const int r = wr * WM * 32 + i * 32 + l32;
+            bf16x8 ap[3];
+            split3(*reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv)),
+                   *reinterpret_cast<const f32x4*>(L + r * ROWB + 16 * lds_pos(r, kv + 1)), ap[0], ap[1], ap[2]);
+#pragma unroll
+            for (int t = 0; t < 6; ++t)
+#pragma unroll
+              for (int j = 0; j < WN; ++j)
+                acc[i][j] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
+          }
+          // keep the scheduler from hoisting the next step's reads and splits
+          // above these products (their registers would not fit)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
+    // fp32 with 16 waves (bf16split.h): K stages of 16 k (64 bytes per row) double
+    // buffered; every stage is split once, cooperatively (each operand value
+    // by one thread, not by each of the four waves that read it), into
+    // three bf16 term planes, also double buffered.  While the planes of
+    // stage kt are multiplied, the same waves split stage kt + 1 and stage
+    // kt + 2 is in flight.  Stage rows: 16-byte chunk kv of row r at
+    // position kv ^ ((r / 4) % 4); plane rows: 16 k as two chunks of 8 bf16
+    // (k = 8 c + e), chunk c at position c ^ ((r / 8) % 2).
+    constexpr int SROW = 64, SCPR = SROW / 16, FST = Tl::NROWS * SROW;
+    constexpr int PROW = 32, PLANE = Tl::NROWS * PROW, PST = 3 * PLANE;
+    constexpr int IPW2 = FST / 1024 / Tl::NW;
+    constexpr int UPT = Tl::NROWS * 2 / Tl::NTHR;   // 8-value units per thread and stage
+    static_assert(FST % (1024 * Tl::NW) == 0 && Tl::NROWS * 2 % Tl::NTHR == 0 && IPW2 < 16,
+                  "stage split over the waves and threads");
+    static_assert(2 * FST + 2 * PST == Tl::NROWS * 320, "LDS layout");
+    uint8_t* const Fb = lds;
+    uint8_t* const Pb = lds + 2 * FST;
+    auto fpos = [](int r, int kv) { return kv ^ ((r >> 2) & 3); };
+    auto ppos = [](int r, int c) { return c ^ ((r >> 3) & 1); };
+    const uint8_t* src2[IPW2];
+    int kvb2[IPW2];
+#pragma unroll
+    for (int p = 0; p < IPW2; ++p) {
+      const int v = (wave * IPW2 + p) * 64 + lane;
+      const int r = v / SCPR, q = v % SCPR;
+      kvb2[p] = fpos(r, q) * 16;
+      int64_t g = r < BM ? m0 + r : n0 + r - BM;
+      if (EDGE) g = r < BM ? (g < M ? g : M - 1) : (g < N ? g : N - 1);
+      src2[p] = (r < BM ? A + g * lda : B + g * ldb) + kvb2[p];
+    }
+    auto issue2 = [&](int64_t kt, int buf) {
+#pragma unroll
+      for (int p = 0; p < IPW2; ++p) {
+        const void* g = src2[p] + kt * SROW;
+        if (EDGE && kt * SROW + kvb2[p] >= rowbytes) g = kZeroChunk;
+        dma16(g, lds_addr(Fb + buf * FST + (wave * IPW2 + p) * 1024));
+      }
+    };
+    auto split_stage = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        const int v = tid + q * Tl::NTHR;
+        const int r = v >> 1, c = v & 1;
+        const uint8_t* f = Fb + buf * FST + r * SROW;
+        bf16x8 t0, t1, t2;
+        split3(*reinterpret_cast<const f32x4*>(f + 16 * fpos(r, 2 * c)),
+               *reinterpret_cast<const f32x4*>(f + 16 * fpos(r, 2 * c + 1)), t0, t1, t2);
+        uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, c);
+        *reinterpret_cast<bf16x8*>(d) = t0;
+        *reinterpret_cast<bf16x8*>(d + PLANE) = t1;
+        *reinterpret_cast<bf16x8*>(d + 2 * PLANE) = t2;
+      }
+    };
+    const int64_t nk = (rowbytes + SROW - 1) / SROW;
+    issue2(0, 0);
+    if (nk > 1) issue2(1, 1);
+    asm volatile("" ::: "memory");
+    if (nk > 1)
+      __builtin_amdgcn_s_waitcnt((IPW2 & 15) | (7 << 4) | (15 << 8));   // vmcnt(IPW2): stage 0 has landed
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    split_stage(0);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      // the planes of stage kt are complete and stage kt + 1 has landed;
+      // every wave is done with the planes of stage kt - 1 and with the
+      // stage buffer of stage kt
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 2 < nk) issue2(kt + 2, cur);
+      if (kt + 1 < nk) split_stage(cur ^ 1);
+      // six term products per block: half h takes plane chunk h
+      // (k = 16 kt + 8 h + e); the x blocks one at a time (registers)
+      const uint8_t* P = Pb + cur * PST;
+      bf16x8 bp[WN][3];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int r = BM + wc * WN * 32 + j * 32 + l32;
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+          bp[j][u] = *reinterpret_cast<const bf16x8*>(P + u * PLANE + r * PROW + 16 * ppos(r, half));
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const int r = wr * WM * 32 + i * 32 + l32;
+        bf16x8 ap[3];
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+          ap[u] = *reinterpret_cast<const bf16x8*>(P + u * PLANE + r * PROW + 16 * ppos(r, half));
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
       }
     }
   }
