@@ -76,10 +76,10 @@ def algorithmic_backward_bytes(w) -> float:
 
 # the sources each profiled kernel is built and launched from
 KERNEL_SOURCES = {
-    "k_newton_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
-    "k_bw_sp": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
-    "k_newton_sp_fused": ["prn_device.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
-    "k_proj": ["proj.h", "proj.hip"],
+    "k_newton_sp": ["prn_device.h", "bf16split.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
+    "k_bw_sp": ["prn_device.h", "bf16split.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "backward.h", "prn_api.hip"],
+    "k_newton_sp_fused": ["prn_device.h", "bf16split.h", "fused_proj.h", "newton_kernels.h", "newton_sp.h", "prn_api.hip"],
+    "k_proj": ["proj.h", "bf16split.h", "proj.hip"],
     "k_hm": ["prn_device.h", "headmix.h", "prn_api.hip"],
 }
 
