@@ -140,13 +140,16 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias,
  * prn_input_proj_backward_workspace_bytes(params); it covers all three
  * outputs), stream; n_seqs must be 0 (a ragged pack is B = 1, T = N).
  * dxproj must be 16-byte aligned (it is read by the matrix-core tiles);
- * the other pointers need only their element alignment.
+ * so must x when dW_out is asked for and G*d_h and d_in are multiples of
+ * 256 (dW then reads both operands along their rows); the other pointers
+ * need only their element alignment.
  * Products on the matrix cores as in prn_input_proj (fp32, or bf16 with fp32
  * accumulation); every sum is taken in a fixed order (the result is bitwise
  * reproducible) and rounded once to the storage dtype; dbias sums in fp32.
  * The weight gradient is split over token slices whose fp32 partial sums are
- * added in slice order; both of its operands are first transposed into the
- * workspace (the workspace holds dxproj and x once more). */
+ * added in slice order.  When G*d_h and d_in are multiples of 256 its tiles
+ * read both operands along their rows; otherwise both are first transposed
+ * into the workspace (which then holds dxproj and x once more). */
 prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void* W,
                                    const prn_params* params, void* dx_out, void* dW_out,
                                    float* dbias_out);

@@ -592,13 +592,15 @@ struct PlanPb {
   int64_t M, N, Kd;      // tokens, G d_h, d_in
   bool do_dx, do_dw, do_db;
   bool pad_g;            // dxproj rows are not whole 16-byte chunks: use a padded copy for dx
+  bool tn;               // dW without transposed copies (G d_h and d_in multiples of 256)
   int64_t Np;            // row length (elements) of W^T and of the padded dxproj
   int splits;
   int64_t ks, Mp, n_rt;  // tokens per slice, padded tokens, 64-token tiles of the dxproj transpose
   int64_t n_slices, per;  // the tile column sums: n_rt rows reduced in n_slices slices of per rows
   size_t wt_off, gp_off, gt_off, xt_off, part_off, csum_off, cslice_off, total;
 };
-constexpr int64_t kPbWgTarget = 1024;   // workgroups the split-K product aims for
+constexpr int64_t kPbWgTarget = 1024;   // workgroups the split-K product aims for (128 x 128 tiles)
+constexpr int64_t kPbWgTargetTn = 256;  // the same for 256 x 256 tiles, one workgroup per CU
 constexpr int64_t kPbTok = 256;         // slices are multiples of 256 tokens
 
 PlanPb plan_pb(const prn_params* p, const Shape& sh, bool dx, bool dw, bool db) {
@@ -612,10 +614,15 @@ PlanPb plan_pb(const prn_params* p, const Shape& sh, bool dx, bool dw, bool db) 
   const int64_t vec = 16 / int64_t(sh.elt);
   pl.pad_g = pl.N % vec != 0;
   pl.Np = pl.pad_g ? (pl.N + vec - 1) / vec * vec : pl.N;
-  const int64_t tiles = ((pl.N + 127) / 128) * ((pl.Kd + 127) / 128);
-  int64_t splits = (kPbWgTarget + tiles - 1) / tiles;
+  pl.tn = pl.N % 256 == 0 && pl.Kd % 256 == 0;
+  const int64_t tiles = pl.tn ? (pl.N / 256) * (pl.Kd / 256) : ((pl.N + 127) / 128) * ((pl.Kd + 127) / 128);
+  const int64_t target = pl.tn ? kPbWgTargetTn : kPbWgTarget;
+  // 128 x 128 tiles: at least the target; 256 x 256 tiles (one workgroup
+  // per CU): at most, so that the slices run in one round
+  int64_t splits = pl.tn ? std::max<int64_t>(1, target / tiles) : (target + tiles - 1) / tiles;
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, (pl.M + kPbTok - 1) / kPbTok));
   pl.ks = ((pl.M + splits - 1) / splits + kPbTok - 1) / kPbTok * kPbTok;
+  if (pl.tn) splits = std::max<int64_t>(1, (pl.M + pl.ks - 1) / pl.ks);   // no slice left empty
   pl.splits = int(splits);
   pl.Mp = pl.ks * splits;
   pl.n_rt = (pl.Mp + 63) / 64;
@@ -630,8 +637,10 @@ PlanPb plan_pb(const prn_params* p, const Shape& sh, bool dx, bool dw, bool db) 
     if (pl.pad_g) pl.gp_off = take(size_t(pl.M) * pl.Np * sh.elt);
   }
   if (pl.do_dw) {
-    pl.gt_off = take(size_t(pl.N) * pl.Mp * sh.elt);
-    pl.xt_off = take(size_t(pl.Kd) * pl.Mp * sh.elt);
+    if (!pl.tn) {
+      pl.gt_off = take(size_t(pl.N) * pl.Mp * sh.elt);
+      pl.xt_off = take(size_t(pl.Kd) * pl.Mp * sh.elt);
+    }
     pl.part_off = take(size_t(pl.splits) * pl.N * pl.Kd * 4);
   }
   if (pl.do_db) {
@@ -936,6 +945,9 @@ prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void
       misaligned(dW_out, sh.elt) || misaligned(dbias_out, 4))
     return fail(PRN_ERR_INVALID_ARG, "dxproj must be 16-byte aligned, the other tensors aligned to their element size");
   const PlanPb pl = plan_pb(p, sh, dx_out != nullptr, dW_out != nullptr, dbias_out != nullptr);
+  if (pl.do_dw && pl.tn && misaligned(x, 16))
+    return fail(PRN_ERR_INVALID_ARG, "x must be 16-byte aligned for the weight gradient when G*d_h and d_in are "
+                                     "multiples of 256");
   if (pl.total > 0) {
     if (!p->workspace || p->workspace_bytes < pl.total)
       return fail(PRN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", p->workspace_bytes,
@@ -974,7 +986,14 @@ prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void
     prn::launch_proj_ld(bf, g, pl.Np * elt, wt, pl.Np * elt, dx_out, M, Kd, pl.Np, st);
   }
   float* csum = pl.do_db ? reinterpret_cast<float*>(ws + pl.csum_off) : nullptr;
-  if (pl.do_dw) {
+  if (pl.do_dw && pl.tn) {
+    // dW (N x Kd) = dxproj^T x, split-K over tokens, read along the rows of
+    // both operands (no transposed copies); dbias from the same column sums
+    float* part = reinterpret_cast<float*>(ws + pl.part_off);
+    prn::launch_proj_tn(bf, dxproj, N * elt, x, Kd * elt, part, M, N, Kd, pl.ks, pl.splits, st);
+    prn::launch_splitk_sum(bf, part, pl.splits, N * Kd, dW_out, st);
+    if (pl.do_db) prn::launch_colsum64(bf, dxproj, M, N, pl.n_rt, csum, st);
+  } else if (pl.do_dw) {
     // dW (N x Kd) = dxproj^T x, split-K over tokens
     void* gt = ws + pl.gt_off;
     void* xt = ws + pl.xt_off;
@@ -983,6 +1002,8 @@ prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void
     prn::launch_transpose(bf, x, M, Kd, Kd, xt, pl.Mp, nullptr, st);
     prn::launch_proj_splitk(bf, gt, pl.Mp * elt, xt, pl.Mp * elt, part, N, Kd, pl.ks, pl.splits, st);
     prn::launch_splitk_sum(bf, part, pl.splits, N * Kd, dW_out, st);
+  } else if (pl.do_db && N % (16 / int64_t(elt)) == 0) {
+    prn::launch_colsum64(bf, dxproj, M, N, pl.n_rt, csum, st);
   } else if (pl.do_db) {
     prn::launch_transpose(bf, dxproj, M, N, N, nullptr, pl.Mp, csum, st);
   }

@@ -35,6 +35,15 @@ void launch_transpose(bool bf16, const void* in, int64_t R, int64_t C, int64_t l
                       float* csum, hipStream_t stream);
 // out (R x Cp) = in (R x C) with zero columns appended
 void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out, int64_t Cp, hipStream_t stream);
+// P[z][n][j] = sum over tokens t of slice z (tokens [z ks, min((z+1) ks, M)))
+// of A[t][n] B[t][j]: A tokens x N, B tokens x Kd, rows lda / ldb bytes
+// apart, both 16-byte aligned; N and Kd multiples of 256; fp32 sums,
+// unrounded (P: splits x N x Kd).  No transposed copies.
+void launch_proj_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M, int64_t N,
+                    int64_t Kd, int64_t ks, int splits, hipStream_t stream);
+// csum (n_rt x C) = column sums of every 64 rows of in (R x C, row-major,
+// zero past R), in row order; in 16-byte aligned, C a multiple of 16 bytes
+void launch_colsum64(bool bf16, const void* in, int64_t R, int64_t C, int64_t n_rt, float* csum, hipStream_t stream);
 // out[i] = sum_z P[z n + i] in z order, rounded once to the storage dtype
 void launch_splitk_sum(bool bf16, const float* P, int S, int64_t n, void* out, hipStream_t stream);
 

@@ -435,6 +435,184 @@ void launch_tiles(bool bf16, const void* A, const void* B, const float* bias, vo
   }
 }
 
+
+// Products whose reduction index runs along the operand rows, as in the
+// weight gradient dW = dxproj^T x:
+//   P[z][n][j] = sum over tokens t of slice z of A[t][n] B[t][j]
+// (A: tokens x N, B: tokens x Kd, row-major, rows lda / ldb bytes apart),
+// fp32 sums, unrounded; slice z = blockIdx.y covers tokens
+// [z ks, min((z + 1) ks, M)) (ks a multiple of the stage).  256 x 256
+// output tiles (N and Kd multiples of 256), 16 waves of 64 x 64 as in
+// k_proj.  A K stage is 16 tokens (fp32) or 32 (bf16): the
+// stage buffer holds, per token, the tile's 256 A values and 256 B values
+// (loaded straight into LDS, 1 KB of a row per wave load); the split into
+// bf16 term planes (bf16split.h; for bf16 storage the single plane is the
+// value itself) reads each plane row's 8 tokens down a column of the stage,
+// so the planes come out in the layout k_proj's planes have, with k = t,
+// and no transposed copy of either operand is ever made.  Stages and planes
+// are double buffered as in k_proj.
+template <bool BF16>
+__global__ void __launch_bounds__(1024)
+k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* __restrict__ P, int64_t M, int64_t N,
+          int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j) {
+  constexpr int BM = 256, BN = 256, NROWS = BM + BN, NW = 16, NTHR = 64 * NW, WC = 4, WM = 2, WN = 2;
+  constexpr int ELT = BF16 ? 2 : 4, NPL = BF16 ? 1 : 3, NTERM = BF16 ? 1 : 6;
+  // tokens per stage: 16 for fp32 (three planes), 32 for bf16 (one plane,
+  // and a stage's products would otherwise be too short next to its barrier)
+  constexpr int KS = BF16 ? 32 : 16;
+  constexpr int FROW = NROWS * ELT, FST = KS * FROW;  // a token's row of the stage; the stage
+  constexpr int PCH = KS / 8, PROW = 16 * PCH;        // 16-byte chunks (8 tokens) of a plane row
+  constexpr int PLANE = NROWS * PROW, PST = NPL * PLANE;
+  constexpr int NLD = FST / 1024, IPW = NLD / NW;     // 1 KB wave loads per stage; per wave
+  constexpr int UPT = NROWS * PCH / NTHR;             // plane chunks each thread fills per stage
+  static_assert(NLD % NW == 0 && IPW < 16 && NROWS * PCH % NTHR == 0, "stage geometry");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * FST + 2 * PST];
+  uint8_t* const Fb = lds;
+  uint8_t* const Pb = lds + 2 * FST;
+  // chunk c of plane row r: rows of 32 bytes change key every 8 rows, rows
+  // of 64 bytes every 4 (16 consecutive rows read at one chunk: all banks)
+  auto ppos = [](int r, int c) { return PCH == 2 ? c ^ ((r >> 3) & 1) : c ^ ((r >> 2) & 3); };
+
+  const int64_t z = blockIdx.y;
+  const int64_t t0 = z * ks, t1 = t0 + ks < M ? t0 + ks : M;
+  const int64_t bid = blockIdx.x;
+  const int64_t n0 = (bid / n_tiles_j) * BM, j0 = (bid % n_tiles_j) * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // wave load li = wave IPW + p fills stage bytes [1024 li, +1024): token
+  // row 1024 li / FROW of the stage, from byte 1024 li % FROW of that row
+  // (its A values first); lane l the 16 bytes at 16 l past that
+  const uint8_t* src[IPW];
+  int64_t ldr[IPW];
+  int trow[IPW];
+#pragma unroll
+  for (int p = 0; p < IPW; ++p) {
+    const int li = wave * IPW + p;
+    trow[p] = li * 1024 / FROW;
+    const int off = li * 1024 % FROW + 16 * lane;
+    const bool in_a = off < BM * ELT;
+    src[p] = in_a ? A + n0 * ELT + off : B + j0 * ELT + (off - BM * ELT);
+    ldr[p] = in_a ? lda : ldb;
+  }
+  auto issue = [&](int64_t kt, int buf) {
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int64_t t = t0 + kt * KS + trow[p];
+      const void* g = t < t1 ? static_cast<const void*>(src[p] + t * ldr[p]) : static_cast<const void*>(kZeroChunk);
+      dma16(g, lds_addr(Fb + buf * FST + (wave * IPW + p) * 1024));
+    }
+  };
+  // unit v: plane row r (A rows, then B rows), tokens 8 kc .. 8 kc + 7 of the stage
+  auto split_unit = [&](int buf, int v) {
+    const int r = v & (NROWS - 1), kc = v / NROWS;
+    const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
+    uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, kc);
+    if constexpr (BF16) {
+      typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(f + 2 * q * FROW)) |
+               (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(f + (2 * q + 1) * FROW)) << 16);
+      *reinterpret_cast<u32x4*>(d) = v;
+    } else {
+      f32x4 va, vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        va[e] = *reinterpret_cast<const float*>(f + e * FROW);
+        vb[e] = *reinterpret_cast<const float*>(f + (4 + e) * FROW);
+      }
+      bf16x8 h0, h1, h2;
+      split3(va, vb, h0, h1, h2);
+      *reinterpret_cast<bf16x8*>(d) = h0;
+      *reinterpret_cast<bf16x8*>(d + PLANE) = h1;
+      *reinterpret_cast<bf16x8*>(d + 2 * PLANE) = h2;
+    }
+  };
+  auto split_stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < UPT; ++q) split_unit(buf, tid + q * NTHR);
+  };
+
+  f32x16 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int64_t nk = (ks + KS - 1) / KS;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  asm volatile("" ::: "memory");
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt((IPW & 15) | (7 << 4) | (15 << 8));   // vmcnt(IPW): stage 0 has landed
+  else
+    __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  split_stage(0);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // the planes of stage kt are complete and stage kt + 1 has landed;
+    // every wave is done with the planes of stage kt - 1 and the stage
+    // buffer of stage kt
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2, cur);
+    if (kt + 1 < nk) split_stage(cur ^ 1);
+    const uint8_t* Pl = Pb + cur * PST;
+#pragma unroll
+    for (int ks2 = 0; ks2 < KS / 16; ++ks2) {
+      // 16 tokens per step: half h takes plane chunk 2 ks2 + h
+      const int c = 2 * ks2 + half;
+      bf16x8 bp[WN][NPL];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int r = BM + wc * WN * 32 + j * 32 + l32;
+#pragma unroll
+        for (int u = 0; u < NPL; ++u)
+          bp[j][u] = *reinterpret_cast<const bf16x8*>(Pl + u * PLANE + r * PROW + 16 * ppos(r, c));
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const int r = wr * WM * 32 + i * 32 + l32;
+        bf16x8 ap[NPL];
+#pragma unroll
+        for (int u = 0; u < NPL; ++u)
+          ap[u] = *reinterpret_cast<const bf16x8*>(Pl + u * PLANE + r * PROW + 16 * ppos(r, c));
+#pragma unroll
+        for (int t = 0; t < NTERM; ++t)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane l, accumulator r of block (i, j): row n0 + .. + 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  float* Pz = P + z * N * Kd;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int64_t gj = j0 + wc * WN * 32 + j * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t gn = n0 + wr * WM * 32 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        Pz[gn * Kd + gj] = acc[i][j][r];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 void launch_proj(bool bf16, const void* A, const void* B, const float* bias, void* C, int64_t M, int64_t N,
@@ -522,6 +700,33 @@ __global__ void __launch_bounds__(256) k_pad_rows(const typename Elt<BF16>::T* _
   out[i] = c < C ? in[r * C + c] : Elt<BF16>::st(0.0f);
 }
 
+// csum[rt * C + c] = the sum of in[r][c] over the rows r = 64 rt ..
+// 64 rt + 63 (0 at r >= R), in row order: the column sums k_transpose takes.
+// A thread sums the 16 bytes of columns at c0 .. (C a multiple of those, in
+// 16-byte aligned rows), so every load is a whole 16-byte chunk.
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_colsum64(const typename Elt<BF16>::T* __restrict__ in, int64_t R, int64_t C,
+                                                  float* __restrict__ csum) {
+  constexpr int V = 16 / sizeof(typename Elt<BF16>::T);
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x) * V, r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  if (c0 >= C) return;
+  float sum[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) sum[e] = 0.0f;
+  // the rows past R add zeros, which leave a sum that started at +0 unchanged
+  const int n = static_cast<int>(R - r0 < 64 ? R - r0 : 64);
+  const typename Elt<BF16>::T* src = in + r0 * C + c0;
+  for (int i = 0; i < n; ++i, src += C) {
+    const uint4 q = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+      sum[e] += BF16 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16)) : __uint_as_float(w[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) csum[static_cast<int64_t>(blockIdx.x) * C + c0 + e] = sum[e];
+}
+
 // out[i] = the sum over z = 0 .. S-1, in that order, of P[z * n + i],
 // rounded once to the storage dtype
 template <bool BF16>
@@ -553,6 +758,27 @@ void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out,
     k_pad_rows<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(in), R, C, static_cast<uint16_t*>(out), Cp);
   else
     k_pad_rows<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(in), R, C, static_cast<float*>(out), Cp);
+}
+
+void launch_proj_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M, int64_t N,
+                    int64_t Kd, int64_t ks, int splits, hipStream_t stream) {
+  const int tj = static_cast<int>(Kd / 256);
+  const dim3 grid(static_cast<unsigned>((N / 256) * tj), static_cast<unsigned>(splits));
+  if (bf16)
+    k_proj_tn<true><<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N,
+                                               Kd, lda, ldb, ks, tj);
+  else
+    k_proj_tn<false><<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M,
+                                                N, Kd, lda, ldb, ks, tj);
+}
+
+void launch_colsum64(bool bf16, const void* in, int64_t R, int64_t C, int64_t n_rt, float* csum, hipStream_t stream) {
+  const int64_t v = bf16 ? 8 : 4;
+  const dim3 grid(static_cast<unsigned>(n_rt), static_cast<unsigned>((C / v + 255) / 256));
+  if (bf16)
+    k_colsum64<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(in), R, C, csum);
+  else
+    k_colsum64<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(in), R, C, csum);
 }
 
 void launch_splitk_sum(bool bf16, const float* P, int S, int64_t n, void* out, hipStream_t stream) {

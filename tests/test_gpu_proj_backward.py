@@ -8,8 +8,11 @@ floating-point summation errors are measured against):
   bf16 storage: |got - ref| <= 2^-8 |ref| + 2e-5 ref_abs  (one rounding of the
                 result to 8 significant bits, fp32 accumulation)
 Shapes cover ragged tiles, rows of dxproj that are not whole 16-byte chunks
-(the padded-copy path), a misaligned dxproj (rejected), T = 0, optional outputs, and
-the long LSTM workload at full size on sampled entries."""
+(the padded-copy path), the weight gradient read along the operand rows
+(G d_h and d_in multiples of 256) and through transposed copies, a
+misaligned dxproj (rejected) and a misaligned x where the rows are read
+directly (rejected), T = 0, optional outputs, and the long LSTM workload at
+full size on sampled entries."""
 import numpy as np
 import pytest
 import torch
@@ -60,7 +63,9 @@ CASES = [
     ("lstm", "bf16", 2, 300, 40, 130),
     ("gru", "bf16", 1, 513, 24, 42),    # rows of 252 bytes: padded copy
     ("lstm", "f32", 1, 1, 4, 16),
-    ("gru", "f32", 4, 2048, 256, 256),
+    ("gru", "f32", 4, 2048, 256, 256),  # G d_h and d_in multiples of 256: dW along the rows, no transposes
+    ("gru", "f32", 1, 1234, 512, 256),  # the same with a ragged last slice of tokens
+    ("lstm", "bf16", 2, 1500, 256, 128),
 ]
 
 
@@ -93,6 +98,15 @@ def test_projection_backward_optional_outputs_misaligned_input_and_empty():
     dxm = buf[1:].view(dxp.shape)
     with pytest.raises(B.PrnError, match="16-byte"):
         _run(cell, dxm, x, W)
+    # x not 16-byte aligned where dW reads the operand rows directly (G d_h, d_in multiples of 256): rejected
+    dxq, xq, Wq = _inputs("gru", dtype, 1, 300, 256, 256, seed=4)
+    xbuf = torch.empty(xq.numel() + 1, device="cuda")
+    xm = xbuf[1:].view(xq.shape)
+    xm.copy_(xq)
+    with pytest.raises(B.PrnError, match="16-byte"):
+        _run("gru", dxq, xm, Wq)
+    dxo, _, _ = _run("gru", dxq, xm, Wq, dW=False)   # dx and dbias alone do not read x
+    assert torch.equal(dxo, _run("gru", dxq, xq, Wq, dW=False)[0])
     # T = 0: dW = 0, dbias = 0, dx empty
     e = _run(cell, dxp[:, :0].contiguous(), x[:, :0].contiguous(), W)
     assert e[0].numel() == 0 and float(e[1].abs().max()) == 0.0 and float(e[2].abs().max()) == 0.0
