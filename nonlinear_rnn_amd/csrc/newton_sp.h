@@ -443,7 +443,12 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   };
   residual_put(rmax);
 
-  for (int k = 0; k < K; ++k) {
+  // iteration k; the last one (LAST) is a separate copy after the loop, so
+  // that the maps the loop carries keep one register assignment (with the
+  // last iteration inside the loop, the compiler copied all LS maps at both
+  // ends of the loop body)
+  auto iteration = [&](int k, auto last_t) __attribute__((always_inline)) {
+    constexpr bool last = decltype(last_t)::value;
     const int pb = k & 1;
     part[pb][w][lane] = acc;
     __syncthreads();
@@ -474,7 +479,6 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       rec_publish(rec.status + (static_cast<int64_t>(k) * n_chains + chain) * n_ch + chunk, kRecPrefix, lane);
 
     // ---- fix-up of iteration k+1, linearisation of iteration k+2 ----
-    const bool last = (k == K - 1);
     // The output addresses are formed at the stores: an opaque copy of the
     // bases per iteration keeps the compiler from hoisting LS 64-bit
     // addresses out of the iteration loop, which would hold their registers
@@ -496,7 +500,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
 #pragma unroll
     for (int q = 0; q < S; ++q) pr[q] = ST::round(s[q]);
     if (fast) {
-      if (!last) {
+      if constexpr (!last) {
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
           apply(ms[j], s);
@@ -555,7 +559,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
           }
           float fv[S], xj[G];
           xs_get(j, xj);
-          if (!last) {
+          if constexpr (!last) {
             ms[j] = C::fj(xj, p, cf.as, cf.a, head, fv);
             acc = compose(ms[j], acc);
           } else {
@@ -582,7 +586,9 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
       }
     }
     residual_put(rmax);
-  }
+  };
+  for (int k = 0; k < K - 1; ++k) iteration(k, std::false_type{});
+  iteration(K - 1, std::true_type{});
   __syncthreads();
   residual_finish(K);
 }
