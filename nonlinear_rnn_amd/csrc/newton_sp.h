@@ -191,11 +191,11 @@ __device__ __forceinline__ void lookback_carry(const SpRecords& rec, int64_t bas
 // which a short unroll over the p - 1 steps before it (from xproj, or from
 // h0 at the segment's head) supplies.
 // Waves per SIMD the compiler must leave room for: two for the longest
-// chunk (LS = 16, fp32 LSTM), whose register need otherwise lands a few
-// registers above 256 (the states_out instance: 264, 20 bytes of spills under
-// the cap) and halves the resident waves; no constraint otherwise.
-// The fused-projection instances (FX) hold the projection's accumulators on
-// top of the Newton state and are capped the same way.
+// chunk (LS = 16, fp32 LSTM: 205 registers, 207 with states_out; a bound
+// that only matters if a change pushes it past 256, where one wave per SIMD
+// would halve the resident waves); no constraint otherwise.  The
+// fused-projection instances (FX) hold the projection's accumulators on top
+// of the Newton state and are capped the same way.
 template <class C, int DT, int LS, bool FX>
 constexpr int sp_min_waves() {
   return (FX || (C::S == 2 && DT == kF32 && LS >= 16)) ? 2 : 1;

@@ -464,8 +464,8 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
   constexpr int PCH = KS / 8, PROW = 16 * PCH;        // 16-byte chunks (8 tokens) of a plane row
   constexpr int PLANE = NROWS * PROW, PST = NPL * PLANE;
   constexpr int NLD = FST / 1024, IPW = NLD / NW;     // 1 KB wave loads per stage; per wave
-  constexpr int UPT = NROWS * PCH / NTHR;             // plane chunks each thread fills per stage
-  static_assert(NLD % NW == 0 && IPW < 16 && NROWS * PCH % NTHR == 0, "stage geometry");
+  constexpr int UPT = NROWS * PCH / (BF16 ? 2 : 1) / NTHR;   // split units of each thread per stage
+  static_assert(NLD % NW == 0 && IPW < 16 && NROWS * PCH % (NTHR * (BF16 ? 2 : 1)) == 0, "stage geometry");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * FST + 2 * PST];
   uint8_t* const Fb = lds;
   uint8_t* const Pb = lds + 2 * FST;
@@ -505,20 +505,29 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
       dma16(g, lds_addr(Fb + buf * FST + (wave * IPW + p) * 1024));
     }
   };
-  // unit v: plane row r (A rows, then B rows), tokens 8 kc .. 8 kc + 7 of the stage
+  // unit v: plane row r (A rows, then B rows), tokens 8 kc .. 8 kc + 7 of
+  // the stage; for bf16 storage the unit is the pair of plane rows r, r + 1
+  // (r even), read as the 32-bit words that hold both values of a token
   auto split_unit = [&](int buf, int v) {
-    const int r = v & (NROWS - 1), kc = v / NROWS;
-    const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
-    uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, kc);
     if constexpr (BF16) {
       typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-      u32x4 v;
+      const int r = 2 * (v & (NROWS / 2 - 1)), kc = v / (NROWS / 2);
+      const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
+      uint32_t wv[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(f + 2 * q * FROW)) |
-               (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(f + (2 * q + 1) * FROW)) << 16);
-      *reinterpret_cast<u32x4*>(d) = v;
+      for (int e = 0; e < 8; ++e) wv[e] = *reinterpret_cast<const uint32_t*>(f + e * FROW);
+      u32x4 lo, hi;   // the values of row r (low halves), of row r + 1 (high halves)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = __builtin_amdgcn_perm(wv[2 * q + 1], wv[2 * q], 0x05040100u);
+        hi[q] = __builtin_amdgcn_perm(wv[2 * q + 1], wv[2 * q], 0x07060302u);
+      }
+      *reinterpret_cast<u32x4*>(Pb + buf * PST + r * PROW + 16 * ppos(r, kc)) = lo;
+      *reinterpret_cast<u32x4*>(Pb + buf * PST + (r + 1) * PROW + 16 * ppos(r + 1, kc)) = hi;
     } else {
+      const int r = v & (NROWS - 1), kc = v / NROWS;
+      const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
+      uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, kc);
       f32x4 va, vb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
