@@ -443,35 +443,30 @@ void launch_tiles(bool bf16, const void* A, const void* B, const float* bias, vo
 // fp32 sums, unrounded; slice z = blockIdx.y covers tokens
 // [z ks, min((z + 1) ks, M)) (ks a multiple of the stage).  256 x 256
 // output tiles (N and Kd multiples of 256), 16 waves of 64 x 64 as in
-// k_proj.  A K stage is 16 tokens (fp32) or 32 (bf16): the
-// stage buffer holds, per token, the tile's 256 A values and 256 B values
-// (loaded straight into LDS, 1 KB of a row per wave load); the split into
-// bf16 term planes (bf16split.h; for bf16 storage the single plane is the
-// value itself) reads each plane row's 8 tokens down a column of the stage,
-// so the planes come out in the layout k_proj's planes have, with k = t,
-// and no transposed copy of either operand is ever made.  Stages and planes
-// are double buffered as in k_proj.
-template <bool BF16>
+// k_proj.  fp32 operands (bf16 ones: k_proj_tn_tr).  A K stage is 16
+// tokens: the stage buffer holds, per token, the tile's 256 A values and
+// 256 B values (loaded straight into LDS, 1 KB of a row per wave load); the
+// split into bf16 term planes (bf16split.h) reads each plane row's 8 tokens
+// down a column of the stage, so the planes come out in the layout k_proj's
+// planes have, with k = t, and no transposed copy of either operand is ever
+// made.  Stages and planes are double buffered as in k_proj.
 __global__ void __launch_bounds__(1024)
 k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* __restrict__ P, int64_t M, int64_t N,
           int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j) {
   constexpr int BM = 256, BN = 256, NROWS = BM + BN, NW = 16, NTHR = 64 * NW, WC = 4, WM = 2, WN = 2;
-  constexpr int ELT = BF16 ? 2 : 4, NPL = BF16 ? 1 : 3, NTERM = BF16 ? 1 : 6;
-  // tokens per stage: 16 for fp32 (three planes), 32 for bf16 (one plane,
-  // and a stage's products would otherwise be too short next to its barrier)
-  constexpr int KS = BF16 ? 32 : 16;
+  constexpr int ELT = 4, NPL = 3, NTERM = 6, KS = 16;
   constexpr int FROW = NROWS * ELT, FST = KS * FROW;  // a token's row of the stage; the stage
   constexpr int PCH = KS / 8, PROW = 16 * PCH;        // 16-byte chunks (8 tokens) of a plane row
   constexpr int PLANE = NROWS * PROW, PST = NPL * PLANE;
   constexpr int NLD = FST / 1024, IPW = NLD / NW;     // 1 KB wave loads per stage; per wave
-  constexpr int UPT = NROWS * PCH / (BF16 ? 2 : 1) / NTHR;   // split units of each thread per stage
-  static_assert(NLD % NW == 0 && IPW < 16 && NROWS * PCH % (NTHR * (BF16 ? 2 : 1)) == 0, "stage geometry");
+  constexpr int UPT = NROWS * PCH / NTHR;             // split units of each thread per stage
+  static_assert(NLD % NW == 0 && IPW < 16 && NROWS * PCH % NTHR == 0, "stage geometry");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * FST + 2 * PST];
   uint8_t* const Fb = lds;
   uint8_t* const Pb = lds + 2 * FST;
-  // chunk c of plane row r: rows of 32 bytes change key every 8 rows, rows
-  // of 64 bytes every 4 (16 consecutive rows read at one chunk: all banks)
-  auto ppos = [](int r, int c) { return PCH == 2 ? c ^ ((r >> 3) & 1) : c ^ ((r >> 2) & 3); };
+  // chunk c of plane row r (rows of 32 bytes) changes key every 8 rows (16
+  // consecutive rows read at one chunk: all banks)
+  auto ppos = [](int r, int c) { return c ^ ((r >> 3) & 1); };
 
   const int64_t z = blockIdx.y;
   const int64_t t0 = z * ks, t1 = t0 + ks < M ? t0 + ks : M;
@@ -505,41 +500,22 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
       dma16(g, lds_addr(Fb + buf * FST + (wave * IPW + p) * 1024));
     }
   };
-  // unit v: plane row r (A rows, then B rows), tokens 8 kc .. 8 kc + 7 of
-  // the stage; for bf16 storage the unit is the pair of plane rows r, r + 1
-  // (r even), read as the 32-bit words that hold both values of a token
+  // unit v: plane row r (A rows, then B rows), tokens 8 kc .. 8 kc + 7 of the stage
   auto split_unit = [&](int buf, int v) {
-    if constexpr (BF16) {
-      typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-      const int r = 2 * (v & (NROWS / 2 - 1)), kc = v / (NROWS / 2);
-      const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
-      uint32_t wv[8];
+    const int r = v & (NROWS - 1), kc = v / NROWS;
+    const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
+    uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, kc);
+    f32x4 va, vb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wv[e] = *reinterpret_cast<const uint32_t*>(f + e * FROW);
-      u32x4 lo, hi;   // the values of row r (low halves), of row r + 1 (high halves)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lo[q] = __builtin_amdgcn_perm(wv[2 * q + 1], wv[2 * q], 0x05040100u);
-        hi[q] = __builtin_amdgcn_perm(wv[2 * q + 1], wv[2 * q], 0x07060302u);
-      }
-      *reinterpret_cast<u32x4*>(Pb + buf * PST + r * PROW + 16 * ppos(r, kc)) = lo;
-      *reinterpret_cast<u32x4*>(Pb + buf * PST + (r + 1) * PROW + 16 * ppos(r + 1, kc)) = hi;
-    } else {
-      const int r = v & (NROWS - 1), kc = v / NROWS;
-      const uint8_t* f = Fb + buf * FST + 8 * kc * FROW + r * ELT;
-      uint8_t* d = Pb + buf * PST + r * PROW + 16 * ppos(r, kc);
-      f32x4 va, vb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        va[e] = *reinterpret_cast<const float*>(f + e * FROW);
-        vb[e] = *reinterpret_cast<const float*>(f + (4 + e) * FROW);
-      }
-      bf16x8 h0, h1, h2;
-      split3(va, vb, h0, h1, h2);
-      *reinterpret_cast<bf16x8*>(d) = h0;
-      *reinterpret_cast<bf16x8*>(d + PLANE) = h1;
-      *reinterpret_cast<bf16x8*>(d + 2 * PLANE) = h2;
+    for (int e = 0; e < 4; ++e) {
+      va[e] = *reinterpret_cast<const float*>(f + e * FROW);
+      vb[e] = *reinterpret_cast<const float*>(f + (4 + e) * FROW);
     }
+    bf16x8 h0, h1, h2;
+    split3(va, vb, h0, h1, h2);
+    *reinterpret_cast<bf16x8*>(d) = h0;
+    *reinterpret_cast<bf16x8*>(d + PLANE) = h1;
+    *reinterpret_cast<bf16x8*>(d + 2 * PLANE) = h2;
   };
   auto split_stage = [&](int buf) {
 #pragma unroll
@@ -709,6 +685,135 @@ __global__ void __launch_bounds__(256) k_pad_rows(const typename Elt<BF16>::T* _
   out[i] = c < C ? in[r * C + c] : Elt<BF16>::st(0.0f);
 }
 
+// The bf16 weight-gradient tile (P as in k_proj_tn, bf16 operands) without a
+// repack: the stage keeps the tokens as rows, as loaded, and the operand
+// fragments come straight from it through ds_read_b64_tr_b16.  That
+// instruction treats each 16 lanes as a group: lane j of the group names an
+// 8-byte run (four 16-bit values) and lane i receives value i % 4 of the
+// runs named by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4, in that order
+// (checked by an in-bounds probe).  So if lane j names token row
+// t0 + j / 4, columns c0 + 4 (j % 4) .. + 3, lane i receives tokens
+// t0 .. t0 + 3 of column c0 + i: four consecutive k of one row of the
+// operand, half of what a lane holds for a 32 x 32 x 16 product.  The
+// fragments hold the same k in the same places as the planes of k_proj_tn,
+// so the sums are bitwise the same.  Three 32-token stages (one being read,
+// two in flight).  Within a token row the 16-byte chunk c sits at c ^
+// swz(t), so the eight rows one transposed read touches (t0 + 0..3 and
+// t0 + 8..11) fall into eight different 64-byte segments.
+__global__ void __launch_bounds__(1024)
+k_proj_tn_tr(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* __restrict__ P, int64_t M,
+             int64_t N, int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j) {
+  constexpr int BM = 256, BN = 256, NROWS = BM + BN, NW = 16, WC = 4, WM = 2, WN = 2;
+  constexpr int KS = 32, FROW = NROWS * 2, FST = KS * FROW, NBUF = 3;
+  constexpr int NLD = FST / 1024, IPW = NLD / NW;   // a wave load fills one token row (1 KB)
+  static_assert(FROW == 1024 && NLD % NW == 0 && IPW < 16, "stage geometry");
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * FST];
+  auto swz = [](int t) { return 4 * ((t & 3) | (((t >> 3) & 1) << 2)); };
+
+  const int64_t z = blockIdx.y;
+  const int64_t t0 = z * ks, t1 = t0 + ks < M ? t0 + ks : M;
+  const int64_t bid = blockIdx.x;
+  const int64_t n0 = (bid / n_tiles_j) * BM, j0 = (bid % n_tiles_j) * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // wave load li = wave IPW + p fills token row li of the stage: lane l the
+  // 16 bytes at position l, i.e. chunk l ^ swz(li) of the row (chunks 0..31:
+  // the A columns n0 .., 32..63: the B columns j0 ..)
+  const uint8_t* src[IPW];
+  int64_t ldr[IPW];
+#pragma unroll
+  for (int p = 0; p < IPW; ++p) {
+    const int li = wave * IPW + p, c = lane ^ swz(li);
+    src[p] = c < 32 ? A + n0 * 2 + 16 * c : B + j0 * 2 + 16 * (c - 32);
+    ldr[p] = c < 32 ? lda : ldb;
+  }
+  auto issue = [&](int64_t kt, int buf) {
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int li = wave * IPW + p;
+      const int64_t t = t0 + kt * KS + li;
+      const void* g = t < t1 ? static_cast<const void*>(src[p] + t * ldr[p]) : static_cast<const void*>(kZeroChunk);
+      dma16(g, lds_addr(lds + buf * FST + li * 1024));
+    }
+  };
+  // this lane's part of a transposed read: group g = lane / 16 takes columns
+  // c0 + 16 (g % 2) .. + 15 and tokens 8 (g / 2) .. + 7 of the 16-token step
+  const int grp = lane >> 4, jl = lane & 15;
+  const int rsub = 8 * (grp >> 1) + (jl >> 2);          // token row within the step, before + 4 call
+  const int csub = 16 * (grp & 1) + 4 * (jl & 3);       // column offset within the 32-column block
+  auto frag = [&](const uint8_t* st, int step, int c0) {
+    s16x8 v;
+#pragma unroll
+    for (int call = 0; call < 2; ++call) {
+      const int t = 16 * step + rsub + 4 * call, col = c0 + csub;
+      const uint8_t* a = st + t * FROW + 16 * ((col >> 3) ^ swz(t)) + 2 * (col & 7);
+      const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(a));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * call + e] = r[e];
+    }
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int64_t nk = (ks + KS - 1) / KS;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = static_cast<int>(kt % NBUF);
+    // stage kt has landed (stage kt + 1 may still be in flight); every wave
+    // is done with the buffer of stage kt - 1, which stage kt + 2 refills
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk)
+      __builtin_amdgcn_s_waitcnt((IPW & 15) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2, static_cast<int>((kt + 2) % NBUF));
+    const uint8_t* st = lds + cur * FST;
+#pragma unroll
+    for (int step = 0; step < KS / 16; ++step) {
+      bf16x8 bp[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) bp[j] = frag(st, step, BM + wc * WN * 32 + j * 32);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const bf16x8 ap = frag(st, step, wr * WM * 32 + i * 32);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bp[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane l, accumulator r of block (i, j): row n0 + .. + 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  float* Pz = P + z * N * Kd;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int64_t gj = j0 + wc * WN * 32 + j * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t gn = n0 + wr * WM * 32 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        Pz[gn * Kd + gj] = acc[i][j][r];
+      }
+    }
+  }
+}
+
 // csum[rt * C + c] = the sum of in[r][c] over the rows r = 64 rt ..
 // 64 rt + 63 (0 at r >= R), in row order: the column sums k_transpose takes.
 // A thread sums the 16 bytes of columns at c0 .. (C a multiple of those, in
@@ -774,11 +879,11 @@ void launch_proj_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_
   const int tj = static_cast<int>(Kd / 256);
   const dim3 grid(static_cast<unsigned>((N / 256) * tj), static_cast<unsigned>(splits));
   if (bf16)
-    k_proj_tn<true><<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N,
-                                               Kd, lda, ldb, ks, tj);
+    k_proj_tn_tr<<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N, Kd,
+                                            lda, ldb, ks, tj);
   else
-    k_proj_tn<false><<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M,
-                                                N, Kd, lda, ldb, ks, tj);
+    k_proj_tn<<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N, Kd,
+                                         lda, ldb, ks, tj);
 }
 
 void launch_colsum64(bool bf16, const void* in, int64_t R, int64_t C, int64_t n_rt, float* csum, hipStream_t stream) {
