@@ -44,7 +44,7 @@ constexpr int kLS = 8;
 constexpr int kNW = 8;
 constexpr int kLC = kLS * kNW;
 constexpr int kScanSeg = 16;
-// single-pass geometry (lane = channel, NW = 4 waves of LS serial steps).
+// single-pass geometry (lane = channel, NW waves of LS serial steps).
 // Longer chunks mean fewer carry look-backs per step, which is what bounds
 // the kernel when few chains (rows x 64-channel tiles) run side by side:
 // every chunk of a chain waits on the look-back of the chunks before it.
@@ -61,7 +61,16 @@ constexpr int kScanSeg = 16;
 // chains: 0.96 -> 0.91 ms; LS = 16 took 1.05 ms there).  With few chains the
 // four-wave 64-step chunk also beat the other shapes tried on the 4-chain
 // ragged pack (LS x NW = 16 x 4: 0.24 ms; 12 x 4: 0.27; 16 x 3: 0.27;
-// 8 x 4: 0.32; 24 x 2: 0.31; 16 x 2: 0.34).
+// 8 x 4: 0.32; 24 x 2: 0.31; 16 x 2: 0.34).  Once the last iteration was
+// peeled out of the iteration loop (fp32 GRU at LS = 16: 168 -> 96
+// registers), eight waves of 10 steps (80-step chunks, 69 KB of LDS, two
+// workgroups per CU) beat it (MALL flushed; 32-chain GRU 8 x 4096 x 256 /
+// 4-chain ragged pack): 16 x 4 0.105 / 0.255 ms; 10 x 8 0.099 / 0.220;
+// 9 x 8 0.100 / 0.227; 8 x 8 0.098 / 0.236; 6 x 8 0.098 / 0.244; 4 x 16
+// 0.127 / 0.290; 12 x 8 0.118 / 0.285; 10 x 6 0.108 / 0.264.  Eight waves
+// lost where the chains are many or the state is wider: bf16 GRU at 128
+// chains 8 x 8 0.978 and 5 x 8 0.953 ms against 0.836 at 10 x 4; the long
+// LSTM 8 x 8 0.909 against 0.678 at 16 x 4.
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
 // keeps LS = 8 (LS = 12 already needs 256 registers, LS = 16 spills); the
 // bf16 GRU with many chains takes LS = 10, the longest chunk that keeps four
@@ -69,16 +78,18 @@ constexpr int kScanSeg = 16;
 // 512: LS = 8 / 10 took 1.06 / 0.97 ms.
 constexpr int kSpNW = 4;
 constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
-constexpr int kSpLsGruFew = 16, kSpNwGruFew = 4;   // GRU below kSpManyChains chains
+constexpr int kSpNwLstm = 4, kSpNwLstmBf16 = 4, kSpNwGruMany = 4, kSpNwGruManyBf16 = 4;
+constexpr int kSpLsGruFew = 10, kSpNwGruFew = 8;   // GRU below kSpManyChains chains
 constexpr int kSpLsFusedGru = 16, kSpLsFusedLstm = 16;
 constexpr int64_t kSpManyChains = 64;
 struct SpGeo {
   int ls, nw;   // steps per wave, waves per workgroup
 };
 SpGeo sp_geo(int cell, int dtype, int64_t n_chains) {
-  if (cell != PRN_CELL_DIAG_GRU) return {dtype == PRN_BF16 ? kSpLsLstmBf16 : kSpLsLstm, kSpNW};
+  if (cell != PRN_CELL_DIAG_GRU)
+    return dtype == PRN_BF16 ? SpGeo{kSpLsLstmBf16, kSpNwLstmBf16} : SpGeo{kSpLsLstm, kSpNwLstm};
   if (n_chains < kSpManyChains) return {kSpLsGruFew, kSpNwGruFew};
-  return {dtype == PRN_BF16 ? kSpLsGruManyBf16 : kSpLsGruMany, kSpNW};
+  return dtype == PRN_BF16 ? SpGeo{kSpLsGruManyBf16, kSpNwGruManyBf16} : SpGeo{kSpLsGruMany, kSpNwGruMany};
 }
 // With the projection fused into the Newton kernel, a chunk must be a
 // multiple of 32 steps (the projection's 32-row blocks), and longer chunks
@@ -88,7 +99,7 @@ SpGeo sp_geo(int cell, int dtype, int64_t n_chains) {
 SpGeo sp_geo_fused(int cell, int dtype, int64_t n_chains) {
   if (cell == PRN_CELL_DIAG_GRU) return {kSpLsFusedGru, kSpNW};
   if (dtype == PRN_F32) return {kSpLsFusedLstm, kSpNW};
-  return sp_geo(cell, dtype, n_chains);
+  return {kSpLsLstmBf16, kSpNW};
 }
 constexpr unsigned kSpinLimit = 1u << 16;   // polls (~1 us each) of one look-back wait before giving up
 // PRN_SPIN_LIMIT overrides the poll limit at every call; 0 makes every
@@ -418,16 +429,16 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
       }
     } else if constexpr (S == 2) {
       if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsLstmBf16>{}, NW4{}, F_{});
+        launch(std::integral_constant<int, kSpLsLstmBf16>{}, std::integral_constant<int, kSpNwLstmBf16>{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsLstm>{}, NW4{}, F_{});
+        launch(std::integral_constant<int, kSpLsLstm>{}, std::integral_constant<int, kSpNwLstm>{}, F_{});
     } else {
       if (pl.n_chains < kSpManyChains)
         launch(std::integral_constant<int, kSpLsGruFew>{}, std::integral_constant<int, kSpNwGruFew>{}, F_{});
       else if constexpr (DT == prn::kBF16)
-        launch(std::integral_constant<int, kSpLsGruManyBf16>{}, NW4{}, F_{});
+        launch(std::integral_constant<int, kSpLsGruManyBf16>{}, std::integral_constant<int, kSpNwGruManyBf16>{}, F_{});
       else
-        launch(std::integral_constant<int, kSpLsGruMany>{}, NW4{}, F_{});
+        launch(std::integral_constant<int, kSpLsGruMany>{}, std::integral_constant<int, kSpNwGruMany>{}, F_{});
     }
     if (res) prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, res);
   } else {

@@ -42,9 +42,11 @@ IDS = [w.name for w in CASES]
 
 
 def same_chunking(w) -> bool:
-    """Do the fused and two-call forwards take the same chunk length?  The
-    unfused GRU shortens its chunks from 64 (row, 64-channel) chains on."""
-    return w.cell == "lstm" or w.B * -(-w.d_h // 64) < 64
+    """Do the fused and two-call forwards take the same chunks?  Only the
+    LSTM: the fused GRU takes 64-step chunks of four waves, the unfused one
+    80-step chunks of eight waves below 64 (row, 64-channel) chains and 48-
+    or 40-step chunks from 64 on."""
+    return w.cell == "lstm"
 
 
 def lim_rr(w):
@@ -198,7 +200,7 @@ def test_fused_full_size_sampled_parity(name):
     ref = oracle_newton(w, xp, inp["a"][:, chans], w.K, cu=inp["cu_seqlens"])
     err = np.abs(to_f64(out["H"][rows][:, :, chans]) - ref["H"][..., -1, :]).max()
     say(f"  {name}: max|fused - two-call| {d:.3e}; sampled max|H - oracle| {err:.3e}; residuals {out['res']}")
-    if w.cell == "lstm" or w.B * -(-w.d_h // 64) < 64:   # same chunking: the same bits
+    if same_chunking(w):   # the same chunks: the same bits
         assert d == 0
     else:
         assert state_err(w, out["H"].float().cpu(), two["H"].float().cpu(), 1e-5) <= 1
@@ -268,5 +270,9 @@ def test_fused_states_out_matches_two_call_trajectory(cell, dtype):
             B.prn_newton_forward(xp, a, 3, H, cell=cell, h0=h0, cu_seqlens=cu_d, states_out=st, workspace=ws)
         torch.cuda.synchronize()
         outs.append((H, st))
-    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][0], outs[1][0])   # same chunking
+    if same_chunking(w):   # the same chunks: the same bits
+        assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][0], outs[1][0])
+    else:
+        assert (outs[0][1].float() - outs[1][1].float()).abs().max().item() <= lim_rr(w)
+        assert (outs[0][0].float() - outs[1][0].float()).abs().max().item() <= lim_rr(w)
     assert torch.equal(outs[1][1][..., w.S - 1, :], outs[1][0])   # h part of the states is H_out
