@@ -81,6 +81,10 @@ constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruMany
 constexpr int kSpNwLstm = 4, kSpNwLstmBf16 = 4, kSpNwGruMany = 4, kSpNwGruManyBf16 = 4;
 constexpr int kSpLsGruFew = 10, kSpNwGruFew = 8;   // GRU below kSpManyChains chains
 constexpr int kSpLsFusedGru = 16, kSpLsFusedLstm = 16;
+// fused GRU below kSpManyChains chains: eight waves lost there (MALL flushed,
+// 32-chain GRU / 4-chain ragged pack: 16 x 4 0.189 / 0.343 ms, 8 x 8 0.205 /
+// 0.407, 4 x 8 0.227 / 0.508)
+constexpr int kSpLsFusedGruFew = 16, kSpNwFusedGruFew = 4;
 constexpr int64_t kSpManyChains = 64;
 struct SpGeo {
   int ls, nw;   // steps per wave, waves per workgroup
@@ -97,7 +101,8 @@ SpGeo sp_geo(int cell, int dtype, int64_t n_chains) {
 // chunks (16 per lane), also with many chains where the unfused kernel takes
 // 48 or 40 (bf16 GRU at 128 chains: 32-step chunks 2.54 ms, 64-step 1.76 ms).
 SpGeo sp_geo_fused(int cell, int dtype, int64_t n_chains) {
-  if (cell == PRN_CELL_DIAG_GRU) return {kSpLsFusedGru, kSpNW};
+  if (cell == PRN_CELL_DIAG_GRU)
+    return n_chains < kSpManyChains ? SpGeo{kSpLsFusedGruFew, kSpNwFusedGruFew} : SpGeo{kSpLsFusedGru, kSpNW};
   if (dtype == PRN_F32) return {kSpLsFusedLstm, kSpNW};
   return {kSpLsLstmBf16, kSpNW};
 }
@@ -424,6 +429,8 @@ prn_status newton_sp(const prn_params* p, const Shape& sh, const void* xproj_v, 
           launch(std::integral_constant<int, kSpLsLstmBf16>{}, NW4{}, T_{});
         else
           launch(std::integral_constant<int, kSpLsFusedLstm>{}, NW4{}, T_{});
+      } else if (pl.n_chains < kSpManyChains) {
+        launch(std::integral_constant<int, kSpLsFusedGruFew>{}, std::integral_constant<int, kSpNwFusedGruFew>{}, T_{});
       } else {
         launch(std::integral_constant<int, kSpLsFusedGru>{}, NW4{}, T_{});
       }
