@@ -422,7 +422,9 @@ def main() -> int:
         pb_ms = float(t_pb.mean())
         pfl = 2.0 * proj_flops(w)   # dx and dW: one projection's worth of products each
         backward["input_proj_backward"] = {
-            "kernels": "transposes + k_proj (dx) + split-K k_proj (dW) + ordered sums (prn_input_proj_backward)",
+            "kernels": ("W transpose + k_proj (dx); k_proj_tn (fp32) / k_proj_tn_tr (bf16) split-K over tokens, "
+                        "operand rows read directly (dW); k_splitk_sum; k_colsum64 + ordered sums (dbias) "
+                        "(prn_input_proj_backward)"),
             "ms_mean": pb_ms, "ms_min": float(t_pb.min()), "workspace_bytes": int(pws.numel()),
             "roofline": mfma_roofline(w.dtype, pfl, pb_ms)}
         del dxi, dWi, pws

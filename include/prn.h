@@ -148,8 +148,11 @@ prn_status prn_input_proj(const void* x, const void* W, const float* bias,
  * reproducible) and rounded once to the storage dtype; dbias sums in fp32.
  * The weight gradient is split over token slices whose fp32 partial sums are
  * added in slice order.  When G*d_h and d_in are multiples of 256 its tiles
- * read both operands along their rows; otherwise both are first transposed
- * into the workspace (which then holds dxproj and x once more). */
+ * read both operands along their rows, and also take dbias's column sums
+ * per token slice (so dbias asked for with dW_out may differ in the last
+ * bits from dbias asked for without it, which sums 64-token tiles; each is
+ * bitwise reproducible); otherwise both are first transposed into the
+ * workspace (which then holds dxproj and x once more). */
 prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void* W,
                                    const prn_params* params, void* dx_out, void* dW_out,
                                    float* dbias_out);

@@ -614,7 +614,8 @@ struct PlanPb {
   int64_t Np;            // row length (elements) of W^T and of the padded dxproj
   int splits;
   int64_t ks, Mp, n_rt;  // tokens per slice, padded tokens, 64-token tiles of the dxproj transpose
-  int64_t n_slices, per;  // the tile column sums: n_rt rows reduced in n_slices slices of per rows
+  int64_t n_cs;           // rows of column sums: a row per slice (dW along the rows), else per 64-token tile
+  int64_t n_slices, per;  // the column sums: n_cs rows reduced in n_slices slices of per rows
   size_t wt_off, gp_off, gt_off, xt_off, part_off, csum_off, cslice_off, total;
 };
 constexpr int64_t kPbWgTarget = 1024;   // workgroups the split-K product aims for (128 x 128 tiles)
@@ -662,10 +663,17 @@ PlanPb plan_pb(const prn_params* p, const Shape& sh, bool dx, bool dw, bool db) 
     pl.part_off = take(size_t(pl.splits) * pl.N * pl.Kd * 4);
   }
   if (pl.do_db) {
-    pl.per = (pl.n_rt + kDaSlices - 1) / kDaSlices;
-    pl.n_slices = (pl.n_rt + pl.per - 1) / pl.per;
-    pl.csum_off = take(size_t(pl.n_rt) * pl.N * 4);
-    pl.cslice_off = take(size_t(pl.n_slices) * pl.N * 4);
+    pl.n_cs = pl.do_dw && pl.tn ? pl.splits : pl.n_rt;
+    pl.per = (pl.n_cs + kDaSlices - 1) / kDaSlices;
+    pl.n_slices = (pl.n_cs + pl.per - 1) / pl.per;
+    // sized for the 64-token tiles (at least the slices) whichever outputs
+    // are asked for, so the size queried with every output covers any call
+    pl.csum_off = take(size_t(std::max(pl.n_rt, int64_t(pl.splits))) * pl.N * 4);
+    auto slices_for = [](int64_t n) {
+      const int64_t per = (n + kDaSlices - 1) / kDaSlices;
+      return (n + per - 1) / per;
+    };
+    pl.cslice_off = take(size_t(std::max(slices_for(pl.n_rt), slices_for(pl.splits))) * pl.N * 4);
   }
   pl.total = off;
   return pl;
@@ -1006,11 +1014,11 @@ prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void
   float* csum = pl.do_db ? reinterpret_cast<float*>(ws + pl.csum_off) : nullptr;
   if (pl.do_dw && pl.tn) {
     // dW (N x Kd) = dxproj^T x, split-K over tokens, read along the rows of
-    // both operands (no transposed copies); dbias from the same column sums
+    // both operands (no transposed copies); the same tiles take dxproj's
+    // column sums per slice on the way (dbias)
     float* part = reinterpret_cast<float*>(ws + pl.part_off);
-    prn::launch_proj_tn(bf, dxproj, N * elt, x, Kd * elt, part, M, N, Kd, pl.ks, pl.splits, st);
+    prn::launch_proj_tn(bf, dxproj, N * elt, x, Kd * elt, part, M, N, Kd, pl.ks, pl.splits, csum, st);
     prn::launch_splitk_sum(bf, part, pl.splits, N * Kd, dW_out, st);
-    if (pl.do_db) prn::launch_colsum64(bf, dxproj, M, N, pl.n_rt, csum, st);
   } else if (pl.do_dw) {
     // dW (N x Kd) = dxproj^T x, split-K over tokens
     void* gt = ws + pl.gt_off;
@@ -1028,7 +1036,7 @@ prn_status prn_input_proj_backward(const void* dxproj, const void* x, const void
   if (pl.do_db) {
     float* cslice = reinterpret_cast<float*>(ws + pl.cslice_off);
     prn::k_bw_da_partial<1><<<dim3(unsigned((N + 63) / 64), 1u, unsigned(pl.n_slices)), 256, 0, st>>>(
-        csum, pl.n_rt, pl.per, N, cslice);
+        csum, pl.n_cs, pl.per, N, cslice);
     prn::k_bw_da_reduce<1><<<dim3(unsigned((N + 63) / 64), 1u), 256, 0, st>>>(cslice, pl.n_slices, N, dbias_out);
   }
   return launched("prn_input_proj_backward");

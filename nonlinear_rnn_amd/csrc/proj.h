@@ -38,9 +38,11 @@ void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out,
 // P[z][n][j] = sum over tokens t of slice z (tokens [z ks, min((z+1) ks, M)))
 // of A[t][n] B[t][j]: A tokens x N, B tokens x Kd, rows lda / ldb bytes
 // apart, both 16-byte aligned; N and Kd multiples of 256; fp32 sums,
-// unrounded (P: splits x N x Kd).  No transposed copies.
+// unrounded (P: splits x N x Kd).  No transposed copies.  csum (optional,
+// splits x N): csum[z][n] = the sum of A[t][n] over the tokens of slice z,
+// in a fixed order.
 void launch_proj_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M, int64_t N,
-                    int64_t Kd, int64_t ks, int splits, hipStream_t stream);
+                    int64_t Kd, int64_t ks, int splits, float* csum, hipStream_t stream);
 // csum (n_rt x C) = column sums of every 64 rows of in (R x C, row-major,
 // zero past R), in row order; in 16-byte aligned, C a multiple of 16 bytes
 void launch_colsum64(bool bf16, const void* in, int64_t R, int64_t C, int64_t n_rt, float* csum, hipStream_t stream);

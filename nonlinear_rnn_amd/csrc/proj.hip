@@ -450,9 +450,14 @@ void launch_tiles(bool bf16, const void* A, const void* B, const float* bias, vo
 // down a column of the stage, so the planes come out in the layout k_proj's
 // planes have, with k = t, and no transposed copy of either operand is ever
 // made.  Stages and planes are double buffered as in k_proj.
+// csum (optional): csum[z][n] = the sum of A[t][n] over the slice's tokens,
+// taken by the workgroups of the first column tile (bid % n_tiles_j == 0)
+// on the split, where each value passes one thread: the thread of column n
+// and token half h (tokens 16 s + 8 h .. + 7 of every stage s) sums its
+// values in token order, and the two halves are added last (h = 0 first).
 __global__ void __launch_bounds__(1024)
 k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* __restrict__ P, int64_t M, int64_t N,
-          int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j) {
+          int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j, float* __restrict__ csum) {
   constexpr int BM = 256, BN = 256, NROWS = BM + BN, NW = 16, NTHR = 64 * NW, WC = 4, WM = 2, WN = 2;
   constexpr int ELT = 4, NPL = 3, NTERM = 6, KS = 16;
   constexpr int FROW = NROWS * ELT, FST = KS * FROW;  // a token's row of the stage; the stage
@@ -476,6 +481,9 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC;
   const int half = lane >> 5, l32 = lane & 31;
+  // this thread's column sum (threads of the A rows, first column tile)
+  const bool sums = csum && bid % n_tiles_j == 0 && (tid & (NROWS - 1)) < BM;
+  float cs = 0.0f;
 
   // wave load li = wave IPW + p fills stage bytes [1024 li, +1024): token
   // row 1024 li / FROW of the stage, from byte 1024 li % FROW of that row
@@ -510,6 +518,12 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
     for (int e = 0; e < 4; ++e) {
       va[e] = *reinterpret_cast<const float*>(f + e * FROW);
       vb[e] = *reinterpret_cast<const float*>(f + (4 + e) * FROW);
+    }
+    if (sums) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs += va[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs += vb[e];
     }
     bf16x8 h0, h1, h2;
     split3(va, vb, h0, h1, h2);
@@ -580,6 +594,16 @@ k_proj_tn(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* _
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kSplitU[t]], bp[j][kSplitV[t]], acc[i][j], 0, 0, 0);
       }
     }
+  }
+
+  if (csum && bid % n_tiles_j == 0) {
+    // the two token halves of each column: h = 1 hands its sum over through
+    // LDS (the stage buffers are free once every wave has left the loop)
+    float* const hand = reinterpret_cast<float*>(lds);
+    __syncthreads();
+    if (sums && tid >= NROWS) hand[tid - NROWS] = cs;
+    __syncthreads();
+    if (sums && tid < NROWS) csum[z * N + n0 + tid] = cs + hand[tid];
   }
 
   // lane l, accumulator r of block (i, j): row n0 + .. + 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
@@ -699,10 +723,13 @@ __global__ void __launch_bounds__(256) k_pad_rows(const typename Elt<BF16>::T* _
 // so the sums are bitwise the same.  Three 32-token stages (one being read,
 // two in flight).  Within a token row the 16-byte chunk c sits at c ^
 // swz(t), so the eight rows one transposed read touches (t0 + 0..3 and
-// t0 + 8..11) fall into eight different 64-byte segments.
+// t0 + 8..11) fall into eight different 64-byte segments.  csum (optional)
+// as in k_proj_tn: in the workgroups of the first column tile, the thread
+// of column n and token quarter q sums tokens 32 s + 8 q .. + 7 of every
+// stage s in token order, and the quarters are added last, in order.
 __global__ void __launch_bounds__(1024)
 k_proj_tn_tr(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float* __restrict__ P, int64_t M,
-             int64_t N, int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j) {
+             int64_t N, int64_t Kd, int64_t lda, int64_t ldb, int64_t ks, int n_tiles_j, float* __restrict__ csum) {
   constexpr int BM = 256, BN = 256, NROWS = BM + BN, NW = 16, WC = 4, WM = 2, WN = 2;
   constexpr int KS = 32, FROW = NROWS * 2, FST = KS * FROW, NBUF = 3;
   constexpr int NLD = FST / 1024, IPW = NLD / NW;   // a wave load fills one token row (1 KB)
@@ -720,6 +747,9 @@ k_proj_tn_tr(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC;
   const int half = lane >> 5, l32 = lane & 31;
+  const bool sums = csum && bid % n_tiles_j == 0;   // wave-uniform
+  const int scol = tid & (BM - 1), sq = tid / BM;   // this thread's column and token quarter
+  float cs = 0.0f;
 
   // wave load li = wave IPW + p fills token row li of the stage: lane l the
   // 16 bytes at position l, i.e. chunk l ^ swz(li) of the row (chunks 0..31:
@@ -784,6 +814,14 @@ k_proj_tn_tr(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float
     asm volatile("" ::: "memory");
     if (kt + 2 < nk) issue(kt + 2, static_cast<int>((kt + 2) % NBUF));
     const uint8_t* st = lds + cur * FST;
+    if (sums) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * sq + e;
+        const uint16_t v = *reinterpret_cast<const uint16_t*>(st + t * FROW + 16 * ((scol >> 3) ^ swz(t)) + 2 * (scol & 7));
+        cs += __uint_as_float(static_cast<uint32_t>(v) << 16);
+      }
+    }
 #pragma unroll
     for (int step = 0; step < KS / 16; ++step) {
       bf16x8 bp[WN];
@@ -796,6 +834,15 @@ k_proj_tn_tr(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, float
         for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bp[j], acc[i][j], 0, 0, 0);
       }
     }
+  }
+
+  if (sums) {
+    // the four token quarters of each column, added in order
+    float* const hand = reinterpret_cast<float*>(lds);
+    __syncthreads();
+    hand[tid] = cs;
+    __syncthreads();
+    if (tid < BM) csum[z * N + n0 + tid] = ((hand[tid] + hand[BM + tid]) + hand[2 * BM + tid]) + hand[3 * BM + tid];
   }
 
   // lane l, accumulator r of block (i, j): row n0 + .. + 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
@@ -875,15 +922,15 @@ void launch_pad_rows(bool bf16, const void* in, int64_t R, int64_t C, void* out,
 }
 
 void launch_proj_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, float* P, int64_t M, int64_t N,
-                    int64_t Kd, int64_t ks, int splits, hipStream_t stream) {
+                    int64_t Kd, int64_t ks, int splits, float* csum, hipStream_t stream) {
   const int tj = static_cast<int>(Kd / 256);
   const dim3 grid(static_cast<unsigned>((N / 256) * tj), static_cast<unsigned>(splits));
   if (bf16)
     k_proj_tn_tr<<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N, Kd,
-                                            lda, ldb, ks, tj);
+                                            lda, ldb, ks, tj, csum);
   else
     k_proj_tn<<<grid, 1024, 0, stream>>>(static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), P, M, N, Kd,
-                                         lda, ldb, ks, tj);
+                                         lda, ldb, ks, tj, csum);
 }
 
 void launch_colsum64(bool bf16, const void* in, int64_t R, int64_t C, int64_t n_rt, float* csum, hipStream_t stream) {

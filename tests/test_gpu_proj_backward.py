@@ -85,6 +85,24 @@ def test_projection_backward_matches_oracle(cell, dtype, Bn, T, d_in, d_h):
     assert torch.equal(dx, dx2) and torch.equal(dW, dW2) and torch.equal(db, db2)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dbias_with_and_without_the_weight_gradient(dtype):
+    """Where dW reads the operand rows (G d_h and d_in multiples of 256) the
+    dW tiles also take dbias's column sums (one per token slice); asked for
+    alone, dbias comes from 64-token column sums.  Both against the oracle,
+    and each bitwise reproducible."""
+    cell = "gru"
+    dxp, x, W = _inputs(cell, dtype, 2, 1500, 256, 256, seed=11)
+    _, _, db_all = _run(cell, dxp, x, W)
+    _, _, db_alone = _run(cell, dxp, x, W, dx=False, dW=False)
+    g64 = to_f64(dxp).reshape(-1, dxp.shape[-2] * dxp.shape[-1])
+    ref, ref_abs = g64.sum(0), np.abs(g64).sum(0)
+    _check("f32", db_all, ref, ref_abs, "dbias with dW")
+    _check("f32", db_alone, ref, ref_abs, "dbias alone")
+    assert torch.equal(db_all, _run(cell, dxp, x, W)[2])
+    assert torch.equal(db_alone, _run(cell, dxp, x, W, dx=False, dW=False)[2])
+
+
 def test_projection_backward_optional_outputs_misaligned_input_and_empty():
     cell, dtype = "lstm", "f32"
     dxp, x, W = _inputs(cell, dtype, 2, 500, 24, 40, seed=3)
