@@ -76,6 +76,18 @@ template <> __device__ __forceinline__ Aff<2> rec_load_map<2>(const float* p) {
           rec_load(p + 3 * kWave), rec_load(p + 4 * kWave), rec_load(p + 5 * kWave)};
 }
 
+// an LDS map slot reused for a wave's carry-in (its first S floats)
+__device__ __forceinline__ void map_put_carry(Aff<1>& m, const float* c) { m.a = c[0]; }
+__device__ __forceinline__ void map_put_carry(Aff<2>& m, const float* c) {
+  m.a00 = c[0];
+  m.a01 = c[1];
+}
+__device__ __forceinline__ void map_get_carry(const Aff<1>& m, float* c) { c[0] = m.a; }
+__device__ __forceinline__ void map_get_carry(const Aff<2>& m, float* c) {
+  c[0] = m.a00;
+  c[1] = m.a01;
+}
+
 struct SpRecords {
   unsigned* status;    // [K][n_chains][n_ch]
   float* agg;          // [K][n_chains][n_ch][NC][64]
@@ -230,12 +242,12 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   static_assert(!(FX && PIC), "the Picard sweep reads the step before the chunk, which the fused tile lacks");
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform, kept in SGPRs
-  __shared__ Map part[2][NW][kWave];
-  // one buffer suffices: the look-back wave writes it only after the next
-  // iteration's first barrier, which every wave reaches after reading it
-  // (and 53.5 KB instead of 53.8 KB lets three GRU workgroups of 16-step
-  // sub-chunks share a CU's 160 KB)
-  __shared__ float carry_sh[S][kWave];
+  // part[w][lane]: wave w's sub-chunk map, written before an iteration's
+  // first barrier; the look-back wave reads every slot and overwrites it
+  // with that wave's carry-in (map_put_carry) before the second barrier.
+  // A wave reads only its own slot after that and rewrites it only in the
+  // next iteration, so one buffer serves every iteration.
+  __shared__ Map part[NW][kWave];
   __shared__ unsigned red[NW];
   __shared__ unsigned tk;
   // the chunk's scaled projected inputs, read-only after the first walk:
@@ -449,21 +461,29 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   // ends of the loop body)
   auto iteration = [&](int k, auto last_t) __attribute__((always_inline)) {
     constexpr bool last = decltype(last_t)::value;
-    const int pb = k & 1;
-    part[pb][w][lane] = acc;
+    part[w][lane] = acc;
     __syncthreads();
     residual_finish(k);
 
     // ---- carry across chunks: one wave publishes and looks back ----
     if (w == NW - 1 && ticket < n_wg) {
-      Map tot = part[pb][0][lane];
+      Map tot = part[0][lane];
 #pragma unroll
-      for (int v = 1; v < NW; ++v) tot = compose(part[pb][v][lane], tot);
+      for (int v = 1; v < NW; ++v) tot = compose(part[v][lane], tot);
       const int64_t base = (static_cast<int64_t>(k) * n_chains + chain) * n_ch;
       float cin[S];
       lookback_carry<S>(rec, base, chunk, tot, lane, spin_limit, agg_first, cin);
+      // each wave's carry-in: the chunk's, through the maps of the waves
+      // before it, applied in wave order
+      float c[S];
 #pragma unroll
-      for (int q = 0; q < S; ++q) carry_sh[q][lane] = cin[q];
+      for (int q = 0; q < S; ++q) c[q] = cin[q];
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const Map m = part[v][lane];
+        map_put_carry(part[v][lane], c);
+        if (v + 1 < NW) apply(m, c);
+      }
       // the inclusive prefix (state after the chunk's last step) goes out
       // before the barrier; its status is published right after it, while
       // the other waves already start their fix-up
@@ -493,9 +513,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
     acc = Map::identity();
     rmax = 0;
     float s[S];
-#pragma unroll
-    for (int q = 0; q < S; ++q) s[q] = carry_sh[q][lane];
-    for (int v = 0; v < w; ++v) apply(part[pb][v][lane], s);
+    map_get_carry(part[w][lane], s);
     float pr[S];
 #pragma unroll
     for (int q = 0; q < S; ++q) pr[q] = ST::round(s[q]);

@@ -70,7 +70,12 @@ constexpr int kScanSeg = 16;
 // 0.127 / 0.290; 12 x 8 0.118 / 0.285; 10 x 6 0.108 / 0.264.  Eight waves
 // lost where the chains are many or the state is wider: bf16 GRU at 128
 // chains 8 x 8 0.978 and 5 x 8 0.953 ms against 0.836 at 10 x 4; the long
-// LSTM 8 x 8 0.909 against 0.678 at 16 x 4.
+// LSTM 8 x 8 0.909 against 0.678 at 16 x 4.  With the waves' maps in one
+// LDS buffer instead of two (the slot of each wave then carries its
+// carry-in), 12 x 8 fits two workgroups per CU (77 KB) and took the ragged
+// pack from 0.216 to 0.204 ms (32 chains: 0.0965 -> 0.0961 ms); the long
+// LSTM at 8 x 8 (two workgroups per CU then) still took 0.894 ms, at 7 x 8
+// 0.947, against 0.666 at 16 x 4.
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
 // keeps LS = 8 (LS = 12 already needs 256 registers, LS = 16 spills); the
 // bf16 GRU with many chains takes LS = 10, the longest chunk that keeps four
@@ -79,7 +84,7 @@ constexpr int kScanSeg = 16;
 constexpr int kSpNW = 4;
 constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
 constexpr int kSpNwLstm = 4, kSpNwLstmBf16 = 4, kSpNwGruMany = 4, kSpNwGruManyBf16 = 4;
-constexpr int kSpLsGruFew = 10, kSpNwGruFew = 8;   // GRU below kSpManyChains chains
+constexpr int kSpLsGruFew = 12, kSpNwGruFew = 8;   // GRU below kSpManyChains chains
 constexpr int kSpLsFusedGru = 16, kSpLsFusedLstm = 16;
 // fused GRU below kSpManyChains chains: eight waves lost there (MALL flushed,
 // 32-chain GRU / 4-chain ragged pack: 16 x 4 0.189 / 0.343 ms, 8 x 8 0.205 /
