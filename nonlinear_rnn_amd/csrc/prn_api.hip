@@ -75,14 +75,18 @@ constexpr int kScanSeg = 16;
 // carry-in), 12 x 8 fits two workgroups per CU (77 KB) and took the ragged
 // pack from 0.216 to 0.204 ms (32 chains: 0.0965 -> 0.0961 ms); the long
 // LSTM at 8 x 8 (two workgroups per CU then) still took 0.894 ms, at 7 x 8
-// 0.947, against 0.666 at 16 x 4.
+// 0.947, against 0.666 at 16 x 4.  The bf16 GRU at 128 chains then took
+// 0.812 / 0.781 / 0.758 / 0.824 ms at LS = 10 / 11 / 12 / 13 (four waves);
+// the long LSTM at LS = 18 (72-step chunks, 80 KB, still two per CU) 0.662
+// against 0.673 ms, not taken: the fused forward's chunks must be multiples
+// of 32 steps, and at equal chunks both forwards give the same bits.
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
-// keeps LS = 8 (LS = 12 already needs 256 registers, LS = 16 spills); the
-// bf16 GRU with many chains takes LS = 10, the longest chunk that keeps four
-// waves per SIMD (122 registers, 35 KB of LDS) -- measured at 16 x 16384 x
-// 512: LS = 8 / 10 took 1.06 / 0.97 ms.
+// keeps LS = 8 (LS = 12 needed 256 registers before the peel, LS = 16
+// spilled); the bf16 GRU with many chains took LS = 10 while that was the
+// longest chunk that kept four waves per SIMD (measured at 16 x 16384 x
+// 512: LS = 8 / 10 took 1.06 / 0.97 ms then), and takes 12 since (above).
 constexpr int kSpNW = 4;
-constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruManyBf16 = 10;
+constexpr int kSpLsLstm = 16, kSpLsLstmBf16 = 8, kSpLsGruMany = 12, kSpLsGruManyBf16 = 12;
 constexpr int kSpNwLstm = 4, kSpNwLstmBf16 = 4, kSpNwGruMany = 4, kSpNwGruManyBf16 = 4;
 constexpr int kSpLsGruFew = 12, kSpNwGruFew = 8;   // GRU below kSpManyChains chains
 constexpr int kSpLsFusedGru = 16, kSpLsFusedLstm = 16;

@@ -44,8 +44,8 @@ IDS = [w.name for w in CASES]
 def same_chunking(w) -> bool:
     """Do the fused and two-call forwards take the same chunks?  Only the
     LSTM: the fused GRU takes 64-step chunks of four waves, the unfused one
-    96-step chunks of eight waves below 64 (row, 64-channel) chains and 48-
-    or 40-step chunks from 64 on."""
+    96-step chunks of eight waves below 64 (row, 64-channel) chains and
+    48-step chunks from 64 on."""
     return w.cell == "lstm"
 
 
