@@ -605,16 +605,19 @@ prn_status check_head(const prn_params* p, Shape* sh, int32_t d_head) {
 }
 
 // ---- the projection's backward ----
-// dW = dxproj^T x reduces over tokens, the row index of both operands; the
-// matrix-core tile multiplies operands whose reduction index runs along
-// their rows, so both are transposed into the workspace first (token-padded
-// with zeros to splits x ks), and the product runs split-K: slice z
-// multiplies tokens [z ks, (z+1) ks) into its own fp32 block, and the blocks
-// are summed in slice order.  dx = dxproj W only needs W transposed; dxproj
-// is read in place when its rows are whole 16-byte chunks, else from a
-// zero-padded copy.  dbias comes from the column sums the dxproj transpose
-// takes on the way (per 64 tokens, then in token order, in two fixed-order
-// levels).
+// dW = dxproj^T x reduces over tokens, the row index of both operands.
+// When G d_h and d_in are multiples of 256, the dW tiles read both operands
+// along their rows (token-major K stages; fp32 through the split into term
+// planes, bf16 through transposed LDS reads) and take dxproj's column sums
+// per token slice on the way (dbias).  Otherwise both operands are first
+// transposed into the workspace (token-padded with zeros to splits x ks) for
+// the split-K instance of the forward's tile, and dbias comes from the
+// column sums the dxproj transpose takes (per 64 tokens).  Either way slice
+// z multiplies tokens [z ks, (z+1) ks) into its own fp32 block and the
+// blocks are summed in slice order.  dx = dxproj W only needs W transposed;
+// dxproj is read in place when its rows are whole 16-byte chunks, else from
+// a zero-padded copy.  Every column-sum set is reduced in two fixed-order
+// levels.
 struct PlanPb {
   int64_t M, N, Kd;      // tokens, G d_h, d_in
   bool do_dx, do_dw, do_db;
