@@ -79,7 +79,9 @@ constexpr int kScanSeg = 16;
 // 0.812 / 0.781 / 0.758 / 0.824 ms at LS = 10 / 11 / 12 / 13 (four waves);
 // the long LSTM at LS = 18 (72-step chunks, 80 KB, still two per CU) 0.662
 // against 0.673 ms, not taken: the fused forward's chunks must be multiples
-// of 32 steps, and at equal chunks both forwards give the same bits.
+// of 32 steps, and at equal chunks both forwards give the same bits.  Other
+// long-LSTM shapes on the same build: 11 x 4 and 12 x 4 under a
+// three-waves-per-SIMD cap 0.723 / 0.761 ms, 16 x 2 0.841, 16 x 3 0.823.
 // bf16 storage needs more registers per step (unpacking): the bf16 LSTM
 // keeps LS = 8 (LS = 12 needed 256 registers before the peel, LS = 16
 // spilled); the bf16 GRU with many chains took LS = 10 while that was the
