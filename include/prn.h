@@ -323,20 +323,26 @@ prn_status prn_decode_step(const void* x, const void* W, const float* bias, cons
  * Newton as for the diagonal cells, with dense Jacobian blocks per head.
  *   A          (3, n_heads, d_head, d_head) fp32, gate order z, r, c; A[g][k][i][j]
  *              multiplies channel j of head k into channel i (row-major blocks)
- *   xproj      (B, T, 3, d_h) fp32, as for the diagonal GRU; 16-byte aligned
- *   h0         (B, d_h) fp32 or NULL (zeros); 16-byte aligned
- *   H_out      (B, T, d_h) fp32; 16-byte aligned (the Newton forward reads
- *              and writes it in 4-channel vectors)
- * params: cell = PRN_CELL_DIAG_GRU, dtype = PRN_F32, B, T, d_h, n_seqs = 0,
- * state_last_out ((B, d_h) or NULL), workspace, stream; a, states_out and
- * picard_iters are not used (states_out / picard_iters must be 0).
- * Supported: d_head = 16, fp32, rectangular batches (the pages' head-mix
- * fused path takes no ragged pack); anything else is PRN_ERR_UNSUPPORTED.
+ *   xproj      (B, T, 3, d_h) storage dtype, as for the diagonal GRU; aligned
+ *              to 4 elements (16 bytes fp32, 8 bytes bf16)
+ *   h0         (B, d_h) storage dtype or NULL (zeros); aligned to 4 elements
+ *   H_out      (B, T, d_h) storage dtype; aligned to 4 elements (the Newton
+ *              forward reads the iterates in 4-channel vectors)
+ * params: cell = PRN_CELL_DIAG_GRU, dtype (PRN_F32 or PRN_BF16: the storage
+ * of xproj, h0, the iterates, H_out and state_last_out; A and every
+ * operation are fp32, each stored iterate is rounded once to nearest even),
+ * B, T, d_h, n_seqs = 0, state_last_out ((B, d_h) or NULL), workspace,
+ * stream; a, states_out and picard_iters are not used (states_out /
+ * picard_iters must be 0).
+ * Supported: d_head = 16, rectangular batches (the pages' head-mix fused
+ * path takes no ragged pack); anything else is PRN_ERR_UNSUPPORTED.
  * Errors as for prn_newton_forward; residual_out as there (K + 1 values). */
 size_t prn_head_workspace_bytes(const prn_params* params, int32_t d_head, int32_t K);
 prn_status prn_head_newton_forward(const void* xproj, const prn_params* params, const float* A, int32_t d_head,
                                    const void* h0, int32_t K, void* H_out, float* residual_out);
-/* The unroll h_t = f(h_{t-1}, x_t) of the head-mix GRU; no workspace. */
+/* The unroll h_t = f(h_{t-1}, x_t) of the head-mix GRU, the state chain in
+ * fp32 and every output rounded once to the storage dtype; no workspace;
+ * pointers aligned to their element size. */
 prn_status prn_head_sequential_forward(const void* xproj, const prn_params* params, const float* A,
                                        int32_t d_head, const void* h0, void* H_out);
 

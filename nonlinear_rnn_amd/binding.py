@@ -422,8 +422,12 @@ def prn_decode_step(x, W, bias, a, state_out, *, cell: str, state_in=None, h_out
 
 
 def _head_common(xproj, A, H_out, h0, state_last_out, d_head):
-    for t, n in ((xproj, "xproj"), (A, "A"), (H_out, "H_out"), (h0, "h0"), (state_last_out, "state_last_out")):
-        _dev(t, n, torch.float32)
+    _dev(xproj, "xproj")
+    if xproj.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported storage dtype {xproj.dtype}")
+    _dev(A, "A", torch.float32)
+    for t, n in ((H_out, "H_out"), (h0, "h0"), (state_last_out, "state_last_out")):
+        _dev(t, n, xproj.dtype)
     Bn, T, G, d_h = xproj.shape
     if G != 3 or d_h % d_head or A.shape != (3, d_h // d_head, d_head, d_head) or H_out.shape != (Bn, T, d_h):
         raise ValueError(f"shape mismatch: xproj {tuple(xproj.shape)} A {tuple(A.shape)} H_out {tuple(H_out.shape)}")
@@ -433,8 +437,8 @@ def _head_common(xproj, A, H_out, h0, state_last_out, d_head):
     return Bn, T, d_h
 
 
-def prn_head_workspace_bytes(B: int, T: int, d_h: int, K: int, d_head: int = 16) -> int:
-    p = make_params("gru", torch.float32, B, T, d_h)
+def prn_head_workspace_bytes(B: int, T: int, d_h: int, K: int, d_head: int = 16, dtype=torch.float32) -> int:
+    p = make_params("gru", dtype, B, T, d_h)
     n = int(lib().prn_head_workspace_bytes(ctypes.byref(p), d_head, K))
     if n == 0 and T > 0 and prn_last_error():
         raise PrnError(PRN_ERR_INVALID_ARG, prn_last_error())
@@ -443,10 +447,11 @@ def prn_head_workspace_bytes(B: int, T: int, d_h: int, K: int, d_head: int = 16)
 
 def prn_head_newton_forward(xproj, A, K: int, H_out, *, d_head: int = 16, h0=None, residual_out=None,
                             state_last_out=None, workspace=None, stream=None) -> None:
-    """Head-mix GRU Newton forward: xproj (B,T,3,d_h), A (3, d_h/d_head, d_head, d_head), fp32."""
+    """Head-mix GRU Newton forward: xproj (B,T,3,d_h) and H_out, h0, state_last_out in the storage dtype
+    (fp32 or bf16), A (3, d_h/d_head, d_head, d_head) fp32."""
     Bn, T, d_h = _head_common(xproj, A, H_out, h0, state_last_out, d_head)
     _dev(residual_out, "residual_out", torch.float32)
-    p = make_params("gru", torch.float32, Bn, T, d_h, state_last_out=state_last_out, workspace=workspace,
+    p = make_params("gru", xproj.dtype, Bn, T, d_h, state_last_out=state_last_out, workspace=workspace,
                     stream=stream)
     _check(lib().prn_head_newton_forward(_ptr(xproj), ctypes.byref(p), _ptr(A), d_head, _ptr(h0), int(K),
                                          _ptr(H_out), _ptr(residual_out)))
@@ -455,5 +460,5 @@ def prn_head_newton_forward(xproj, A, K: int, H_out, *, d_head: int = 16, h0=Non
 def prn_head_sequential_forward(xproj, A, H_out, *, d_head: int = 16, h0=None, state_last_out=None,
                                 stream=None) -> None:
     Bn, T, d_h = _head_common(xproj, A, H_out, h0, state_last_out, d_head)
-    p = make_params("gru", torch.float32, Bn, T, d_h, state_last_out=state_last_out, stream=stream)
+    p = make_params("gru", xproj.dtype, Bn, T, d_h, state_last_out=state_last_out, stream=stream)
     _check(lib().prn_head_sequential_forward(_ptr(xproj), ctypes.byref(p), _ptr(A), d_head, _ptr(h0), _ptr(H_out)))

@@ -1,5 +1,7 @@
 // Head-mix GRU (dense d_head x d_head recurrent blocks, d_head = 16): the
-// parallel Newton forward and the sequential unroll, fp32 storage.
+// parallel Newton forward and the sequential unroll, fp32 or bf16 storage
+// (xproj, h0, the iterates and H; the blocks A and all arithmetic fp32; a
+// stored iterate is rounded once, the chain it came from is not).
 //
 // Cell (per head, A_g the head's block of gate g, h the head's 16 channels):
 //   z = sig(x_z + A_z h)  r = sig(x_r + A_r h)  c = tanh(x_c + A_c (r h))
@@ -116,27 +118,34 @@ struct HmShared {
 };
 
 __device__ __forceinline__ hm_f4 hm_ld4(const float* p) { return *reinterpret_cast<const hm_f4*>(p); }
+// four consecutive stored values (16 bytes fp32, 8 bytes bf16) as floats
+__device__ __forceinline__ hm_f4 hm_ld4s(const float* p) { return hm_ld4(p); }
+__device__ __forceinline__ hm_f4 hm_ld4s(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return hm_f4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
 
 // phase A for steps jb .. jb + 15 of the chunk (lane L: step jb + L % 16,
 // channels 4 (L / 16) .. + 3 of the head); steps at or past n are computed
 // on clamped inputs and ignored
-template <bool RES>
-__device__ __forceinline__ void hm_phase_a(const HmBlocks& blk, const float* xproj, const float* Hprev,
-                                           const float* h0, int64_t b, int64_t head, int64_t t0, int jb, int n,
-                                           int64_t T, int64_t d_h, int lane, HmShared& sh, unsigned& rmax) {
+template <bool RES, class E>
+__device__ __forceinline__ void hm_phase_a(const HmBlocks& blk, const E* xproj, const E* Hprev, const E* h0,
+                                           int64_t b, int64_t head, int64_t t0, int jb, int n, int64_t T,
+                                           int64_t d_h, int lane, HmShared& sh, unsigned& rmax) {
   const int col = lane & 15, mk = 4 * (lane >> 4);
   const int j = jb + col;
   const bool valid = j < n;
   const int64_t t = t0 + (valid ? j : n - 1);
   const int64_t c0 = head * kHmD + mk;
-  const float* xp = xproj + ((b * T + t) * 3) * d_h + c0;
-  const hm_f4 xz = hm_ld4(xp), xr = hm_ld4(xp + d_h), xc = hm_ld4(xp + 2 * d_h);
+  const E* xp = xproj + ((b * T + t) * 3) * d_h + c0;
+  const hm_f4 xz = hm_ld4s(xp), xr = hm_ld4s(xp + d_h), xc = hm_ld4s(xp + 2 * d_h);
   hm_f4 P = {0.0f, 0.0f, 0.0f, 0.0f}, cur = {0.0f, 0.0f, 0.0f, 0.0f};
   if (Hprev) {
-    cur = hm_ld4(Hprev + (b * T + t) * d_h + c0);
-    if (t > 0) P = hm_ld4(Hprev + (b * T + t - 1) * d_h + c0);
+    cur = hm_ld4s(Hprev + (b * T + t) * d_h + c0);
+    if (t > 0) P = hm_ld4s(Hprev + (b * T + t - 1) * d_h + c0);
   }
-  if (t == 0 && h0) P = hm_ld4(h0 + b * d_h + c0);
+  if (t == 0 && h0) P = hm_ld4s(h0 + b * d_h + c0);
   else if (t == 0) P = hm_f4{0.0f, 0.0f, 0.0f, 0.0f};
   // linearising at H = 0 (the first iteration; no h0 in this block): the
   // recurrent terms A_g P vanish, and so do their block products
@@ -202,11 +211,14 @@ __device__ __forceinline__ float hm_chain_step(const HmBlocks& blk, HmShared& sh
 //   prev_t), into Hout (and the row's final state into slast);
 // kHmResidual: only the residual of Hprev.
 // J_0 := 0 (the map of a sequence's first step is constant, f_0).
-template <int MODE>
+template <int MODE, int DT>
 __global__ void __launch_bounds__(kWave)
-k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
-          const float* __restrict__ Hprev, const float* __restrict__ carry, int64_t T, int64_t d_h, int64_t n_ch,
-          float* __restrict__ agg, float* __restrict__ rpart, float* __restrict__ Hout, float* __restrict__ slast) {
+k_hm_pass(const typename Storage<DT>::T* __restrict__ xproj, const float* __restrict__ A,
+          const typename Storage<DT>::T* __restrict__ h0, const typename Storage<DT>::T* __restrict__ Hprev,
+          const float* __restrict__ carry, int64_t T, int64_t d_h, int64_t n_ch, float* __restrict__ agg,
+          float* __restrict__ rpart, typename Storage<DT>::T* __restrict__ Hout,
+          typename Storage<DT>::T* __restrict__ slast) {
+  using ST = Storage<DT>;
   const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
   const int mr = lane & 15, mk = 4 * (lane >> 4);  // product layout: rows mk..mk+3 of column mr
   const int64_t chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
@@ -261,7 +273,7 @@ k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const fl
           }
           d = hm_chain_step(blk, sh, s, d, i, q, zprev);
         }
-        if (MODE == kHmFix && q == 0) Hout[(b * T + t0 + jb + s) * d_h + head * kHmD + i] = d;
+        if (MODE == kHmFix && q == 0) Hout[(b * T + t0 + jb + s) * d_h + head * kHmD + i] = ST::pack(d);
       }
     }
     __syncthreads();  // the coefficients are rewritten by the next block
@@ -272,7 +284,7 @@ k_hm_pass(const float* __restrict__ xproj, const float* __restrict__ A, const fl
     for (int r = 0; r < 4; ++r) out[(mk + r) * kHmD + mr] = M[r];
     if (q == 0) out[kHmD * kHmD + i] = d;
   }
-  if (MODE == kHmFix && slast && t0 + n == T && q == 0) slast[b * d_h + head * kHmD + i] = d;
+  if (MODE == kHmFix && slast && t0 + n == T && q == 0) slast[b * d_h + head * kHmD + i] = ST::pack(d);
   if (MODE != kHmFix && rpart) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, kWave)));
@@ -383,34 +395,37 @@ k_hm_expand(const float* __restrict__ agg, const float* __restrict__ gcarry, int
 }
 
 // The sequential unroll: one wave per (row, head), h_t = f(h_(t-1), x_t).
+template <int DT>
 __global__ void __launch_bounds__(kWave)
-k_hm_sequential(const float* __restrict__ xproj, const float* __restrict__ A, const float* __restrict__ h0,
-                int64_t T, int64_t d_h, float* __restrict__ Hout, float* __restrict__ slast) {
+k_hm_sequential(const typename Storage<DT>::T* __restrict__ xproj, const float* __restrict__ A,
+                const typename Storage<DT>::T* __restrict__ h0, int64_t T, int64_t d_h,
+                typename Storage<DT>::T* __restrict__ Hout, typename Storage<DT>::T* __restrict__ slast) {
+  using ST = Storage<DT>;
   const int lane = threadIdx.x, i = lane >> 2, q = lane & 3;
   const int64_t head = blockIdx.x, b = blockIdx.y, n_heads = gridDim.x;
   const int64_t ch = head * kHmD + i;
   __shared__ float xs[kHmSeqBlock][3][kHmD];
   HmBlocks blk;
   hm_load_blocks(A, n_heads, head, lane, blk);
-  float h = h0 ? h0[b * d_h + ch] : 0.0f;
+  float h = h0 ? ST::load(h0 + b * d_h + ch) : 0.0f;
   for (int64_t t0 = 0; t0 < T; t0 += kHmSeqBlock) {
     // the next block's inputs, all loads in flight at once
     const int n = static_cast<int>(imin(T - t0, kHmSeqBlock));
-    const float* xb = xproj + ((b * T + t0) * 3) * d_h + head * kHmD;
+    const typename ST::T* xb = xproj + ((b * T + t0) * 3) * d_h + head * kHmD;
     __syncthreads();  // the previous block's reads are done
 #pragma unroll 8
     for (int e = lane; e < n * 3 * kHmD; e += kWave) {
       const int j = e / (3 * kHmD), r = e - j * 3 * kHmD, g = r / kHmD, c = r - g * kHmD;
-      xs[j][g][c] = xb[(static_cast<int64_t>(j) * 3 + g) * d_h + c];
+      xs[j][g][c] = ST::load(xb + (static_cast<int64_t>(j) * 3 + g) * d_h + c);
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
       const float x[3] = {xs[j][0][i], xs[j][1][i], xs[j][2][i]};
       h = hm_step(blk, x, h, q);
-      if (q == 0) Hout[(b * T + t0 + j) * d_h + ch] = h;
+      if (q == 0) Hout[(b * T + t0 + j) * d_h + ch] = ST::pack(h);
     }
   }
-  if (slast && q == 0) slast[b * d_h + ch] = h;
+  if (slast && q == 0) slast[b * d_h + ch] = ST::pack(h);
 }
 
 }  // namespace prn

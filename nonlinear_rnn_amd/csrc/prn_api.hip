@@ -576,7 +576,7 @@ PlanHm plan_hm(const prn_params* p, int K) {
   pl.n_ch = (p->T + prn::kHmChunk - 1) / prn::kHmChunk;
   pl.n_wg = p->B * pl.n_heads * pl.n_ch;
   pl.n_iter = size_t(std::min(K - 1, 2));  // ping-pong iterates H^(1..K-1); H^(K) goes to H_out
-  const size_t it = align_up(size_t(p->B) * p->T * p->d_h * 4);
+  const size_t it = align_up(size_t(p->B) * p->T * p->d_h * (p->dtype == PRN_BF16 ? 2 : 4));
   pl.iter_off = 0;
   pl.agg_off = pl.n_iter * it;
   pl.carry_off = pl.agg_off + align_up(size_t(pl.n_wg) * prn::kHmNC * 4);
@@ -590,13 +590,12 @@ PlanHm plan_hm(const prn_params* p, int K) {
   return pl;
 }
 
-// Head-mix support: the GRU, fp32 storage, rectangular batches (the pages'
-// head-mix fused path takes no ragged pack), d_head = 16.
+// Head-mix support: the GRU, fp32 or bf16 storage, rectangular batches (the
+// pages' head-mix fused path takes no ragged pack), d_head = 16.
 prn_status check_head(const prn_params* p, Shape* sh, int32_t d_head) {
   prn_status s = check_common(p, sh);
   if (s != PRN_OK) return s;
   if (p->cell != PRN_CELL_DIAG_GRU) return fail(PRN_ERR_UNSUPPORTED, "head-mix blocks are built for the GRU cell");
-  if (p->dtype != PRN_F32) return fail(PRN_ERR_UNSUPPORTED, "head-mix runs with fp32 storage only");
   if (p->n_seqs != 0) return fail(PRN_ERR_UNSUPPORTED, "head-mix takes rectangular batches, not a ragged pack");
   if (d_head != prn::kHmD) return fail(PRN_ERR_UNSUPPORTED, "d_head = %d: head-mix is built for d_head = 16", d_head);
   if (p->d_h % d_head != 0) return fail(PRN_ERR_INVALID_ARG, "d_h = %lld is not a multiple of d_head", (long long)p->d_h);
@@ -1067,6 +1066,55 @@ size_t prn_head_workspace_bytes(const prn_params* p, int32_t d_head, int32_t K) 
   return p->T > 0 ? plan_hm(p, K).total : 0;
 }
 
+}  // extern "C"
+
+namespace {
+// the head-mix Newton passes for storage dtype DT (validated by the caller)
+template <int DT>
+void head_newton_launch(const void* xproj_v, const prn_params* p, const float* A, const void* h0_v, int32_t K,
+                        void* H_out_v, float* residual_out, const PlanHm& pl, hipStream_t st) {
+  using T = typename prn::Storage<DT>::T;
+  char* ws = static_cast<char*>(p->workspace);
+  const size_t it = align_up(size_t(p->B) * p->T * p->d_h * sizeof(T));
+  T* iter[2] = {reinterpret_cast<T*>(ws + pl.iter_off), reinterpret_cast<T*>(ws + pl.iter_off + it)};
+  float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
+  float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
+  float* rpart = residual_out ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
+  float* gagg = reinterpret_cast<float*>(ws + pl.gagg_off);
+  float* gcarry = reinterpret_cast<float*>(ws + pl.gcarry_off);
+  const T* xp = static_cast<const T*>(xproj_v);
+  const T* h0 = static_cast<const T*>(h0_v);
+  T* Hout = static_cast<T*>(H_out_v);
+  T* slast = static_cast<T*>(p->state_last_out);
+  const dim3 grid(unsigned(pl.n_ch), unsigned(pl.n_heads), unsigned(p->B));
+  const dim3 sgrid(unsigned(pl.n_heads), unsigned(p->B));
+  const T* Hprev = nullptr;
+  for (int k = 0; k < K; ++k) {
+    T* Hk = (k == K - 1) ? Hout : iter[k % 2];
+    prn::k_hm_pass<prn::kHmReduce, DT><<<grid, 64, 0, st>>>(xp, A, h0, Hprev, nullptr, p->T, p->d_h, pl.n_ch, agg,
+                                                            rpart ? rpart + k * pl.n_wg : nullptr, nullptr, nullptr);
+    if (pl.n_groups) {
+      const dim3 ggrid(unsigned(pl.n_groups), unsigned(pl.n_heads), unsigned(p->B));
+      prn::k_hm_group<<<ggrid, 64, 0, st>>>(agg, pl.n_ch, pl.n_groups, gagg);
+      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(gagg, pl.n_groups, gcarry);
+      prn::k_hm_expand<<<ggrid, 64, 0, st>>>(agg, gcarry, pl.n_ch, pl.n_groups, carry);
+    } else {
+      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
+    }
+    prn::k_hm_pass<prn::kHmFix, DT><<<grid, 64, 0, st>>>(xp, A, h0, Hprev, carry, p->T, p->d_h, pl.n_ch, nullptr,
+                                                         nullptr, Hk, k == K - 1 ? slast : nullptr);
+    Hprev = Hk;
+  }
+  if (rpart) {
+    prn::k_hm_pass<prn::kHmResidual, DT><<<grid, 64, 0, st>>>(xp, A, h0, Hout, nullptr, p->T, p->d_h, pl.n_ch,
+                                                              nullptr, rpart + K * pl.n_wg, nullptr, nullptr);
+    prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, residual_out);
+  }
+}
+}  // namespace
+
+extern "C" {
+
 prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const float* A, int32_t d_head,
                                    const void* h0, int32_t K, void* H_out, float* residual_out) {
   Shape sh;
@@ -1076,18 +1124,22 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
   if (misaligned(A, 4)) return fail(PRN_ERR_INVALID_ARG, "A is not 4-byte aligned");
   if (K < 1) return fail(PRN_ERR_INVALID_ARG, "K must be >= 1, got %d", K);
   if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
-  if (misaligned(xproj, 16) || misaligned(h0, 16) || misaligned(H_out, 16))
-    return fail(PRN_ERR_INVALID_ARG, "xproj, h0 and H_out must be 16-byte aligned (4-channel vector loads)");
-  if (misaligned(p->state_last_out, 4) || misaligned(residual_out, 4))
-    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not 4-byte aligned");
+  const size_t vec = 4 * sh.elt;   // four channels per vector load
+  if (misaligned(xproj, vec) || misaligned(h0, vec) || misaligned(H_out, vec))
+    return fail(PRN_ERR_INVALID_ARG, "xproj, h0 and H_out must be %zu-byte aligned (4-channel vector loads)", vec);
+  if (misaligned(p->state_last_out, sh.elt) || misaligned(residual_out, 4))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   hipStream_t st = static_cast<hipStream_t>(p->stream);
-  const float* h0f = static_cast<const float*>(h0);
-  float* slast = static_cast<float*>(p->state_last_out);
   if (p->T == 0) {
     if (residual_out) prn::k_zero_f32<<<unsigned((K + 256) / 256), 256, 0, st>>>(residual_out, K + 1);
-    if (slast) {
+    if (p->state_last_out) {
       const int64_t n = p->B * p->d_h;
-      prn::k_copy_or_zero<float><<<unsigned((n + 255) / 256), 256, 0, st>>>(h0f, slast, n);
+      if (p->dtype == PRN_BF16)
+        prn::k_copy_or_zero<uint16_t><<<unsigned((n + 255) / 256), 256, 0, st>>>(
+            static_cast<const uint16_t*>(h0), static_cast<uint16_t*>(p->state_last_out), n);
+      else
+        prn::k_copy_or_zero<float><<<unsigned((n + 255) / 256), 256, 0, st>>>(
+            static_cast<const float*>(h0), static_cast<float*>(p->state_last_out), n);
     }
     return launched("prn_head_newton_forward");
   }
@@ -1097,40 +1149,10 @@ prn_status prn_head_newton_forward(const void* xproj, const prn_params* p, const
                 p->workspace, pl.total);
   if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
     return fail(PRN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-  char* ws = static_cast<char*>(p->workspace);
-  float* iter[2] = {reinterpret_cast<float*>(ws + pl.iter_off),
-                    reinterpret_cast<float*>(ws + pl.iter_off + align_up(size_t(p->B) * p->T * p->d_h * 4))};
-  float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
-  float* carry = reinterpret_cast<float*>(ws + pl.carry_off);
-  float* rpart = residual_out ? reinterpret_cast<float*>(ws + pl.rpart_off) : nullptr;
-  float* gagg = reinterpret_cast<float*>(ws + pl.gagg_off);
-  float* gcarry = reinterpret_cast<float*>(ws + pl.gcarry_off);
-  const float* xp = static_cast<const float*>(xproj);
-  float* Hout = static_cast<float*>(H_out);
-  const dim3 grid(unsigned(pl.n_ch), unsigned(pl.n_heads), unsigned(p->B));
-  const dim3 sgrid(unsigned(pl.n_heads), unsigned(p->B));
-  const float* Hprev = nullptr;
-  for (int k = 0; k < K; ++k) {
-    float* Hk = (k == K - 1) ? Hout : iter[k % 2];
-    prn::k_hm_pass<prn::kHmReduce><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, nullptr, p->T, p->d_h, pl.n_ch, agg,
-                                                        rpart ? rpart + k * pl.n_wg : nullptr, nullptr, nullptr);
-    if (pl.n_groups) {
-      const dim3 ggrid(unsigned(pl.n_groups), unsigned(pl.n_heads), unsigned(p->B));
-      prn::k_hm_group<<<ggrid, 64, 0, st>>>(agg, pl.n_ch, pl.n_groups, gagg);
-      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(gagg, pl.n_groups, gcarry);
-      prn::k_hm_expand<<<ggrid, 64, 0, st>>>(agg, gcarry, pl.n_ch, pl.n_groups, carry);
-    } else {
-      prn::k_hm_scan<<<sgrid, 64, 0, st>>>(agg, pl.n_ch, carry);
-    }
-    prn::k_hm_pass<prn::kHmFix><<<grid, 64, 0, st>>>(xp, A, h0f, Hprev, carry, p->T, p->d_h, pl.n_ch, nullptr,
-                                                     nullptr, Hk, k == K - 1 ? slast : nullptr);
-    Hprev = Hk;
-  }
-  if (rpart) {
-    prn::k_hm_pass<prn::kHmResidual><<<grid, 64, 0, st>>>(xp, A, h0f, Hout, nullptr, p->T, p->d_h, pl.n_ch,
-                                                          nullptr, rpart + K * pl.n_wg, nullptr, nullptr);
-    prn::k_residual_reduce<<<unsigned(K + 1), 1024, 0, st>>>(rpart, pl.n_wg, residual_out);
-  }
+  if (p->dtype == PRN_BF16)
+    head_newton_launch<prn::kBF16>(xproj, p, A, h0, K, H_out, residual_out, pl, st);
+  else
+    head_newton_launch<prn::kF32>(xproj, p, A, h0, K, H_out, residual_out, pl, st);
   return launched("prn_head_newton_forward");
 }
 
@@ -1142,13 +1164,19 @@ prn_status prn_head_sequential_forward(const void* xproj, const prn_params* p, c
   if (!A) return fail(PRN_ERR_INVALID_ARG, "the recurrent blocks A are NULL");
   if (misaligned(A, 4)) return fail(PRN_ERR_INVALID_ARG, "A is not 4-byte aligned");
   if (p->T > 0 && (!xproj || !H_out)) return fail(PRN_ERR_INVALID_ARG, "xproj or H_out is NULL");
-  if (misaligned(xproj, 4) || misaligned(h0, 4) || misaligned(H_out, 4) || misaligned(p->state_last_out, 4))
-    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not 4-byte aligned");
+  if (misaligned(xproj, sh.elt) || misaligned(h0, sh.elt) || misaligned(H_out, sh.elt) ||
+      misaligned(p->state_last_out, sh.elt))
+    return fail(PRN_ERR_INVALID_ARG, "a tensor pointer is not aligned to its element size");
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   const dim3 sgrid(unsigned(p->d_h / prn::kHmD), unsigned(p->B));
-  prn::k_hm_sequential<<<sgrid, 64, 0, st>>>(static_cast<const float*>(xproj), A, static_cast<const float*>(h0),
-                                             p->T, p->d_h, static_cast<float*>(H_out),
-                                             static_cast<float*>(p->state_last_out));
+  if (p->dtype == PRN_BF16)
+    prn::k_hm_sequential<prn::kBF16><<<sgrid, 64, 0, st>>>(
+        static_cast<const uint16_t*>(xproj), A, static_cast<const uint16_t*>(h0), p->T, p->d_h,
+        static_cast<uint16_t*>(H_out), static_cast<uint16_t*>(p->state_last_out));
+  else
+    prn::k_hm_sequential<prn::kF32><<<sgrid, 64, 0, st>>>(
+        static_cast<const float*>(xproj), A, static_cast<const float*>(h0), p->T, p->d_h,
+        static_cast<float*>(H_out), static_cast<float*>(p->state_last_out));
   return launched("prn_head_sequential_forward");
 }
 

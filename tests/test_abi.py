@@ -251,7 +251,8 @@ def test_decode_step_rejects_bad_arguments_before_launch(kw, args, status):
 
 @pytest.mark.parametrize("kw,args,status", [
     (dict(cell=1, a=None), {}, B.PRN_ERR_UNSUPPORTED),                   # LSTM head-mix is not built
-    (dict(dtype=1, a=None), {}, B.PRN_ERR_UNSUPPORTED),                  # bf16 head-mix is not built
+    (dict(dtype=1, a=None), {}, B.PRN_ERR_WORKSPACE),                    # bf16 head-mix: checked up to the workspace
+    (dict(dtype=1, a=None, d_h=32), dict(xproj=FAKE + 4), B.PRN_ERR_INVALID_ARG),   # bf16 rows need 8-byte alignment
     (dict(B=1, n_seqs=2, a=None), {}, B.PRN_ERR_UNSUPPORTED),            # no ragged pack for head-mix
     (dict(a=None), dict(d_head=8), B.PRN_ERR_UNSUPPORTED),
     (dict(a=None, d_h=24), {}, B.PRN_ERR_INVALID_ARG),                   # d_h not a multiple of d_head
@@ -275,7 +276,10 @@ def test_head_workspace_bytes():
     w3 = B.prn_head_workspace_bytes(2, 1000, 64, 3)
     w1 = B.prn_head_workspace_bytes(2, 1000, 64, 1)
     assert w3 > w1 > 0 and w3 % 256 == 0
-    p = _params(d_h=64, dtype=1)
+    # bf16 iterates take half the bytes of fp32 ones; the rest is fp32 either way
+    w3b = B.prn_head_workspace_bytes(2, 1000, 64, 3, dtype=torch.bfloat16)
+    assert w1 < w3b < w3 and w3b % 256 == 0
+    p = _params(d_h=64, cell=1)   # the LSTM has no head-mix: 0 bytes and a message
     assert B.lib().prn_head_workspace_bytes(ctypes.byref(p), 16, 3) == 0 and B.prn_last_error()
 
 

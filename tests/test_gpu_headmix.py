@@ -4,7 +4,9 @@ against the oracle (oracle/headmix.py), through the C ABI.
 Tolerances (max-abs, fp32 storage): Newton vs the oracle's Newton at equal
 K 1e-5 (each 16-term block product carries fp32 rounding into the next
 linearisation); the sequential kernel vs the oracle's unroll 1e-5; Newton
-at a converged K vs the unroll tau = 1e-4; residuals 2e-5 + 1e-3 r.
+at a converged K vs the unroll tau = 1e-4; residuals 2e-5 + 1e-3 r.  bf16
+storage (xproj, h0, iterates, H): BF16_ABS on h against the oracle's Newton
+with bf16 stores and against its float64 unroll; residuals 2e-2 + 2e-2 r.
 The small cases span several 64-step chunks with a ragged tail, several
 heads, B > 1, and T = 1.
 """
@@ -14,7 +16,9 @@ import torch
 
 from gpu_helpers import hm_dev as dev, hm_inputs as inputs, hm_newton as gpu_newton, hm_sequential as gpu_sequential, say, to_f64
 from nonlinear_rnn_amd import binding as B
+from gpu_helpers import BF16_ABS
 from oracle import headmix as ohm
+from oracle import rounding as oround
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +52,73 @@ def test_sequential_kernel_matches_oracle(Bn, T, d_h, seed):
     e = np.abs(H - ref).max()
     say(f"[case] head-mix sequential B={Bn} T={T} d_h={d_h}: {e:.2e}")
     assert e <= 1e-5 and np.abs(last - ref_last).max() <= 1e-5
+
+
+def _bf16_case(Bn, T, d_h, seed):
+    """Inputs held in bf16 (xproj and h0 rounded to nearest even once), A in fp32."""
+    xp, A, h0 = inputs(Bn, T, d_h, seed)
+    return oround.bf16_round(xp), A, (None if h0 is None else oround.bf16_round(h0))
+
+
+def _dev16(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("Bn,T,d_h,seed", CASES)
+@pytest.mark.parametrize("K", [1, 3])
+def test_bf16_newton_matches_oracle_at_equal_K(Bn, T, d_h, seed, K):
+    """bf16 storage: iterates stored rounded (the oracle's store), every block
+    product and the chain in fp32.  Band: BF16_ABS on h (a rounding flip of
+    one stored iterate between fp32 and fp64 arithmetic moves h by one bf16
+    step); residuals 2e-2 + 2e-2 r as for the diagonal bf16 cells."""
+    say(f"[case] head-mix bf16 newton B={Bn} T={T} d_h={d_h} K={K}")
+    xp, A, h0 = _bf16_case(Bn, T, d_h, seed)
+    H = torch.empty((Bn, T, d_h), dtype=torch.bfloat16, device="cuda")
+    res = torch.full((K + 1,), -1.0, device="cuda")
+    last = torch.empty((Bn, d_h), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(B.prn_head_workspace_bytes(Bn, T, d_h, K, dtype=torch.bfloat16), 1), dtype=torch.uint8,
+                     device="cuda")
+    B.prn_head_newton_forward(_dev16(xp), dev(A), K, H, h0=_dev16(h0), residual_out=res, state_last_out=last,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    Hg, resg = to_f64(H), res.cpu().numpy().astype(np.float64)
+    ref = ohm.newton(xp, A, K, h0=h0, dtype="bf16")
+    e = np.abs(Hg - ref["H"]).max()
+    say(f"  H err {e:.2e}; residuals gpu {np.round(resg, 5)} oracle {np.round(ref['residuals'], 5)}")
+    assert e <= BF16_ABS
+    assert np.array_equal(to_f64(last), Hg[:, T - 1])
+    r = np.asarray(ref["residuals"])
+    assert np.all(np.abs(resg - r) <= 2e-2 + 2e-2 * r)
+
+
+@pytest.mark.parametrize("Bn,T,d_h,seed", CASES[:3])
+def test_bf16_sequential_kernel_matches_oracle(Bn, T, d_h, seed):
+    """bf16 storage: the chain in fp32, every output rounded once; against the
+    oracle's float64 unroll on the same (rounded) inputs, band BF16_ABS."""
+    xp, A, h0 = _bf16_case(Bn, T, d_h, seed)
+    H = torch.empty((Bn, T, d_h), dtype=torch.bfloat16, device="cuda")
+    last = torch.empty((Bn, d_h), dtype=torch.bfloat16, device="cuda")
+    B.prn_head_sequential_forward(_dev16(xp), dev(A), H, h0=_dev16(h0), state_last_out=last)
+    torch.cuda.synchronize()
+    ref, ref_last = ohm.sequential(xp, A, h0=h0)
+    e = np.abs(to_f64(H) - ref).max()
+    say(f"[case] head-mix bf16 sequential B={Bn} T={T} d_h={d_h}: {e:.2e}")
+    assert e <= BF16_ABS and np.abs(to_f64(last) - ref_last).max() <= BF16_ABS
+
+
+def test_bf16_run_to_run_and_mixed_dtypes_rejected():
+    xp, A, h0 = _bf16_case(2, 300, 32, 9)
+    outs = []
+    for _ in range(2):
+        H = torch.empty((2, 300, 32), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(B.prn_head_workspace_bytes(2, 300, 32, 3, dtype=torch.bfloat16), dtype=torch.uint8,
+                         device="cuda")
+        B.prn_head_newton_forward(_dev16(xp), dev(A), 3, H, h0=_dev16(h0), workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(H)
+    assert torch.equal(outs[0], outs[1])
+    with pytest.raises(TypeError):   # H_out must share xproj's storage dtype
+        B.prn_head_newton_forward(_dev16(xp), dev(A), 3, torch.empty((2, 300, 32), device="cuda"), workspace=ws)
 
 
 def test_newton_converges_to_the_unroll():
