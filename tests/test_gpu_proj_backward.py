@@ -66,6 +66,8 @@ CASES = [
     ("gru", "f32", 4, 2048, 256, 256),  # G d_h and d_in multiples of 256: dW along the rows, no transposes
     ("gru", "f32", 1, 1234, 512, 256),  # the same with a ragged last slice of tokens
     ("lstm", "bf16", 2, 1500, 256, 128),
+    ("gru", "f32", 1, 700, 512, 256),   # two column tiles of dW: only the first takes the dbias sums
+    ("gru", "bf16", 1, 700, 512, 256),
 ]
 
 
