@@ -228,27 +228,34 @@ def hm_inputs(Bn, T, d_h, seed, scale=0.5, with_h0=True):
     return xp, A, h0
 
 
-def hm_dev(a):
-    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+def hm_dev(a, dtype="f32"):
+    """A device tensor of a (float64 values exactly representable in dtype)."""
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return t if dtype == "f32" else t.to(torch.bfloat16)
 
 
-def hm_newton(xp, A, K, h0=None, want_last=False):
+def hm_newton(xp, A, K, h0=None, want_last=False, dtype="f32"):
+    """Head-mix Newton forward on the GPU; xp and h0 must hold values of the storage dtype."""
     Bn, T, _, d_h = xp.shape
-    H = torch.empty((Bn, T, d_h), device="cuda")
+    dt = TORCH_DT[dtype]
+    H = torch.empty((Bn, T, d_h), dtype=dt, device="cuda")
     res = torch.full((K + 1,), -1.0, device="cuda")
-    last = torch.empty((Bn, d_h), device="cuda") if want_last else None
-    ws = torch.empty(max(B.prn_head_workspace_bytes(Bn, T, d_h, K), 1), dtype=torch.uint8, device="cuda")
-    B.prn_head_newton_forward(hm_dev(xp), hm_dev(A), K, H, h0=hm_dev(h0), residual_out=res, state_last_out=last,
-                              workspace=ws)
+    last = torch.empty((Bn, d_h), dtype=dt, device="cuda") if want_last else None
+    ws = torch.empty(max(B.prn_head_workspace_bytes(Bn, T, d_h, K, dtype=dt), 1), dtype=torch.uint8, device="cuda")
+    B.prn_head_newton_forward(hm_dev(xp, dtype), hm_dev(A), K, H, h0=hm_dev(h0, dtype), residual_out=res,
+                              state_last_out=last, workspace=ws)
     torch.cuda.synchronize()
     return to_f64(H), res.cpu().numpy().astype(np.float64), (None if last is None else to_f64(last))
 
 
-def hm_sequential(xp, A, h0=None):
+def hm_sequential(xp, A, h0=None, dtype="f32"):
     Bn, T, _, d_h = xp.shape
-    H = torch.empty((Bn, T, d_h), device="cuda")
-    last = torch.empty((Bn, d_h), device="cuda")
-    B.prn_head_sequential_forward(hm_dev(xp), hm_dev(A), H, h0=hm_dev(h0), state_last_out=last)
+    dt = TORCH_DT[dtype]
+    H = torch.empty((Bn, T, d_h), dtype=dt, device="cuda")
+    last = torch.empty((Bn, d_h), dtype=dt, device="cuda")
+    B.prn_head_sequential_forward(hm_dev(xp, dtype), hm_dev(A), H, h0=hm_dev(h0, dtype), state_last_out=last)
     torch.cuda.synchronize()
     return to_f64(H), to_f64(last)
 

@@ -21,7 +21,9 @@ import torch
 from gpu_helpers import (TORCH_DT, gpu_backward, gpu_forward_states, gpu_run, gpu_run_fused, gpu_sequential, hm_inputs,
                          hm_newton, hm_sequential, oracle_backward, oracle_newton, oracle_sequential, random_grads,
                          rel_err, say, state_err, to_f64, tol, tols)
+from gpu_helpers import BF16_ABS
 from oracle import headmix as ohm
+from oracle.rounding import bf16_round
 from workloads import Workload, make_inputs, random_state
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +147,34 @@ def draw_head_case(i: int):
     T = int(rng.integers(1, 1501)) if rng.integers(12) else 0
     K = int(rng.integers(1, 6))
     return Bn, T, d_h, K, bool(rng.integers(2))
+
+
+@pytest.mark.parametrize("i", range(8), ids=lambda i: "{}-B{}-T{}-dh{}-K{}-h0{}".format(i, *draw_head_case(100 + i)))
+def test_sweep_head_mix_bf16_against_the_oracle(i):
+    """Head-mix GRU with bf16 storage (inputs rounded once to bf16): Newton at
+    equal K against the oracle's Newton with bf16 stores (BF16_ABS on h;
+    residuals 2e-2 + 2e-2 r), the sequential kernel against the float64
+    unroll (BF16_ABS)."""
+    Bn, T, d_h, K, with_h0 = draw_head_case(100 + i)
+    say(f"[case] sweep head-mix bf16 B={Bn} T={T} d_h={d_h} K={K} h0={with_h0}")
+    xp, A, h0 = hm_inputs(Bn, T, d_h, seed=9000 + i, with_h0=with_h0)
+    xp = bf16_round(xp)
+    h0 = None if h0 is None else bf16_round(h0)
+    H, res, last = hm_newton(xp, A, K, h0, want_last=True, dtype="bf16")
+    if T == 0:
+        assert np.array_equal(res, np.zeros(K + 1))
+        assert np.array_equal(last, np.zeros((Bn, d_h)) if h0 is None else h0)
+        return
+    ref = ohm.newton(xp, A, K, h0=h0, dtype="bf16")
+    r = np.asarray(ref["residuals"])
+    e = np.abs(H - ref["H"]).max()
+    say(f"  newton max err {e:.2e}")
+    assert e <= BF16_ABS
+    assert np.array_equal(last, H[:, -1])
+    assert np.all(np.abs(res - r) <= 2e-2 + 2e-2 * r)
+    Hs, _ = hm_sequential(xp, A, h0, dtype="bf16")
+    seq, _ = ohm.sequential(xp, A, h0=h0)
+    assert np.abs(Hs - seq).max() <= BF16_ABS
 
 
 @pytest.mark.parametrize("i", range(16), ids=lambda i: "{}-B{}-T{}-dh{}-K{}-h0{}".format(i, *draw_head_case(i)))
