@@ -20,7 +20,7 @@ import torch
 
 from gpu_helpers import (TORCH_DT, gpu_backward, gpu_forward_states, gpu_run, gpu_run_fused, gpu_sequential, hm_inputs,
                          hm_newton, hm_sequential, oracle_backward, oracle_newton, oracle_sequential, random_grads,
-                         rel_err, say, state_err, to_f64, tol, tols)
+                         rel_err, say, state_err, to_f64, tols)
 from gpu_helpers import BF16_ABS
 from oracle import headmix as ohm
 from oracle.rounding import bf16_round
