@@ -38,6 +38,21 @@ k_decode(const typename Storage<DT>::T* __restrict__ x, const typename Storage<D
   const int64_t s0 = static_cast<int64_t>(blockIdx.y) * SB;
   const int n_s = static_cast<int>(imin(SB, n_slots - s0));
 
+  // what the cell step needs besides the projection (this lane's bias term,
+  // the channel's recurrent weights, the carry of this lane's slot) is read
+  // here, so that those loads are in flight with the projection's instead of
+  // after them (lanes past the last slot read the last slot's carry and
+  // store nothing)
+  const int g_l = lane / SB;
+  const float bv = (bias && g_l < G) ? bias[g_l * d_h + ch] : 0.0f;
+  ChanCoef<C> cf;
+  cf.load(a, d_h, ch);
+  const int64_t slot = s0 + imin(lane & (SB - 1), n_s - 1);
+  float s[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) s[q] = 0.0f;
+  if (sin) load_state<DT, S>(sin + slot * S * d_h + ch, d_h, s);
+
   // partial dot products: p[g * SB + s] over this lane's k = lane, lane + 64,
   // ...; U row pieces per round, their loads issued together (the loop is
   // bound by load latency, not by the multiply-adds).  The loads carry no
@@ -83,24 +98,17 @@ k_decode(const typename Storage<DT>::T* __restrict__ x, const typename Storage<D
     }
   }
   // lane l = g * SB + s holds the projected value of gate g, slot s
-  const int g_l = lane / SB;
   float v = p[0];
   if (g_l < G) {
-    if (bias) v += bias[g_l * d_h + ch];
+    if (bias) v += bv;
     v = ST::round(v);
   }
   float xs[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) xs[g] = __shfl(v, g * SB + (lane & (SB - 1)), kWave) * C::scale(g);
-  if (lane >= n_s) return;  // lanes 0..n_s-1: one slot each
+  if (lane >= n_s) return;  // lanes 0..n_s-1: one slot each (slot = s0 + lane)
 
-  const int64_t slot = s0 + lane;
-  ChanCoef<C> cf;
-  cf.load(a, d_h, ch);
-  float s[S], o[S];
-#pragma unroll
-  for (int q = 0; q < S; ++q) s[q] = 0.0f;
-  if (sin) load_state<DT, S>(sin + slot * S * d_h + ch, d_h, s);
+  float o[S];
   C::f(xs, s, cf.as, cf.a, o);
 #pragma unroll
   for (int q = 0; q < S; ++q) sout[(slot * S + q) * d_h + ch] = ST::pack(o[q]);
