@@ -187,20 +187,32 @@ prn_status check_newton_args(const prn_params* p, const Shape& sh, const void* x
   return PRN_OK;
 }
 
-// backward geometry.  Single pass (default): per-cell chunks, measured at
-// the long LSTM shape (LS x NW = 8 x 8: 0.95-0.98 ms, 8 x 4: 0.92, 12 x 4:
-// 0.98, 16 x 4: 0.92) and one 65536-step GRU row (8 x 8: 0.165 ms, 8 x 4:
-// 0.20, 16 x 4: 0.17, 16 x 8: 0.15); workspace: status words, chunk records
-// and the da partials.  Three-phase (PRN_ALGO=tp): chunks of kLC steps;
-// aggregates, carries, da partials.
-// As in the forward, long chunks pay off only with few chains: the bf16 GRU
-// at 16 x 16384 x 512 (128 chains) took 1.16 ms at 16 x 8 against 1.0 ms at
-// 8 x 8, so the GRU takes 16 x 8 below 64 chains and 8 x 8 above; the LSTM
-// takes 8 x 8 (1.035 ms on the long LSTM workload; 8 x 4: 1.048 ms).
-constexpr int kBwNW = 8, kBwLsFew = 16, kBwLs = 8;
+// backward geometry.  Single pass (default): per-cell chunks of LS steps
+// per lane times NW waves; workspace: status words, chunk records and the da
+// partials.  Three-phase (PRN_ALGO=tp): chunks of kLC steps; aggregates,
+// carries, da partials.
+// Measured with the MALL flushed (ms; LS x NW): long LSTM 8 x 8: 0.77,
+// 8 x 16: 0.70-0.73, 7 x 16: 0.74, 6 x 16: 0.75, 8 x 12: 0.79, 8 x 4: 0.93,
+// 12 x 8: 0.93; GRU below 64 chains (8 x 4096 x 256 / one 65536-step ragged
+// row): 16 x 8: 0.125-0.133 / 0.190, 16 x 16: 0.117-0.120 / 0.177-0.179,
+// 12 x 16: 0.110 / 0.204, 20 x 16: 0.112 / 0.210, 16 x 12: 0.139 / 0.213;
+// the bf16 GRU at 128 chains: 8 x 8: 0.925, 8 x 4: 0.909, 6 x 8: 0.97,
+// 12 x 8: 1.14, 4 x 16: 1.36.  Sixteen waves of 1024 threads fill a CU as
+// two eight-wave workgroups did (the LSTM instance keeps 124 registers, four
+// waves per SIMD) with half the look-backs per step; long chunks pay off
+// only with few chains, as in the forward.
+struct BwGeo {
+  int ls, nw;
+};
+constexpr BwGeo kBwLstm{8, 16}, kBwGruFew{16, 16}, kBwGruMany{8, 8};
+BwGeo bw_geo(int cell, int64_t n_chains) {
+  if (cell != PRN_CELL_DIAG_GRU) return kBwLstm;
+  return n_chains < kSpManyChains ? kBwGruFew : kBwGruMany;
+}
 int bw_chunk(int cell, int64_t n_chains, bool sp) {
   if (!sp) return kLC;
-  return (cell == PRN_CELL_DIAG_GRU && n_chains < kSpManyChains ? kBwLsFew : kBwLs) * kBwNW;
+  const BwGeo g = bw_geo(cell, n_chains);
+  return g.ls * g.nw;
 }
 // dL/da is reduced from per-chunk partials in two fixed-order levels: up to
 // kDaSlices slices of chunks, then the slices (one level with only
@@ -516,19 +528,20 @@ prn_status backward(const prn_params* p, const Shape& sh, const void* xproj_v, c
       rec.agg = reinterpret_cast<float*>(ws + pl.agg_off);
       rec.pre = reinterpret_cast<float*>(ws + pl.pre_off);
       prn::k_zero_u32<<<unsigned((pl.n_words + 255) / 256), 256, 0, st>>>(words, int64_t(pl.n_words));
-      auto launch = [&](auto ls) {
-        constexpr int LS = decltype(ls)::value;
-        prn::k_bw_sp<C, DT, LS, kBwNW><<<unsigned(pl.n_ch * pl.n_chains), 64 * kBwNW, 0, st>>>(
+      auto launch = [&](auto ls, auto nw) {
+        constexpr int LS = decltype(ls)::value, NW = decltype(nw)::value;
+        prn::k_bw_sp<C, DT, LS, NW><<<unsigned(pl.n_ch * pl.n_chains), 64 * NW, 0, st>>>(
             xproj, states, h0, cu, p->a, dH, dsl, p->T, p->d_h, p->n_seqs, pl.n_ch, pl.n_tiles, pl.n_chains, dxproj,
             dh0, dap, rec, spin_limit(), pl.n_chains < kAggFirstBelowChains);
       };
+      // the geometry bw_chunk planned the workspace for
       if constexpr (S == 1) {
-        if (pl.lc == kBwLsFew * kBwNW)
-          launch(std::integral_constant<int, kBwLsFew>{});
+        if (pl.n_chains < kSpManyChains)
+          launch(std::integral_constant<int, kBwGruFew.ls>{}, std::integral_constant<int, kBwGruFew.nw>{});
         else
-          launch(std::integral_constant<int, kBwLs>{});
+          launch(std::integral_constant<int, kBwGruMany.ls>{}, std::integral_constant<int, kBwGruMany.nw>{});
       } else {
-        launch(std::integral_constant<int, kBwLs>{});
+        launch(std::integral_constant<int, kBwLstm.ls>{}, std::integral_constant<int, kBwLstm.nw>{});
       }
     } else {
       float* agg = reinterpret_cast<float*>(ws + pl.agg_off);
