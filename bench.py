@@ -178,7 +178,7 @@ def bench_headmix(torch, B, dev, steps: int, warmup: int, Bn: int = 8, T: int = 
     ms = float(t_n.mean())
     fl = headmix_flops(Bn, T, d_h, K)
     return {"config": {"cell": "head-mix GRU", "B": Bn, "T": T, "d_h": d_h, "d_head": 16, "K": K},
-            "kernels": "k_hm_reduce + k_hm_scan + k_hm_fix per iteration (prn_head_newton_forward)",
+            "kernels": "k_hm_pass (reduce, fix-up) + k_hm_scan or k_hm_group, k_hm_scan, k_hm_expand per iteration (prn_head_newton_forward)",
             "newton_ms_mean": ms, "newton_ms_min": float(t_n.min()), "tokens_per_s": Bn * T / (ms * 1e-3),
             "sequential_ms_mean": float(t_s.mean()), "speedup_vs_unroll": float(t_s.mean()) / ms,
             "max_abs_vs_unroll": float((H - Hs).abs().max()), "residual_K": float(res[-1]),
