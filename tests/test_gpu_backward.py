@@ -115,11 +115,16 @@ def test_backward_is_deterministic(w, algo):
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_backward_edge_shapes(cell, algo):
-    """T = 0 (da = 0, dh0 = dstate_last), T = 1, empty and one-step segments."""
+    """T = 0 (da = 0, dh0 = dstate_last), T = 1, empty and one-step segments,
+    and T at and just past whole chunks of the single-pass schedule (128 steps
+    for the LSTM, 256 for the GRU with few chains), with segment heads on the
+    chunk boundaries."""
     G, S = (3, 1) if cell == "gru" else (4, 2)
     d = 70
     for name, B_, T, cu in [("T0", 2, 0, None), ("T1", 3, 1, None), ("one-chunk", 1, 5, None),
-                            ("ragged-empty", 1, 70, [0, 0, 33, 33, 69, 70]), ("ragged-T0", 1, 0, [0, 0, 0])]:
+                            ("ragged-empty", 1, 70, [0, 0, 33, 33, 69, 70]), ("ragged-T0", 1, 0, [0, 0, 0]),
+                            ("T128", 1, 128, None), ("T129", 2, 129, None), ("T256", 1, 256, None),
+                            ("T257", 1, 257, None), ("ragged-at-chunks", 1, 300, [0, 128, 256, 300])]:
         n_seqs = 0 if cu is None else len(cu) - 1
         w = Workload(f"{cell}_{name}", cell, B_, T, 8, d, "f32", 2, n_seqs=n_seqs)
         say(f"[case] backward edge {w}")
