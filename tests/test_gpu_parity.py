@@ -198,8 +198,11 @@ def test_packed_segments_match_separate_runs_and_empty_segments(algo):
         assert torch.allclose(one["H"][0], pk["H"][0, lo:hi], atol=1e-5, rtol=0)
 
 
+# T at and just past whole single-pass chunks too: 64 steps (fp32 LSTM), 96
+# (GRU below 64 chains)
 @pytest.mark.parametrize("T,d_h,K", [(1, 16, 3), (31, 64, 2), (32, 64, 3), (33, 65, 3), (70, 1, 1),
-                                     (45, 63, 50), (0, 16, 3)])
+                                     (45, 63, 50), (0, 16, 3), (64, 64, 3), (65, 40, 2), (96, 64, 3),
+                                     (97, 64, 3), (192, 33, 4)])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_edge_shapes(cell, T, d_h, K, algo):
     w = Workload(f"{cell}_edge", cell, 2, T, 8, d_h, "f32", K)
