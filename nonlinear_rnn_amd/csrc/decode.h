@@ -7,14 +7,17 @@
 // (each weight row and each token is read in coalesced 64-element pieces),
 // and every lane keeps a partial sum for each of the 4 x 16 (gate, slot)
 // outputs (the GRU's three gates padded to four).  A transpose-reduce
-// butterfly (at stage m a lane keeps the half of its partials selected by
-// its lane bit m and adds its xor-m partner's copy of that half: 63
-// shuffle-adds in all) leaves lane l with the complete sum of output l.
+// butterfly (at each lane bit a lane keeps the half of its partials that
+// bit selects and adds its partner's copy of that half: 63 exchange-adds in
+// all, through cross-lane swaps and DPP, not LDS) leaves lane l with the
+// complete sum of output l.
 // The sum gets its bias, is rounded to the storage dtype (as the
 // projection's output would be), and lanes 0..15 gather their slot's gates
 // and step the cell from the carry.  Waves are independent: no LDS, no
 // barrier.
 #pragma once
+
+#include <type_traits>
 
 #include "newton_kernels.h"
 
@@ -85,18 +88,40 @@ k_decode(const typename Storage<DT>::T* __restrict__ x, const typename Storage<D
 #pragma unroll
         for (int s = 0; s < SB; ++s) p[g * SB + s] = fmaf(wv[u][g], xv[u][s], p[g * SB + s]);
   }
-  // transpose-reduce: after the stage with offset m, lane l holds n = m
-  // partials, those of the outputs whose bit log2(m) equals l's bit log2(m)
+  // transpose-reduce: after the stage of lane bit b, lane l holds 2^b
+  // partials, those of the outputs whose bit b equals l's bit b.  The
+  // partner of a lane differs from it in bit b and agrees on the bits above
+  // (it holds the same outputs).  Bits 5 and 4: the half-wave and row swaps
+  // exchange one register of each pair across the halves (rows), and the
+  // sum of the two swapped registers is own + partner's copy of the half
+  // each lane keeps.  Bits 3..0: a lane sends the half it does not keep,
+  // read by its partner through DPP: rotate by 8 in a row (partner l ^ 8),
+  // mirror in 8 lanes (l ^ 7: bit 2 flips, bits 3 and up agree), quad
+  // permutations (l ^ 2, l ^ 1).  No LDS traffic.
 #pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) {
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[i]), __float_as_uint(p[i + 32]), false, false);
+    p[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[i]), __float_as_uint(p[i + 16]), false, false);
+    p[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  auto dpp_stage = [&](auto m_t, auto ctrl_t) __attribute__((always_inline)) {
+    constexpr int m = decltype(m_t)::value, ctrl = decltype(ctrl_t)::value;
     const bool hi = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < m; ++i) {
       const float keep = hi ? p[i + m] : p[i];
       const float send = hi ? p[i] : p[i + m];
-      p[i] = keep + __shfl_xor(send, m, kWave);
+      p[i] = keep + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(send), ctrl, 0xf, 0xf, false));
     }
-  }
+  };
+  dpp_stage(std::integral_constant<int, 8>{}, std::integral_constant<int, 0x128>{});  // row_ror:8
+  dpp_stage(std::integral_constant<int, 4>{}, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  dpp_stage(std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4e>{});   // quad_perm [2,3,0,1]
+  dpp_stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0xb1>{});   // quad_perm [1,0,3,2]
   // lane l = g * SB + s holds the projected value of gate g, slot s
   float v = p[0];
   if (g_l < G) {
