@@ -69,10 +69,11 @@ __device__ __forceinline__ hm_f4 hm_blockmul(const float* xm, const hm_f4& m) {
   return acc;
 }
 
-// sum over the four lanes of a channel
+// sum over the four lanes of a channel (one quad: DPP quad permutations
+// [1,0,3,2] and [2,3,0,1], no LDS)
 __device__ __forceinline__ float hm_rowsum(float x) {
-  x += __shfl_xor(x, 1, kWave);
-  x += __shfl_xor(x, 2, kWave);
+  x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0xb1, 0xf, 0xf, false));
+  x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x4e, 0xf, 0xf, false));
   return x;
 }
 
