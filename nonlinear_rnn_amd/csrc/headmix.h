@@ -287,8 +287,7 @@ k_hm_pass(const typename Storage<DT>::T* __restrict__ xproj, const float* __rest
   }
   if (MODE == kHmFix && slast && t0 + n == T && q == 0) slast[b * d_h + head * kHmD + i] = ST::pack(d);
   if (MODE != kHmFix && rpart) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, kWave)));
+    rmax = wave_max_u32(rmax);
     if (lane == 0) rpart[(b * n_heads + head) * n_ch + chunk] = rmax_finish(rmax);
   }
 }

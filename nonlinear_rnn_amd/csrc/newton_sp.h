@@ -441,8 +441,7 @@ k_newton_sp(const typename Storage<DT>::T* __restrict__ xproj, const typename St
   // workgroup barrier (the one that exchanges the waves' maps) thread 0
   // combines them; red[] is not written again before the look-back barrier
   auto residual_put = [&](unsigned r) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) r = max(r, static_cast<unsigned>(__shfl_xor(static_cast<int>(r), o, kWave)));
+    r = wave_max_u32(r);
     if (lane == 0) red[w] = r;
   };
   auto residual_finish = [&](int k) {

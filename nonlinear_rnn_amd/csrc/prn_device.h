@@ -78,6 +78,21 @@ __device__ __forceinline__ unsigned rmax_bits(unsigned r, float x) { return max(
 __device__ __forceinline__ float rmax_finish(unsigned r) {
   return r > 0x7f800000u ? __builtin_inff() : __uint_as_float(r);
 }
+// maximum of r over the wave, in every lane, without LDS: within each
+// 16-lane row by DPP (partners l ^ 1, l ^ 2 by quad permutations, then the
+// mirror images in 8 and in 16 lanes), then across rows and halves by the
+// gfx950 row swaps (the two results of a swap hold, in each lane, its own
+// row's value and the partner row's)
+__device__ __forceinline__ unsigned wave_max_u32(unsigned r) {
+  r = max(r, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(r), 0xb1, 0xf, 0xf, false)));
+  r = max(r, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(r), 0x4e, 0xf, 0xf, false)));
+  r = max(r, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(r), 0x141, 0xf, 0xf, false)));
+  r = max(r, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(r), 0x140, 0xf, 0xf, false)));
+  const auto x = __builtin_amdgcn_permlane16_swap(r, r, false, false);
+  r = max(x[0], x[1]);
+  const auto y = __builtin_amdgcn_permlane32_swap(r, r, false, false);
+  return max(y[0], y[1]);
+}
 
 // ---------------------------------------------------- affine maps --------
 // One channel's map s -> A s + b (S = 1 or 2).  compose(m2, m1) is "m2 after
